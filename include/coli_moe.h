@@ -1,0 +1,221 @@
+/*
+ * coli_moe.h -- C ABI of the routed-expert MoE layer library (gfx950 / MI355X).
+ *
+ * One MoE layer of a colibri-style engine: a router picks the top-k routed
+ * experts per token, the chosen (token, expert) pairs are grouped by expert so
+ * that each distinct expert's weights are read once per batch (the "batch
+ * union"), every chosen expert applies an int4 group-quantised gate/up
+ * projection, SwiGLU and an int4 down projection, and the expert outputs are
+ * summed with the routing weights (plus an always-on shared expert).
+ *
+ * Sources (web pages about the colibri engine):
+ *  - tantan.ink post "colibri: 把 744B 模型当数据流..." section "它的核心判断":
+ *    routed experts of about 19 MB int4 each, streamed on demand.
+ *  - same post, section "几个关键工程动作": within a batch each distinct expert
+ *    is read once, and its three matrices gate/up/down are stored adjacently.
+ *  - same post, section "我看到的几个坑": the int4 container is group-scaled
+ *    with one scale per 64 weights (gs64), not one per row.
+ *  - alphamatch.ai blog "Colibri：革命性 AI 引擎..." section "優化整數核心":
+ *    the integer kernel takes Q8_0-style int8 activations.
+ *  - aixq.cc article, section "为什么值得关注": the router's choice decides
+ *    which experts are loaded.
+ * The pages state no formula for the router, the activation or the quantiser;
+ * the readings taken here are written next to each definition below.
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
+ *    owns every buffer; the library never allocates, frees or synchronises.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL means the null stream).
+ *  - Arguments are validated on the host before any launch.  On a failed
+ *    check nothing is launched, no output is written, and a negative
+ *    COLI_E_* code is returned.  A failed launch returns COLI_E_HIP; a fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give bit-identical outputs on
+ *    every run (no floating-point atomics anywhere).
+ *  - Calls that share a workspace or route buffer must not overlap in time.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  COLI_OK = 0,
+  COLI_E_INVALID = -1,     /* a NULL pointer, a size out of range, a bad flag */
+  COLI_E_UNSUPPORTED = -2, /* a valid layer shape this build does not run */
+  COLI_E_WORKSPACE = -3,   /* ws_bytes below coli_moe_workspace_bytes() */
+  COLI_E_ALIGN = -4,       /* a pointer below its required alignment */
+  COLI_E_HIP = -5          /* a HIP launch or device query failed */
+};
+
+/* ---- routing flags (coli_moe_layer_t.flags) ------------------------------
+ * The pages do not name the routing function; both used by the model families
+ * they list are provided.
+ *  SOFTMAX: p = softmax over ALL E logits; w_j = p[idx_j].
+ *  SIGMOID: w_j = 1 / (1 + exp(-logit[idx_j])).
+ *  RENORM : afterwards w_j /= sum_j w_j over the k selected experts.
+ * In every case w_j is then multiplied by routed_scale.  The weights always
+ * use the raw logits; the optional selection bias only moves the choice.  */
+enum {
+  COLI_ROUTE_SOFTMAX = 0u,
+  COLI_ROUTE_SIGMOID = 1u,
+  COLI_ROUTE_RENORM = 1u << 8
+};
+
+/* output element type of the forward calls */
+enum { COLI_OUT_BF16 = 0, COLI_OUT_F32 = 1 };
+
+/* quantize_q8_0 source element type */
+enum { COLI_SRC_BF16 = 0, COLI_SRC_F32 = 1 };
+
+/* workspace selector for coli_moe_workspace_bytes */
+enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
+
+/* ---- the int4 gs64 expert container --------------------------------------
+ * Experts e = 0 .. E-1 are routed; when n_shared == 1, expert E is the shared
+ * expert.  Every expert owns three matrices, stored adjacently in this order:
+ *     gate [I rows x H]   up [I rows x H]   down [H rows x I]
+ * Each matrix is row-major with its reduction dimension K contiguous
+ * (K = H for gate/up, K = I for down).
+ *  q4     : (E+S) * 3*I*H/2 bytes.  Byte j of row n holds weight k = 2j in
+ *           its low nibble and k = 2j+1 in its high nibble; a nibble is a
+ *           4-bit two's-complement integer q in [-8, 7].
+ *           Expert e starts at byte e * 3*I*H/2; within it gate starts at 0,
+ *           up at I*H/2, down at I*H.
+ *  scales : (E+S) * 3*I*H/64 IEEE fp16 values.  Scale s[n][g] covers weights
+ *           k in [64g, 64g+64) of row n; row n of a matrix holds K/64 scales.
+ *           Expert e starts at element e * 3*I*H/64; gate at 0, up at I*H/64,
+ *           down at 2*I*H/64.
+ * The weight is w = q * s (symmetric, no zero point).  With H = 6144 and
+ * I = 2048 one expert is 18,874,368 + 1,179,648 = 20,054,016 bytes, which
+ * matches the roughly 19 MB per routed expert given for GLM-5.2 (tantan.ink
+ * post, section "它的核心判断").
+ * Requirements: H, I multiples of 64 in [64, 16384]; 1 <= E <= 1024;
+ * n_shared in {0, 1}; 1 <= k <= min(E, 32); q4 and scales 16-byte aligned.
+ */
+typedef struct coli_moe_layer {
+  int32_t hidden;        /* H */
+  int32_t inter;         /* I */
+  int32_t n_experts;     /* E, routed experts */
+  int32_t n_shared;      /* S, 0 or 1 always-on shared experts (index E) */
+  int32_t top_k;         /* k */
+  uint32_t flags;        /* COLI_ROUTE_* */
+  float routed_scale;    /* multiplies every routing weight (1.0f usually) */
+  const uint8_t *q4;     /* device, see above */
+  const uint16_t *scales;/* device, fp16 bit patterns, see above */
+} coli_moe_layer_t;
+
+/* ---- route buffers (caller-allocated device memory) ---------------------
+ * Written by coli_moe_route, read by the forward calls.  P = T*k pairs; pair
+ * p = t*k + j is token t's j-th choice.
+ *  topk_idx [P] int32 : experts of token t, by score descending, ties to the
+ *                       lower expert index (score = logit [+ sel_bias]).
+ *  topk_w   [P] fp32  : routing weights, see COLI_ROUTE_*.
+ *  counts   [E] int32 : pairs routed to expert e.
+ *  offsets  [E+1]     : exclusive prefix sum of counts; offsets[E] = P.
+ *  pairs    [P] int32 : pair ids grouped by expert (expert 0 first); within
+ *                       an expert in ascending pair id (= ascending token).
+ *  pair_pos [P] int32 : inverse of pairs: pairs[pair_pos[p]] == p.
+ *  union_ids[E] int32 : the batch union, experts with counts > 0 ascending;
+ *                       entries past n_union are left unspecified.
+ *  n_union  [1] int32 : size of the batch union (routed experts only).
+ */
+typedef struct coli_moe_route {
+  int32_t *topk_idx;
+  float *topk_w;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *pairs;
+  int32_t *pair_pos;
+  int32_t *union_ids;
+  int32_t *n_union;
+} coli_moe_route_t;
+
+/* Bytes of device workspace an entry point needs for T tokens (entry is a
+ * COLI_ENTRY_*).  Returns 0 for invalid arguments.  Host-only, no HIP call. */
+size_t coli_moe_workspace_bytes(const coli_moe_layer_t *layer, int32_t T,
+                                int32_t entry);
+
+/* Route T tokens: top-k selection, routing weights and grouping by expert.
+ *  logits   [T*E] fp32 row-major, finite values.
+ *  sel_bias [E] fp32 or NULL: added to the logits for selection only.
+ *  T in [1, 65536] with T*k <= 2^20.
+ * Selection and grouping are exact (comparisons and integer counts only).
+ * Source: aixq.cc article, section "为什么值得关注" (the router decides which
+ * experts load); tantan.ink post, section "几个关键工程动作" (batch union). */
+int coli_moe_route(const coli_moe_layer_t *layer, const float *logits,
+                   const float *sel_bias, int32_t T,
+                   const coli_moe_route_t *route, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* Decode-shaped forward, T in [1, 64] tokens (single-token decode and
+ * multi-token verify).  Activations stay bf16 -> fp32; weights are
+ * dequantised in registers (w = q*s exactly); products are accumulated in
+ * fp32.  For each token t:
+ *   y[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t]) + [S] FFN_E(x[t])
+ *   FFN_e(x) = W_down * (silu(W_gate x) .* (W_up x)),  silu(g) = g/(1+e^-g)
+ * Every distinct expert's weights are streamed from HBM once per call.
+ * A token's result does not depend on which other tokens share the batch.
+ *  x [T*H] bf16;  y [T*H] bf16 (round-to-nearest-even) or fp32 (y_dtype).
+ * Sources: tantan.ink post, sections "它的核心判断" and "几个关键工程动作". */
+int coli_moe_forward_decode(const coli_moe_layer_t *layer,
+                            const coli_moe_route_t *route, const uint16_t *x,
+                            int32_t T, void *y, int32_t y_dtype, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Prefill-shaped forward, T in [1, 65536] tokens, on the integer path:
+ *  1. x[t] (bf16 -> fp32) is quantised Q8_0 per 32 values (see below).
+ *  2. g, u = sum over 32-blocks b of s[n][b/2] * d_x[t][b] * dot_b, where
+ *     dot_b is the exact int32 product of the int4 weights and the int8
+ *     activations over block b (int8 matrix cores).
+ *  3. h = silu(g) * u in fp32, quantised Q8_0 per 32 values along I.
+ *  4. o = the same block-scaled integer product of W_down and q_h.
+ *  5. y[t] = sum_j topk_w[t,j] * o_{t,j} + [S] o_shared(t).
+ * Source: alphamatch.ai blog, section "優化整數核心" (Q8_0-style int8
+ * activations feeding an integer dot kernel) and section "技術卓越"
+ * (batched-union MoE in prefill). */
+int coli_moe_forward_prefill(const coli_moe_layer_t *layer,
+                             const coli_moe_route_t *route, const uint16_t *x,
+                             int32_t T, void *y, int32_t y_dtype, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Q8_0 quantisation of n values (n a multiple of 32), the activation format
+ * of the integer path (alphamatch.ai blog, section "優化整數核心").  Per block
+ * of 32 fp32 values v: a = max|v|; d = a / 127 (IEEE fp32 division);
+ * q = round-half-away-from-zero(v / d) clamped to [-127, 127], or 0 when
+ * a == 0; the stored scale is d rounded to fp16 (nearest-even).  The values
+ * are quantised with the fp32 d, and the fp16 d is what the dot products use.
+ *  src [n] bf16 or fp32 (src_dtype);  q [n] int8;  d [n/32] fp16 bits.
+ * The same device code as the prefill path's quantiser. */
+int coli_moe_quantize_q8_0(const void *src, int32_t src_dtype, int64_t n,
+                           int8_t *q, uint16_t *d, void *stream);
+
+/* The exact int32 block dot products of one weight matrix of one expert
+ * with T rows of int8 activations:
+ *   dots[t][n][b] = sum_{k in [32b, 32b+32)} qw[n][k] * q_act[t][k]
+ *  matrix 0 = gate, 1 = up (K = H, rows = I), 2 = down (K = I, rows = H).
+ *  q_act [T*K] int8, T in [1, 4096];  dots [T*rows*(K/32)] int32.
+ * Computed by the prefill path's int8 matrix-core tile code, for checking it
+ * bit for bit. */
+int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert,
+                        int32_t matrix, const int8_t *q_act, int32_t T,
+                        int32_t *dots, void *stream);
+
+/* Static description of a status code. */
+const char *coli_moe_strerror(int status);
+
+/* Library version, "major.minor.patch". */
+const char *coli_moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLI_MOE_H */

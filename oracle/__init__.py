@@ -1,0 +1,190 @@
+"""CPU oracle of the routed-expert MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package.  It wraps the plain C oracle (coli_oracle.c: loops, fp64
+accumulation, no shared code with the HIP library) with ctypes and numpy.
+
+`build()` compiles liboracle.so next to the source with gcc; the wrappers
+build it on first use if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "coli_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle (gcc, -O2, OpenMP, no FP contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i32, i64, u32, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+    lib.oracle_route.argtypes = [i32, i32, i32, u32, f32, p, p, p, p, p, p, p]
+    lib.oracle_forward_decode.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p]
+    lib.oracle_forward_prefill.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p, p]
+    lib.oracle_quantize_q8_0.argtypes = [p, i64, p, p]
+    lib.oracle_block_dots.argtypes = [i64, i64, i64, i64, p, p, i64, ctypes.c_int, p, i64, p]
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    for f in ("oracle_route", "oracle_forward_decode", "oracle_forward_prefill",
+              "oracle_quantize_q8_0", "oracle_block_dots"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(_LIB)
+    return _lib
+
+
+class use_library:
+    """Context manager: route every wrapper through another build of the
+    oracle (the mutation tests use it to run the pins on broken copies)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = _bind(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def compile_variant(src_text: str, out_path: str) -> str:
+    """Compile C source text (a modified copy of the oracle) to out_path."""
+    c_path = out_path + ".c"
+    with open(c_path, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    "-ffp-contract=off", "-w", "-o", out_path, c_path, "-lm"], check=True)
+    return out_path
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def route(logits, top_k: int, flags: int, routed_scale: float = 1.0, sel_bias=None):
+    """Top-k selection, routing weights and grouping.  logits fp32 [T, E]."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    P = T * top_k
+    out = {
+        "topk_idx": np.zeros(P, np.int32), "topk_w": np.zeros(P, np.float32),
+        "counts": np.zeros(E, np.int32), "offsets": np.zeros(E + 1, np.int32),
+        "pairs": np.zeros(P, np.int32),
+    }
+    sb = None if sel_bias is None else _c(sel_bias, np.float32)
+    rc = lib.oracle_route(T, E, top_k, flags, routed_scale, _ptr(logits), _ptr(sb),
+                          _ptr(out["topk_idx"]), _ptr(out["topk_w"]), _ptr(out["counts"]),
+                          _ptr(out["offsets"]), _ptr(out["pairs"]))
+    if rc != 0:
+        raise ValueError("oracle_route: invalid arguments")
+    out["topk_idx"] = out["topk_idx"].reshape(T, top_k)
+    out["topk_w"] = out["topk_w"].reshape(T, top_k)
+    return out
+
+
+def forward_decode(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16):
+    """Decode-mode layer output, fp64 [T, H].  x_bf16: uint16 bits [T, H]."""
+    lib = _load()
+    q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
+    topk_idx, topk_w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
+    x = _c(x_bf16, np.uint16)
+    T = x.shape[0]
+    y = np.zeros((T, H), np.float64)
+    rc = lib.oracle_forward_decode(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
+                                   _ptr(topk_w), _ptr(x), T, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_forward_decode failed")
+    return y
+
+
+def forward_prefill(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, want_h=False):
+    """Integer-path (Q8_0) layer output, fp64 [T, H] (and fp32 h [T, k+S, I])."""
+    lib = _load()
+    q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
+    topk_idx, topk_w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
+    x = _c(x_bf16, np.uint16)
+    T = x.shape[0]
+    y = np.zeros((T, H), np.float64)
+    h = np.zeros((T, k + S, I), np.float32) if want_h else None
+    rc = lib.oracle_forward_prefill(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
+                                    _ptr(topk_w), _ptr(x), T, _ptr(y), _ptr(h))
+    if rc != 0:
+        raise ValueError("oracle_forward_prefill failed")
+    return (y, h) if want_h else y
+
+
+def quantize_q8_0(v):
+    """Q8_0 of fp32 values (length % 32 == 0) -> (int8 q, uint16 fp16-bits d)."""
+    lib = _load()
+    v = _c(v, np.float32).reshape(-1)
+    q = np.zeros(v.size, np.int8)
+    d = np.zeros(v.size // 32, np.uint16)
+    if lib.oracle_quantize_q8_0(_ptr(v), v.size, _ptr(q), _ptr(d)) != 0:
+        raise ValueError("oracle_quantize_q8_0: length must be a multiple of 32")
+    return q, d
+
+
+def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act):
+    """Exact int32 block dots [T, rows, K/32] of one matrix of one expert."""
+    lib = _load()
+    q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
+    q_act = _c(q_act, np.int8)
+    K = I if matrix == 2 else H
+    rows = H if matrix == 2 else I
+    T = q_act.reshape(-1, K).shape[0]
+    dots = np.zeros((T, rows, K // 32), np.int32)
+    rc = lib.oracle_block_dots(H, I, E, S, _ptr(q4), _ptr(scales), expert, matrix,
+                               _ptr(q_act), T, _ptr(dots))
+    if rc != 0:
+        raise ValueError("oracle_block_dots: invalid arguments")
+    return dots
+
+
+def f32_to_f16_bits(v: float) -> int:
+    return int(_load().oracle_f32_to_f16(float(v)))
+
+
+def threads() -> int:
+    """OpenMP threads the oracle will use (OMP_NUM_THREADS or all cores)."""
+    n = os.environ.get("OMP_NUM_THREADS")
+    return int(n) if n and n.isdigit() else (os.cpu_count() or 1)

@@ -1,0 +1,407 @@
+/*
+ * coli_oracle.c -- plain CPU oracle of the routed-expert MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this file's library.  The product path
+ * never calls it, and it shares no code, header, table or constant with the
+ * HIP library: the container layout and the quantiser below are written out
+ * again here from their definitions.
+ *
+ * Everything is straight loops in the order the definitions read, with fp64
+ * accumulation (built with -ffp-contract=off).  OpenMP splits only
+ * independent output rows / tokens; every sum runs sequentially.
+ *
+ * Definitions followed (web pages about the colibri engine):
+ *  - int4, one fp16 scale per 64 weights ("gs64"): tantan.ink post
+ *    "colibri: 把 744B 模型当数据流...", section "我看到的几个坑".
+ *  - three matrices gate/up/down per expert, each distinct expert read once
+ *    per batch: same post, section "几个关键工程动作".
+ *  - Q8_0-style int8 activations on the integer path: alphamatch.ai blog
+ *    "Colibri：革命性 AI 引擎...", section "優化整數核心".
+ *  - router choice decides the experts: aixq.cc article, section
+ *    "为什么值得关注".
+ * Readings where the pages are silent (routing function, tie order, nibble
+ * order, SwiGLU, the Q8_0 rounding rule) are the ones stated in the library
+ * header and repeated at each function below.
+ *
+ * Pins: every function here is checked by tests against an independent
+ * numpy brute force, closed forms, invariants and hand-derived fixtures.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL -1
+
+/* ---------------------------------------------------------------- numbers */
+
+/* IEEE binary16 bits -> value (exact). */
+static double or_f16(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(m + 1024), e - 25);
+  return sign ? -v : v;
+}
+
+/* bfloat16 bits -> value (exact: the upper half of an IEEE binary32). */
+static double or_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* binary32 -> binary16 bits, round to nearest, ties to even. */
+uint16_t oracle_f32_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  double a = fabs((double)f);
+  if (f != f) return (uint16_t)(sign | 0x7e00u);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u); /* 65520 ties to inf */
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: value = m * 2^-24, m = 0..1024 (1024 = min normal) */
+    double m = nearbyint(a * ldexp(1.0, 24)); /* default mode: ties-to-even */
+    return (uint16_t)(sign | (uint16_t)m);
+  }
+  int e2;
+  frexp(a, &e2);               /* a = f * 2^e2, f in [0.5, 1) */
+  int E = e2 - 1;              /* a in [2^E, 2^(E+1)) */
+  double m = nearbyint(ldexp(a, 10 - E)); /* 11-bit significand in [1024, 2048] */
+  if (m == 2048.0) {
+    m = 1024.0;
+    E += 1;
+  }
+  if (E > 15) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)m - 1024));
+}
+
+/* nibble -> signed int4: two's complement in 4 bits. */
+static int or_nib(uint8_t byte, int high) {
+  int v = high ? (byte >> 4) : (byte & 15);
+  return v >= 8 ? v - 16 : v;
+}
+
+/* weight q[n][k] of a row-major nibble matrix whose rows hold K/2 bytes:
+ * byte k/2, low nibble for even k, high nibble for odd k. */
+static int or_q(const uint8_t *mat, int64_t K, int64_t n, int64_t k) {
+  return or_nib(mat[n * (K / 2) + k / 2], (int)(k & 1));
+}
+
+/* scale s[n][k/64] of a matrix whose rows hold K/64 fp16 scales. */
+static double or_s(const uint16_t *sc, int64_t K, int64_t n, int64_t k) {
+  return or_f16(sc[n * (K / 64) + k / 64]);
+}
+
+/* --------------------------------------------------------------- container */
+
+typedef struct {
+  int64_t H, I, E, S;
+  const uint8_t *q4;      /* host copy of the container */
+  const uint16_t *scales; /* host copy, fp16 bits */
+} or_layer;
+
+/* matrix m (0 gate, 1 up, 2 down) of expert e: nibble base and scale base.
+ * Expert e occupies 3*I*H/2 bytes and 3*I*H/64 scales, matrices in order. */
+static const uint8_t *or_mat(const or_layer *L, int64_t e, int m) {
+  return L->q4 + e * (3 * L->I * L->H / 2) + (int64_t)m * (L->I * L->H / 2);
+}
+static const uint16_t *or_sc(const or_layer *L, int64_t e, int m) {
+  return L->scales + e * (3 * L->I * L->H / 64) + (int64_t)m * (L->I * L->H / 64);
+}
+
+/* ------------------------------------------------------------------ route */
+
+/* Top-k selection, weights and grouping for T tokens.
+ * Selection: score = fp32(logit + sel_bias) (sel_bias may be NULL); the k
+ * largest scores, taken largest first, a tie going to the lower expert index.
+ * Weights (from the raw logits, computed in fp64, stored fp32):
+ *   flags&1 == 0: softmax over all E logits, w_j = p[idx_j];
+ *   flags&1 == 1: w_j = 1/(1+exp(-logit[idx_j]));
+ *   flags&256   : w_j /= sum of the k weights;
+ *   then w_j *= routed_scale.
+ * Grouping (the batch union): counts per expert, exclusive offsets, and the
+ * pair ids p = t*k + j listed expert by expert in ascending p.
+ * Source: aixq.cc article, section "为什么值得关注"; tantan.ink post,
+ * section "几个关键工程动作". */
+int oracle_route(int32_t T, int32_t E, int32_t k, uint32_t flags,
+                 float routed_scale, const float *logits, const float *sel_bias,
+                 int32_t *topk_idx, float *topk_w, int32_t *counts,
+                 int32_t *offsets, int32_t *pairs) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return OR_EINVAL;
+  char *taken = (char *)malloc((size_t)E);
+  double *w = (double *)malloc(sizeof(double) * (size_t)k);
+  if (!taken || !w) {
+    free(taken);
+    free(w);
+    return OR_EINVAL;
+  }
+  for (int32_t t = 0; t < T; ++t) {
+    const float *l = logits + (int64_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      float best_s = 0.0f;
+      for (int32_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        float s = sel_bias ? (float)(l[e] + sel_bias[e]) : l[e];
+        if (best < 0 || s > best_s) { /* strict: earlier (lower) index wins ties */
+          best = e;
+          best_s = s;
+        }
+      }
+      taken[best] = 1;
+      topk_idx[(int64_t)t * k + j] = best;
+    }
+    if ((flags & 1u) == 0) {
+      double mx = l[0];
+      for (int32_t e = 1; e < E; ++e)
+        if (l[e] > mx) mx = l[e];
+      double z = 0.0;
+      for (int32_t e = 0; e < E; ++e) z += exp((double)l[e] - mx);
+      for (int32_t j = 0; j < k; ++j)
+        w[j] = exp((double)l[topk_idx[(int64_t)t * k + j]] - mx) / z;
+    } else {
+      for (int32_t j = 0; j < k; ++j)
+        w[j] = 1.0 / (1.0 + exp(-(double)l[topk_idx[(int64_t)t * k + j]]));
+    }
+    if (flags & 256u) {
+      double sum = 0.0;
+      for (int32_t j = 0; j < k; ++j) sum += w[j];
+      for (int32_t j = 0; j < k; ++j) w[j] /= sum;
+    }
+    for (int32_t j = 0; j < k; ++j)
+      topk_w[(int64_t)t * k + j] = (float)(w[j] * (double)routed_scale);
+  }
+  free(taken);
+  free(w);
+
+  int64_t P = (int64_t)T * k;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[topk_idx[p]] += 1;
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t *fill = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  if (!fill) return OR_EINVAL;
+  for (int32_t e = 0; e < E; ++e) fill[e] = offsets[e];
+  for (int64_t p = 0; p < P; ++p) pairs[fill[topk_idx[p]]++] = (int32_t)p;
+  free(fill);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------- FFN */
+
+static double or_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* Decode-mode expert FFN on one fp64 activation vector x[H]:
+ *   g[n] = sum_k q_g[n][k] s_g[n][k/64] x[k]   (likewise u)
+ *   h[n] = silu(g[n]) * u[n]
+ *   o[m] = sum_n q_d[m][n] s_d[m][n/64] h[n]
+ * SwiGLU is the reading of "gate / up / down" (tantan.ink post, section
+ * "几个关键工程动作"); the pages do not name the activation. */
+static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
+                       double *o) {
+  const int64_t H = L->H, I = L->I;
+  const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
+  const uint16_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  for (int64_t n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int64_t k = 0; k < H; ++k) {
+      g += (double)or_q(qg, H, n, k) * or_s(sg, H, n, k) * x[k];
+      u += (double)or_q(qu, H, n, k) * or_s(su, H, n, k) * x[k];
+    }
+    h[n] = or_silu(g) * u;
+  }
+  for (int64_t m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int64_t n = 0; n < I; ++n)
+      acc += (double)or_q(qd, I, m, n) * or_s(sd, I, m, n) * h[n];
+    o[m] = acc;
+  }
+}
+
+/* Decode-mode layer output for T tokens (x bf16, y fp64 [T][H]):
+ *   y[t] = sum_j topk_w[t][j] * FFN_{topk_idx[t][j]}(x[t]) + [S] FFN_E(x[t])
+ * Each token is computed on its own, so the batch union (which only changes
+ * how often weights are read) does not appear here. */
+int oracle_forward_decode(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
+                          const uint8_t *q4, const uint16_t *scales,
+                          const int32_t *topk_idx, const float *topk_w,
+                          const uint16_t *x_bf16, int64_t T, double *y) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1)
+    return OR_EINVAL;
+  or_layer L = {H, I, E, S, q4, scales};
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t t = 0; t < T; ++t) {
+    double *x = (double *)malloc(sizeof(double) * (size_t)H);
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    double *o = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!x || !h || !o) {
+      bad = 1;
+    } else {
+      for (int64_t i = 0; i < H; ++i) x[i] = or_bf16(x_bf16[t * H + i]);
+      double *yt = y + t * H;
+      for (int64_t i = 0; i < H; ++i) yt[i] = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        int64_t e = topk_idx[t * k + j];
+        double w = (double)topk_w[t * k + j];
+        or_ffn_f64(&L, e, x, h, o);
+        for (int64_t i = 0; i < H; ++i) yt[i] += w * o[i];
+      }
+      if (S) {
+        or_ffn_f64(&L, E, x, h, o);
+        for (int64_t i = 0; i < H; ++i) yt[i] += o[i];
+      }
+    }
+    free(x);
+    free(h);
+    free(o);
+  }
+  return bad ? OR_EINVAL : OR_OK;
+}
+
+/* ------------------------------------------------------------------ Q8_0 */
+
+/* Q8_0 of n fp32 values (n % 32 == 0), per block of 32:
+ *   a = max |v|;  d = a / 127 in fp32;  q = round half away from zero of
+ *   fp32(v / d), clamped to [-127, 127], or 0 when a == 0;  stored scale =
+ *   d rounded to fp16 (nearest-even).
+ * The pages give only "Q8_0-style int8 activations" (alphamatch.ai blog,
+ * section "優化整數核心"); this rounding rule is the reading taken. */
+int oracle_quantize_q8_0(const float *v, int64_t n, int8_t *q, uint16_t *d16) {
+  if (n < 0 || n % 32) return OR_EINVAL;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float *vb = v + 32 * b;
+    float a = 0.0f;
+    for (int i = 0; i < 32; ++i)
+      if (fabsf(vb[i]) > a) a = fabsf(vb[i]);
+    volatile float d = a / 127.0f;
+    d16[b] = oracle_f32_to_f16(d);
+    for (int i = 0; i < 32; ++i) {
+      int r = 0;
+      if (a != 0.0f) {
+        volatile float ratio = vb[i] / d;
+        r = (int)roundf(ratio); /* C roundf: halfway cases away from zero */
+        if (r > 127) r = 127;
+        if (r < -127) r = -127;
+      }
+      q[32 * b + i] = (int8_t)r;
+    }
+  }
+  return OR_OK;
+}
+
+/* Exact int32 dot of one 32-block: weights of row n (nibble matrix with
+ * K/2 bytes per row) against int8 activations a[K], over k in [32b, 32b+32). */
+static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n,
+                            const int8_t *a, int64_t b) {
+  int32_t acc = 0;
+  for (int64_t k = 32 * b; k < 32 * b + 32; ++k) acc += or_q(mat, K, n, k) * (int32_t)a[k];
+  return acc;
+}
+
+/* dots[t][n][b] for matrix m (0 gate, 1 up, 2 down) of expert e. */
+int oracle_block_dots(int64_t H, int64_t I, int64_t E, int64_t S,
+                      const uint8_t *q4, const uint16_t *scales, int64_t e,
+                      int m, const int8_t *q_act, int64_t T, int32_t *dots) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || m < 0 || m > 2 || e < 0 || e >= E + S)
+    return OR_EINVAL;
+  or_layer L = {H, I, E, S, q4, scales};
+  const int64_t K = (m == 2) ? I : H, rows = (m == 2) ? H : I, nb = K / 32;
+  const uint8_t *mat = or_mat(&L, e, m);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t n = 0; n < rows; ++n)
+      for (int64_t b = 0; b < nb; ++b)
+        dots[(t * rows + n) * nb + b] = or_block_dot(mat, K, n, q_act + t * K, b);
+  return OR_OK;
+}
+
+/* Integer-path expert FFN for one Q8_0 activation row (qx[H], dx[H/32]):
+ *   g[n] = sum_b s_g[n][b/2] * d_x[b] * dot_b(q_g[n], q_x)   (likewise u)
+ *   h = fp32(silu(g) * u);  (q_h, d_h) = Q8_0(h)
+ *   o[m] = sum_b s_d[m][b/2] * d_h[b] * dot_b(q_d[m], q_h)
+ * Source: alphamatch.ai blog, section "優化整數核心". */
+static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
+                     const uint16_t *dx, float *hf, int8_t *qh, uint16_t *dh,
+                     double *o) {
+  const int64_t H = L->H, I = L->I;
+  const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
+  const uint16_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  for (int64_t n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int64_t b = 0; b < H / 32; ++b) {
+      double d = or_f16(dx[b]);
+      g += or_f16(sg[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qg, H, n, qx, b);
+      u += or_f16(su[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qu, H, n, qx, b);
+    }
+    hf[n] = (float)(or_silu(g) * u);
+  }
+  if (oracle_quantize_q8_0(hf, I, qh, dh) != OR_OK) return OR_EINVAL;
+  for (int64_t m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int64_t b = 0; b < I / 32; ++b)
+      acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *
+             (double)or_block_dot(qd, I, m, qh, b);
+    o[m] = acc;
+  }
+  return OR_OK;
+}
+
+/* Prefill-mode layer output for T tokens (x bf16, y fp64 [T][H]):
+ * x[t] -> fp32 -> Q8_0, then as decode but with or_ffn_q8 per expert.
+ * If h_out is not NULL it receives the fp32 h of every (token, slot) in
+ * [T][k+S][I] order (slot k = shared expert), for diagnosis in tests. */
+int oracle_forward_prefill(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
+                           const uint8_t *q4, const uint16_t *scales,
+                           const int32_t *topk_idx, const float *topk_w,
+                           const uint16_t *x_bf16, int64_t T, double *y,
+                           float *h_out) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1)
+    return OR_EINVAL;
+  or_layer L = {H, I, E, S, q4, scales};
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t t = 0; t < T; ++t) {
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    int8_t *qx = (int8_t *)malloc((size_t)H);
+    uint16_t *dx = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(H / 32));
+    float *hf = (float *)malloc(sizeof(float) * (size_t)I);
+    int8_t *qh = (int8_t *)malloc((size_t)I);
+    uint16_t *dh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(I / 32));
+    double *o = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!xf || !qx || !dx || !hf || !qh || !dh || !o) {
+      bad = 1;
+    } else {
+      for (int64_t i = 0; i < H; ++i) xf[i] = (float)or_bf16(x_bf16[t * H + i]);
+      if (oracle_quantize_q8_0(xf, H, qx, dx) != OR_OK) bad = 1;
+      double *yt = y + t * H;
+      for (int64_t i = 0; i < H; ++i) yt[i] = 0.0;
+      for (int64_t j = 0; j < k + S && !bad; ++j) {
+        int64_t e = (j < k) ? topk_idx[t * k + j] : E;
+        double w = (j < k) ? (double)topk_w[t * k + j] : 1.0;
+        if (or_ffn_q8(&L, e, qx, dx, hf, qh, dh, o) != OR_OK) bad = 1;
+        if (h_out) memcpy(h_out + (t * (k + S) + j) * I, hf, sizeof(float) * (size_t)I);
+        for (int64_t i = 0; i < H; ++i) yt[i] += w * o[i];
+      }
+    }
+    free(xf);
+    free(qx);
+    free(dx);
+    free(hf);
+    free(qh);
+    free(dh);
+    free(o);
+  }
+  return bad ? OR_EINVAL : OR_OK;
+}

@@ -1,0 +1,147 @@
+"""Dense numpy brute force of the MoE layer, used to pin the oracle.
+
+Written independently of the C oracle: it unpacks every expert of the
+container to dense fp64 matrices with vectorised numpy, runs every expert on
+every token with plain matrix products, and combines them with a dense
+[T, E] routing-weight matrix that is zero for unselected experts.  Top-k uses
+numpy's lexsort and grouping uses a stable argsort.  Small shapes only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def unpack_nibbles(rows_bytes: np.ndarray) -> np.ndarray:
+    """[rows, K/2] uint8 -> [rows, K] int8: even k = low nibble, odd k = high."""
+    b = rows_bytes.astype(np.int16)
+    lo = b & 15
+    hi = b >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((b.shape[0], b.shape[1] * 2), np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def dense_experts(H, I, n, q4, scales):
+    """Dequantised fp64 (Wg [I,H], Wu [I,H], Wd [H,I]) for experts 0..n-1."""
+    q4 = np.asarray(q4, np.uint8)
+    sc = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
+    eb, es = 3 * I * H // 2, 3 * I * H // 64
+    out = []
+    for e in range(n):
+        qe, se = q4[e * eb:(e + 1) * eb], sc[e * es:(e + 1) * es]
+        mats = []
+        for m, (rows, K) in enumerate(((I, H), (I, H), (H, I))):
+            qb = qe[m * (I * H // 2):(m + 1) * (I * H // 2)].reshape(rows, K // 2)
+            sb = se[m * (I * H // 64):(m + 1) * (I * H // 64)].reshape(rows, K // 64)
+            mats.append(unpack_nibbles(qb).astype(np.float64) * np.repeat(sb, 64, axis=1))
+        out.append(tuple(mats))
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def topk(logits, k, sel_bias=None):
+    score = np.asarray(logits, np.float32)
+    if sel_bias is not None:
+        score = (score + np.asarray(sel_bias, np.float32)[None, :]).astype(np.float32)
+    T, E = score.shape
+    idx = np.empty((T, k), np.int32)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -score[t].astype(np.float64)))
+        idx[t] = order[:k]
+    return idx
+
+
+def route_weights(logits, idx, sigmoid, renorm, routed_scale=1.0):
+    l = np.asarray(logits, np.float64)
+    if sigmoid:
+        w = 1.0 / (1.0 + np.exp(-np.take_along_axis(l, idx, axis=1)))
+    else:
+        z = l - l.max(axis=1, keepdims=True)
+        p = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
+        w = np.take_along_axis(p, idx, axis=1)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w * routed_scale
+
+
+def group(idx, E):
+    flat = np.asarray(idx).reshape(-1)
+    pairs = np.argsort(flat, kind="stable").astype(np.int32)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return counts, offsets, pairs
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def decode_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits):
+    x = bf16_to_f64(x_bits)
+    T = x.shape[0]
+    experts = dense_experts(H, I, E + S, q4, scales)
+    wmat = np.zeros((T, E + S))
+    for t in range(T):
+        for j in range(topk_idx.shape[1]):
+            wmat[t, topk_idx[t, j]] += float(np.float32(topk_w[t, j]))
+    if S:
+        wmat[:, E] = 1.0
+    y = np.zeros((T, H))
+    for e, (wg, wu, wd) in enumerate(experts):
+        o = (silu(x @ wg.T) * (x @ wu.T)) @ wd.T
+        y += wmat[:, e:e + 1] * o
+    return y
+
+
+def q8_0(v):
+    """Q8_0 per 32 values: (int8 q, fp16 d) with half-away-from-zero rounding."""
+    v = np.asarray(v, np.float32).reshape(-1, 32)
+    a = np.abs(v).max(axis=1)
+    d = (a / np.float32(127.0)).astype(np.float32)
+    safe = np.where(a == 0, np.float32(1.0), d).astype(np.float32)
+    r = (v / safe[:, None]).astype(np.float32).astype(np.float64)
+    q = np.sign(r) * np.floor(np.abs(r) + 0.5)
+    q = np.clip(q, -127, 127)
+    q[a == 0] = 0
+    return q.astype(np.int8).reshape(-1), d.astype(np.float16)
+
+
+def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits):
+    x32 = bf16_to_f64(x_bits).astype(np.float32)
+    T = x32.shape[0]
+    qx, dx = q8_0(x32)
+    xh = qx.reshape(T, H // 32, 32).astype(np.float64) * dx.astype(np.float64).reshape(T, H // 32, 1)
+    xh = xh.reshape(T, H)
+    experts = dense_experts(H, I, E + S, q4, scales)
+    wmat = np.zeros((T, E + S))
+    for t in range(T):
+        for j in range(topk_idx.shape[1]):
+            wmat[t, topk_idx[t, j]] += float(np.float32(topk_w[t, j]))
+    if S:
+        wmat[:, E] = 1.0
+    y = np.zeros((T, H))
+    for e, (wg, wu, wd) in enumerate(experts):
+        h = (silu(xh @ wg.T) * (xh @ wu.T)).astype(np.float32)
+        qh, dh = q8_0(h)
+        hh = (qh.reshape(T, I // 32, 32).astype(np.float64)
+              * dh.astype(np.float64).reshape(T, I // 32, 1)).reshape(T, I)
+        y += wmat[:, e:e + 1] * (hh @ wd.T)
+    return y
+
+
+def block_dots(H, I, q4, expert, matrix, q_act):
+    eb = 3 * I * H // 2
+    rows, K = ((I, H), (I, H), (H, I))[matrix]
+    qb = np.asarray(q4, np.uint8)[expert * eb + matrix * (I * H // 2):
+                                  expert * eb + (matrix + 1) * (I * H // 2)]
+    w = unpack_nibbles(qb.reshape(rows, K // 2)).astype(np.int64)
+    a = np.asarray(q_act, np.int8).reshape(-1, K).astype(np.int64)
+    T = a.shape[0]
+    prod = w[None, :, :] * a[:, None, :]
+    return prod.reshape(T, rows, K // 32, 32).sum(axis=3).astype(np.int32)

@@ -1,0 +1,76 @@
+"""Plant plausible mistakes in copies of the oracle and check the pins fail.
+
+Each mutant is one textual change of oracle/coli_oracle.c (a dropped term, a
+flipped sign, a wrong index or scale group, a swapped nibble order, a wrong
+rounding rule, ...).  The copy is compiled to a temporary library on the CPU
+and the pin checks of test_oracle_pins.py run against it; at least one check
+must fail for every mutant.  The real oracle is never modified.
+"""
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+CHECKS = [
+    pins.check_f16_rounding, pins.check_q8_0_golden, pins.check_q8_0_vs_bruteforce,
+    pins.check_route_golden, pins.check_route_vs_bruteforce, pins.check_route_invariants,
+    pins.check_decode_vs_bruteforce, pins.check_decode_mean_invariant,
+    pins.check_decode_zero_scales, pins.check_decode_swiglu_mlp, pins.check_decode_closed_form,
+    pins.check_block_dots_vs_bruteforce, pins.check_prefill_vs_bruteforce,
+    pins.check_prefill_zero_scales,
+]
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("nibble order swapped", "int v = high ? (byte >> 4) : (byte & 15);",
+     "int v = high ? (byte & 15) : (byte >> 4);"),
+    ("nibble read unsigned", "return v >= 8 ? v - 16 : v;", "return v;"),
+    ("nibble sign off by one", "return v >= 8 ? v - 16 : v;", "return v > 8 ? v - 16 : v;"),
+    ("scale group of 32", "return or_f16(sc[n * (K / 64) + k / 64]);",
+     "return or_f16(sc[n * (K / 64) + (k / 32) % (K / 64)]);"),
+    ("matrix stride wrong",
+     "return L->q4 + e * (3 * L->I * L->H / 2) + (int64_t)m * (L->I * L->H / 2);",
+     "return L->q4 + e * (3 * L->I * L->H / 2) + (int64_t)m * (L->I * L->H / 4);"),
+    ("up uses gate scales", "*su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {",
+     "*su = or_sc(L, e, 0), *sd = or_sc(L, e, 2);\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {"),
+    ("silu sign flipped", "return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
+    ("gate and up swapped in swiglu", "h[n] = or_silu(g) * u;", "h[n] = or_silu(u) * g;"),
+    ("down transposed", "acc += (double)or_q(qd, I, m, n) * or_s(sd, I, m, n) * h[n];",
+     "acc += (double)or_q(qd, I, n % I, m % I) * or_s(sd, I, m, n) * h[n];"),
+    ("shared expert dropped", "      if (S) {\n        or_ffn_f64(&L, E, x, h, o);", "      if (0) {\n        or_ffn_f64(&L, E, x, h, o);"),
+    ("routing weight ignored", "for (int64_t i = 0; i < H; ++i) yt[i] += w * o[i];\n      }\n      if (S)",
+     "for (int64_t i = 0; i < H; ++i) yt[i] += o[i];\n      }\n      if (S)"),
+    ("tie to higher index", "if (best < 0 || s > best_s) {", "if (best < 0 || s >= best_s) {"),
+    ("selection bias ignored", "float s = sel_bias ? (float)(l[e] + sel_bias[e]) : l[e];", "float s = l[e];"),
+    ("softmax without max shift and wrong sum", "for (int32_t e = 0; e < E; ++e) z += exp((double)l[e] - mx);",
+     "for (int32_t e = 1; e < E; ++e) z += exp((double)l[e] - mx);"),
+    ("renorm skipped", "for (int32_t j = 0; j < k; ++j) w[j] /= sum;", "(void)sum;"),
+    ("routed scale dropped", "(float)(w[j] * (double)routed_scale)", "(float)(w[j])"),
+    ("group order unstable", "for (int64_t p = 0; p < P; ++p) pairs[fill[topk_idx[p]]++] = (int32_t)p;",
+     "for (int64_t p = P - 1; p >= 0; --p) pairs[fill[topk_idx[p]]++] = (int32_t)p;"),
+    ("q8_0 rounds half to even", "r = (int)roundf(ratio);", "r = (int)nearbyintf(ratio);"),
+    ("q8_0 divides by 128", "volatile float d = a / 127.0f;", "volatile float d = a / 128.0f;"),
+    ("q8_0 truncates", "r = (int)roundf(ratio);", "r = (int)ratio;"),
+    ("block dot off by one block", "for (int64_t k = 32 * b; k < 32 * b + 32; ++k)",
+     "for (int64_t k = 32 * b; k < 32 * b + 31; ++k)"),
+    ("prefill weight scale group", "g += or_f16(sg[n * (H / 64) + b / 2]) * d",
+     "g += or_f16(sg[n * (H / 64) + b % (H / 64)]) * d"),
+    ("prefill h not requantised", "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *",
+     "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[0]) *"),
+    ("f16 rounding truncates", "double m = nearbyint(ldexp(a, 10 - E));", "double m = floor(ldexp(a, 10 - E));"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = oracle.source_text()
+    assert src.count(old) == 1, "mutation anchor not found once: " + name
+    lib = oracle.compile_variant(src.replace(old, new), str(tmp_path / "mutant.so"))
+    failed = []
+    with oracle.use_library(lib):
+        for check in CHECKS:
+            try:
+                check()
+            except (AssertionError, ValueError, IndexError):
+                failed.append(check.__name__)
+    assert failed, "no pin caught mutant: " + name

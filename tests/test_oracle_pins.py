@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+Each check compares the oracle with an independent numpy brute force, a
+closed form, an invariant, or a hand-worked fixture under tests/golden/.  The
+checks are plain functions so that test_oracle_mutants.py can rerun them on
+deliberately broken copies of the oracle and see them fail.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import bruteforce as bf
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# Small layer shapes that still cover several 64-groups per row, the shared
+# expert, both routing functions and k > 1.
+SOFTMAX_SMALL = synth.LayerSpec(128, 64, 6, 0, 2, sigmoid=False, renorm=False)
+SIGMOID_SMALL = synth.LayerSpec(192, 128, 5, 1, 3, sigmoid=True, renorm=True)
+TINY = synth.WORKLOADS["tiny"].spec
+
+
+def _host_layer(spec, seed=0):
+    q4, sc = synth.make_weights(spec, seed=seed)
+    return q4.numpy(), synth.f16_bits(sc)
+
+
+def _x_bits(spec, T, seed=0):
+    return synth.bf16_bits(synth.make_x(spec, T, seed=seed))
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ----------------------------------------------------------------- numbers
+
+def check_f16_rounding():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(2000).astype(np.float32) * np.float32(10.0) ** rng.integers(-9, 6, 2000),
+        np.array([0.0, -0.0, 1.0, 65504.0, 65519.0, 65520.0, 1e9, 2.0 ** -24, 2.0 ** -25,
+                  3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1.0 + 2.0 ** -11,
+                  1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0], np.float32),
+    ]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16_bits(v) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_f16_rounding_matches_numpy():
+    check_f16_rounding()
+
+
+# -------------------------------------------------------------------- Q8_0
+
+def check_q8_0_golden():
+    g = json.load(open(os.path.join(GOLDEN, "q8_0_hand.json")))
+    q, d = oracle.quantize_q8_0(np.array(g["blocks"], np.float32).reshape(-1))
+    assert np.array_equal(q, np.array(g["q"], np.int8).reshape(-1))
+    assert np.array_equal(d, np.array(g["d_fp16_bits"], np.uint16))
+
+
+def check_q8_0_vs_bruteforce():
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(32 * 500) * np.repeat(10.0 ** rng.uniform(-6, 4, 500), 32)).astype(np.float32)
+    v[32 * 7:32 * 8] = 0.0  # an all-zero block
+    q, d = oracle.quantize_q8_0(v)
+    qb, db = bf.q8_0(v)
+    assert np.array_equal(q, qb)
+    assert np.array_equal(d, db.view(np.uint16))
+    # properties: |q| <= 127, the max-magnitude element maps to +-127, and
+    # the rounding error is at most half a step of the fp32 scale
+    blocks = v.reshape(-1, 32)
+    qq = q.reshape(-1, 32).astype(np.int32)
+    assert np.abs(qq).max() <= 127
+    for b in range(blocks.shape[0]):
+        a = np.abs(blocks[b]).max()
+        if a == 0:
+            assert not qq[b].any()
+            continue
+        i = int(np.argmax(np.abs(blocks[b])))
+        assert abs(qq[b, i]) == 127
+        dd = np.float32(a / np.float32(127))
+        assert np.all(np.abs(blocks[b].astype(np.float64) - qq[b] * float(dd)) <= 0.5 * float(dd) * (1 + 1e-6))
+
+
+def test_q8_0_golden():
+    check_q8_0_golden()
+
+
+def test_q8_0_vs_bruteforce_and_properties():
+    check_q8_0_vs_bruteforce()
+
+
+# ------------------------------------------------------------------- route
+
+def check_route_golden():
+    g = json.load(open(os.path.join(GOLDEN, "route_hand.json")))
+    lg = np.array(g["logits"], np.float32)
+    r = oracle.route(lg, g["k"], 0)
+    assert np.array_equal(r["topk_idx"], np.array(g["topk_idx"]))
+    assert np.array_equal(r["counts"], np.array(g["counts"]))
+    assert np.array_equal(r["offsets"], np.array(g["offsets"]))
+    assert np.array_equal(r["pairs"], np.array(g["pairs"]))
+    z = 2 * math.exp(0.5) + 2 * math.exp(2.0) + math.exp(-1.0)
+    want0 = [math.exp(2.0) / z, math.exp(2.0) / z, math.exp(0.5) / z]
+    assert np.allclose(r["topk_w"][0], want0, rtol=1e-7, atol=0)
+    assert np.allclose(r["topk_w"][1], [0.2, 0.2, 0.2], rtol=1e-7, atol=0)
+    rs = oracle.route(lg, g["k"], 1 | 256)
+    assert np.allclose(rs["topk_w"][1], [1 / 3] * 3, rtol=1e-7, atol=0)
+    s1 = 1 / (1 + math.exp(-2.0))
+    s0 = 1 / (1 + math.exp(-0.5))
+    assert np.allclose(rs["topk_w"][0], np.array([s1, s1, s0]) / (2 * s1 + s0), rtol=1e-7, atol=0)
+
+
+def check_route_vs_bruteforce():
+    rng = np.random.default_rng(3)
+    for T, E, k in ((37, 8, 2), (50, 64, 8), (20, 256, 8), (9, 5, 5), (3, 300, 17)):
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        lg[:, ::3] = np.round(lg[:, ::3] * 2) / 2  # many exact ties
+        bias = (rng.standard_normal(E) * 0.3).astype(np.float32)
+        for flags in (0, 256, 1, 1 | 256):
+            for sb in (None, bias):
+                r = oracle.route(lg, k, flags, 1.5, sel_bias=sb)
+                idx = bf.topk(lg, k, sb)
+                assert np.array_equal(r["topk_idx"], idx)
+                w = bf.route_weights(lg, idx, flags & 1, flags & 256, 1.5)
+                assert np.allclose(r["topk_w"], w, rtol=2e-7, atol=0)
+                c, o, p = bf.group(idx, E)
+                assert np.array_equal(r["counts"], c)
+                assert np.array_equal(r["offsets"], o)
+                assert np.array_equal(r["pairs"], p)
+
+
+def check_route_invariants():
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal((16, 12)).astype(np.float32)
+    # softmax, k = E: the weights are the full softmax and sum to 1
+    r = oracle.route(lg, 12, 0)
+    assert np.allclose(r["topk_w"].astype(np.float64).sum(1), 1.0, atol=1e-6)
+    # renormalised weights over the top-k sum to 1 for both functions
+    for flags in (256, 1 | 256):
+        r = oracle.route(lg, 4, flags)
+        assert np.allclose(r["topk_w"].astype(np.float64).sum(1), 1.0, atol=1e-6)
+    # equal logits and k = E: every weight is 1/E
+    r = oracle.route(np.full((3, 12), 0.7, np.float32), 12, 0)
+    assert np.allclose(r["topk_w"], 1 / 12, rtol=1e-6)
+    assert np.array_equal(r["topk_idx"], np.tile(np.arange(12), (3, 1)))
+    # a selection bias changes the choice but not the weights' source logits
+    bias = np.zeros(12, np.float32)
+    bias[11] = 100.0
+    r = oracle.route(lg, 2, 1, sel_bias=bias)
+    assert np.all(r["topk_idx"][:, 0] == 11)
+    assert np.allclose(r["topk_w"][:, 0], 1 / (1 + np.exp(-lg[:, 11].astype(np.float64))), rtol=1e-7)
+
+
+def test_route_golden():
+    check_route_golden()
+
+
+def test_route_vs_bruteforce():
+    check_route_vs_bruteforce()
+
+
+def test_route_invariants():
+    check_route_invariants()
+
+
+# ------------------------------------------------------------ decode layer
+
+def _decode_case(spec, T, seed=0, zipf=0.0):
+    q4, sc = _host_layer(spec, seed)
+    lg = synth.make_logits(spec, T, seed=seed, zipf_alpha=zipf).numpy()
+    r = oracle.route(lg, spec.top_k, spec.flags, spec.routed_scale)
+    x = _x_bits(spec, T, seed)
+    return q4, sc, r, x
+
+
+def check_decode_vs_bruteforce():
+    for spec, T in ((TINY, 4), (SOFTMAX_SMALL, 5), (SIGMOID_SMALL, 7)):
+        q4, sc, r, x = _decode_case(spec, T, seed=5, zipf=0.3)
+        s = spec
+        y = oracle.forward_decode(s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k,
+                                  q4, sc, r["topk_idx"], r["topk_w"], x)
+        yb = bf.decode_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
+                             r["topk_idx"], r["topk_w"], x)
+        assert _rel(y, yb) < 1e-10
+
+
+def check_decode_mean_invariant():
+    # k = E, equal logits, softmax: y = mean over experts of FFN_e(x)
+    spec = synth.LayerSpec(128, 64, 4, 0, 4, sigmoid=False, renorm=False)
+    q4, sc = _host_layer(spec, 6)
+    T = 3
+    x = _x_bits(spec, T, 6)
+    r = oracle.route(np.zeros((T, 4), np.float32), 4, 0)
+    y = oracle.forward_decode(128, 64, 4, 0, 4, q4, sc, r["topk_idx"], r["topk_w"], x)
+    outs = []
+    for e in range(4):
+        one = np.zeros((T, 1), np.int32) + e
+        outs.append(oracle.forward_decode(128, 64, 4, 0, 1, q4, sc, one,
+                                          np.ones((T, 1), np.float32), x))
+    assert _rel(y, np.mean(outs, axis=0)) < 1e-12
+
+
+def check_decode_zero_scales():
+    spec = SIGMOID_SMALL
+    q4, sc, r, x = _decode_case(spec, 3, seed=7)
+    y = oracle.forward_decode(spec.hidden, spec.inter, spec.n_experts, spec.n_shared,
+                              spec.top_k, q4, np.zeros_like(sc), r["topk_idx"], r["topk_w"], x)
+    assert np.all(y == 0.0)
+
+
+def check_decode_swiglu_mlp():
+    # E = 1, k = 1, no shared expert: a plain SwiGLU MLP on the dequantised
+    # weights, evaluated with torch's silu in fp64
+    spec = synth.LayerSpec(192, 128, 1, 0, 1, sigmoid=False, renorm=False)
+    q4, sc = _host_layer(spec, 8)
+    T = 4
+    x = _x_bits(spec, T, 8)
+    r = oracle.route(np.zeros((T, 1), np.float32), 1, 0)
+    y = oracle.forward_decode(192, 128, 1, 0, 1, q4, sc, r["topk_idx"], r["topk_w"], x)
+    wg, wu, wd = (torch.from_numpy(m) for m in bf.dense_experts(192, 128, 1, q4, sc)[0])
+    xt = torch.from_numpy(bf.bf16_to_f64(x))
+    want = torch.nn.functional.linear(
+        torch.nn.functional.silu(torch.nn.functional.linear(xt, wg))
+        * torch.nn.functional.linear(xt, wu), wd)
+    assert _rel(y, want.numpy()) < 1e-12
+
+
+def _const_layer(H, I, gate_byte, up_byte, down_byte, s_gate, s_up, s_down):
+    spec = synth.LayerSpec(H, I, 1, 0, 1, sigmoid=False, renorm=False)
+    q4 = np.concatenate([np.full(I * H // 2, gate_byte, np.uint8),
+                         np.full(I * H // 2, up_byte, np.uint8),
+                         np.full(H * I // 2, down_byte, np.uint8)])
+    sc = np.concatenate([np.full(I * H // 64, s_gate, np.float16),
+                         np.full(I * H // 64, s_up, np.float16),
+                         np.full(H * I // 64, s_down, np.float16)]).view(np.uint16)
+    return spec, q4, sc
+
+
+def check_decode_closed_form():
+    # Nibble sign and order, scale grouping and SwiGLU by closed forms.
+    H, I = 128, 64
+    # gate byte 0x0F: even k -> low nibble 0xF = -1, odd k -> high nibble 0
+    # up byte 0x2E: even k -> 0xE = -2, odd k -> 2
+    # down byte 0x31: even n -> 1, odd n -> 3
+    spec, q4, sc = _const_layer(H, I, 0x0F, 0x2E, 0x31, 0.5, 0.25, 2.0)
+    xv = np.where(np.arange(H) % 2 == 0, 1.0, 3.0)  # x = 1 on even k, 3 on odd k
+    x = (xv.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)[None, :]
+    y = oracle.forward_decode(H, I, 1, 0, 1, q4, sc, np.zeros((1, 1), np.int32),
+                              np.ones((1, 1), np.float32), x)
+    g = 0.5 * (H // 2) * (-1 * 1.0)                          # = -32
+    u = 0.25 * (H // 2) * ((-2) * 1.0 + 2 * 3.0)             # = 64
+    h = g / (1 + math.exp(-g)) * u
+    o = 2.0 * (I // 2) * (1 * h + 3 * h)
+    assert np.allclose(y, o, rtol=1e-13, atol=0)
+    # a per-group scale change: scale of group 1 of every gate row doubled
+    sc2 = sc.copy().view(np.float16)
+    sc2[1:I * H // 64:H // 64] = np.float16(1.0)
+    y2 = oracle.forward_decode(H, I, 1, 0, 1, q4, sc2.view(np.uint16), np.zeros((1, 1), np.int32),
+                               np.ones((1, 1), np.float32), x)
+    g2 = 0.5 * 32 * -1 + 1.0 * 32 * -1                       # group 0 at 0.5, group 1 at 1.0
+    h2 = g2 / (1 + math.exp(-g2)) * u
+    assert np.allclose(y2, 2.0 * 32 * 4 * h2, rtol=1e-13, atol=0)
+
+
+def test_decode_vs_bruteforce():
+    check_decode_vs_bruteforce()
+
+
+def test_decode_mean_invariant():
+    check_decode_mean_invariant()
+
+
+def test_decode_zero_scales():
+    check_decode_zero_scales()
+
+
+def test_decode_swiglu_mlp():
+    check_decode_swiglu_mlp()
+
+
+def test_decode_closed_form():
+    check_decode_closed_form()
+
+
+# ----------------------------------------------------- integer (Q8_0) path
+
+def check_block_dots_vs_bruteforce():
+    spec = SIGMOID_SMALL
+    q4, sc = _host_layer(spec, 9)
+    rng = np.random.default_rng(9)
+    for m in (0, 1, 2):
+        K = spec.inter if m == 2 else spec.hidden
+        a = rng.integers(-127, 128, (3, K)).astype(np.int8)
+        a[0, :32] = 127
+        for e in (0, spec.n_total - 1):
+            d = oracle.block_dots(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, q4, sc,
+                                  e, m, a)
+            assert np.array_equal(d, bf.block_dots(spec.hidden, spec.inter, q4, e, m, a))
+    # the full int4 x int8 product table: row 0 of a gate matrix holds the
+    # nibbles 0..15 at k = 0..15; activation row (n, v) is v at k = n only
+    H, I = 64, 64
+    q4t = np.zeros(3 * H * I // 2, np.uint8)
+    nib = np.arange(16, dtype=np.uint8)
+    q4t[:8] = nib[0::2] | (nib[1::2] << 4)
+    vals = np.arange(-127, 128)
+    a = np.zeros((16 * vals.size, H), np.int8)
+    for n in range(16):
+        a[n * vals.size:(n + 1) * vals.size, n] = vals
+    d = oracle.block_dots(H, I, 1, 0, q4t, np.zeros(3 * H * I // 64, np.uint16), 0, 0, a)
+    signed = np.where(nib >= 8, nib.astype(np.int32) - 16, nib.astype(np.int32))
+    want = (signed[:, None] * vals[None, :]).reshape(-1)
+    assert np.array_equal(d[:, 0, 0], want)
+    assert not d[:, 0, 1].any() and not d[:, 1:, :].any()
+    worst = np.full(3 * H * I // 2, 0x88, np.uint8)  # every nibble -8
+    a = np.full((1, H), -127, np.int8)
+    d = oracle.block_dots(H, I, 1, 0, worst, np.zeros(3 * H * I // 64, np.uint16), 0, 0, a)
+    assert np.all(d == 32 * 8 * 127)
+
+
+def check_prefill_vs_bruteforce():
+    for spec, T in ((TINY, 4), (SIGMOID_SMALL, 6)):
+        q4, sc, r, x = _decode_case(spec, T, seed=10, zipf=0.3)
+        s = spec
+        y = oracle.forward_prefill(s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k,
+                                   q4, sc, r["topk_idx"], r["topk_w"], x)
+        yb = bf.prefill_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
+                              r["topk_idx"], r["topk_w"], x)
+        assert _rel(y, yb) < 1e-10
+        # the integer path approximates the decode path to Q8_0 accuracy
+        yd = oracle.forward_decode(s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k,
+                                   q4, sc, r["topk_idx"], r["topk_w"], x)
+        assert 1e-6 < _rel(y, yd) < 5e-2
+
+
+def check_prefill_zero_scales():
+    spec = SIGMOID_SMALL
+    q4, sc, r, x = _decode_case(spec, 3, seed=11)
+    y = oracle.forward_prefill(spec.hidden, spec.inter, spec.n_experts, spec.n_shared,
+                               spec.top_k, q4, np.zeros_like(sc), r["topk_idx"], r["topk_w"], x)
+    assert np.all(y == 0.0)
+
+
+def test_block_dots_vs_bruteforce():
+    check_block_dots_vs_bruteforce()
+
+
+def test_prefill_vs_bruteforce():
+    check_prefill_vs_bruteforce()
+
+
+def test_prefill_zero_scales():
+    check_prefill_zero_scales()
+
+
+# ------------------------------------------------------- container identity
+
+def test_container_sizes_match_the_pages():
+    """One GLM-shaped expert is about 19 MB and 19,456 of them about 370 GB
+    (tantan.ink post on colibri, section 它的核心判断); twelve resident layers
+    of 257 experts are about 58 GB.  These pin gs64 with fp16 scales."""
+    glm = synth.WORKLOADS["glm"].spec
+    assert glm.expert_bytes == 18_874_368
+    assert glm.expert_total_bytes == 20_054_016
+    assert 18.5 < glm.expert_total_bytes / 2**20 < 19.5          # ~19 MB (MiB)
+    assert 350 < 19_456 * glm.expert_total_bytes / 2**30 < 375  # ~370 GB
+    assert 57 < synth.container_gib(glm, 12) < 59               # ~58 GB
+    # per-row scales (the superseded container) would be ~5% smaller
+    assert glm.expert_total_bytes / glm.expert_bytes == pytest.approx(1 + 1 / 16)
+
+
+def test_zipf_counts_shape():
+    """The prefill workload's skew gives per-expert counts of about 0-400."""
+    w = synth.WORKLOADS["glm_prefill"]
+    lg = synth.make_logits(w.spec, 2048, seed=0, zipf_alpha=w.zipf_alpha).numpy()
+    idx = bf.topk(lg, 8)
+    c = np.bincount(idx.reshape(-1), minlength=256)
+    assert c.sum() == 2048 * 8
+    assert 250 <= c.max() <= 500
+    assert c.min() <= 40
