@@ -156,7 +156,7 @@ int coli_moe_route(const coli_moe_layer_t *layer, const float *logits,
                    void *stream);
 
 /* Decode-shaped forward, T in [1, 64] tokens (single-token decode and
- * multi-token verify).  Activations stay bf16 -> fp32; weights are
+ * multi-token verify); needs I <= 15360 (COLI_E_UNSUPPORTED otherwise).  Activations stay bf16 -> fp32; weights are
  * dequantised in registers (w = q*s exactly); products are accumulated in
  * fp32.  For each token t:
  *   y[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t]) + [S] FFN_E(x[t])

@@ -1,0 +1,190 @@
+"""ctypes binding of libcoli_moe.so: argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libcoli_moe.so")
+
+COLI_OK, COLI_E_INVALID, COLI_E_UNSUPPORTED, COLI_E_WORKSPACE, COLI_E_ALIGN, COLI_E_HIP = (
+    0, -1, -2, -3, -4, -5)
+COLI_ROUTE_SOFTMAX, COLI_ROUTE_SIGMOID, COLI_ROUTE_RENORM = 0, 1, 256
+COLI_OUT_BF16, COLI_OUT_F32 = 0, 1
+COLI_SRC_BF16, COLI_SRC_F32 = 0, 1
+COLI_ENTRY_ROUTE, COLI_ENTRY_DECODE, COLI_ENTRY_PREFILL = 0, 1, 2
+
+
+class ColiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s: %s (status %d)" % (fn, coli_moe_strerror(status), status))
+        self.status = status
+
+
+class _LayerC(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("routed_scale", ctypes.c_float),
+        ("q4", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+    ]
+
+
+class _RouteC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_idx", "topk_w", "counts", "offsets", "pairs", "pair_pos", "union_ids", "n_union")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                "libcoli_moe.so is not built (expected at %s); run "
+                "`python -m int4_routed_expert_router_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        P = ctypes.POINTER
+        lib.coli_moe_workspace_bytes.argtypes = [P(_LayerC), i32, i32]
+        lib.coli_moe_workspace_bytes.restype = sz
+        lib.coli_moe_route.argtypes = [P(_LayerC), vp, vp, i32, P(_RouteC), vp, sz, vp]
+        lib.coli_moe_forward_decode.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
+        lib.coli_moe_forward_prefill.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
+        lib.coli_moe_quantize_q8_0.argtypes = [vp, i32, i64, vp, vp, vp]
+        lib.coli_moe_block_dots.argtypes = [P(_LayerC), i32, i32, vp, i32, vp, vp]
+        lib.coli_moe_strerror.argtypes = [ctypes.c_int]
+        lib.coli_moe_strerror.restype = ctypes.c_char_p
+        lib.coli_moe_version.argtypes = []
+        lib.coli_moe_version.restype = ctypes.c_char_p
+        for f in ("coli_moe_route", "coli_moe_forward_decode", "coli_moe_forward_prefill",
+                  "coli_moe_quantize_q8_0", "coli_moe_block_dots"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Layer:
+    """One MoE layer: shape, routing kind and the device int4 gs64 container.
+
+    q4: uint8 tensor of (E+S)*3*I*H/2 bytes; scales: fp16 tensor of
+    (E+S)*3*I*H/64 values (see include/coli_moe.h for the byte layout).
+    """
+
+    def __init__(self, hidden, inter, n_experts, n_shared, top_k, flags, q4, scales,
+                 routed_scale=1.0):
+        self.q4, self.scales = q4, scales  # keep the tensors alive
+        self.c = _LayerC(hidden, inter, n_experts, n_shared, top_k, flags, routed_scale,
+                         _ptr(q4), _ptr(scales))
+
+    @classmethod
+    def from_spec(cls, spec, q4, scales):
+        return cls(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, spec.top_k,
+                   spec.flags, q4, scales, spec.routed_scale)
+
+    hidden = property(lambda s: s.c.hidden)
+    inter = property(lambda s: s.c.inter)
+    n_experts = property(lambda s: s.c.n_experts)
+    n_shared = property(lambda s: s.c.n_shared)
+    top_k = property(lambda s: s.c.top_k)
+
+
+class Route:
+    """Device buffers written by coli_moe_route for up to `max_tokens` tokens."""
+
+    def __init__(self, layer: Layer, max_tokens: int, device="cuda"):
+        P = max_tokens * layer.top_k
+        E = layer.n_experts
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty(P, **i32)
+        self.topk_w = torch.empty(P, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.pairs = torch.empty(P, **i32)
+        self.pair_pos = torch.empty(P, **i32)
+        self.union_ids = torch.empty(E, **i32)
+        self.n_union = torch.empty(1, **i32)
+        self.c = _RouteC(*[_ptr(getattr(self, n)) for n, _ in _RouteC._fields_])
+
+
+def coli_moe_strerror(status: int) -> str:
+    return _load().coli_moe_strerror(status).decode()
+
+
+def coli_moe_version() -> str:
+    return _load().coli_moe_version().decode()
+
+
+def coli_moe_workspace_bytes(layer: Layer, T: int, entry: int) -> int:
+    return int(_load().coli_moe_workspace_bytes(ctypes.byref(layer.c), T, entry))
+
+
+def workspace(layer: Layer, T: int, entry: int, device="cuda") -> torch.Tensor:
+    """A device buffer large enough for `entry` at T tokens (256-byte aligned)."""
+    n = coli_moe_workspace_bytes(layer, T, entry)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _check(fn, rc):
+    if rc != COLI_OK:
+        raise ColiError(fn, rc)
+
+
+def coli_moe_route(layer: Layer, logits, sel_bias, T: int, route: Route, ws=None, stream=None):
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("coli_moe_route", _load().coli_moe_route(
+        ctypes.byref(layer.c), _ptr(logits), _ptr(sel_bias), T, ctypes.byref(route.c),
+        _ptr(ws), nb, _stream(stream)))
+
+
+def coli_moe_forward_decode(layer: Layer, route: Route, x, T: int, y, y_dtype: int, ws,
+                            stream=None):
+    _check("coli_moe_forward_decode", _load().coli_moe_forward_decode(
+        ctypes.byref(layer.c), ctypes.byref(route.c), _ptr(x), T, _ptr(y), y_dtype,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def coli_moe_forward_prefill(layer: Layer, route: Route, x, T: int, y, y_dtype: int, ws,
+                             stream=None):
+    _check("coli_moe_forward_prefill", _load().coli_moe_forward_prefill(
+        ctypes.byref(layer.c), ctypes.byref(route.c), _ptr(x), T, _ptr(y), y_dtype,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def coli_moe_quantize_q8_0(src, src_dtype: int, n: int, q, d, stream=None):
+    _check("coli_moe_quantize_q8_0", _load().coli_moe_quantize_q8_0(
+        _ptr(src), src_dtype, n, _ptr(q), _ptr(d), _stream(stream)))
+
+
+def coli_moe_block_dots(layer: Layer, expert: int, matrix: int, q_act, T: int, dots,
+                        stream=None):
+    _check("coli_moe_block_dots", _load().coli_moe_block_dots(
+        ctypes.byref(layer.c), expert, matrix, _ptr(q_act), T, _ptr(dots), _stream(stream)))
+
+
+def raw_library():
+    """The loaded ctypes library (tests use it to check exported symbols)."""
+    return _load()

@@ -1,0 +1,54 @@
+// internal.h -- host-side declarations shared by the library's source files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "coli_moe.h"
+
+namespace coli {
+
+// A validated copy of the layer description with derived sizes.
+struct Layer {
+  int H, I, E, S, k;
+  uint32_t flags;
+  float routed_scale;
+  const uint8_t *q4;
+  const uint16_t *scales;
+  int64_t expert_bytes;   // 3*I*H/2
+  int64_t expert_scales;  // 3*I*H/64
+};
+
+// Workspace carving: every region 256-byte aligned.
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+// Upper bound of distinct routed experts in a batch of T tokens.
+inline int max_union(const Layer &L, int T) {
+  long long p = (long long)T * L.k;
+  return (int)(p < L.E ? p : L.E);
+}
+
+// Rows of the pair-major intermediate buffers: T*k routed pairs, then T
+// shared-expert rows.
+inline int64_t pair_rows(const Layer &L, int T) { return (int64_t)T * (L.k + L.S); }
+
+size_t decode_workspace(const Layer &L, int T);
+size_t prefill_workspace(const Layer &L, int T);
+
+int launch_route(const Layer &L, const float *logits, const float *sel_bias, int T,
+                 const coli_moe_route_t &r, hipStream_t s);
+int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                  void *y, int y_dtype, void *ws, hipStream_t s);
+int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                   void *y, int y_dtype, void *ws, hipStream_t s);
+void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int k, int S,
+                    void *y, int y_dtype, hipStream_t s);
+int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *d,
+                         hipStream_t s);
+int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_act, int T,
+                      int32_t *dots, hipStream_t s);
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_E_HIP; }
+
+}  // namespace coli

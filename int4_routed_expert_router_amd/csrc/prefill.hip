@@ -1,0 +1,589 @@
+// prefill.hip -- prefill / large-batch forward on the integer path.
+//
+// The integer kernel of the reference engine takes Q8_0-style int8
+// activations (alphamatch.ai blog on colibri, section "優化整數核心"), and
+// prefill runs the MoE as a batched union (same blog, section "技術卓越").
+// Here that contraction runs on gfx950's int8 matrix cores:
+//
+//  quantize : x (bf16) -> Q8_0 int8 + fp16 scale per 32 values.
+//  plan     : the batch union becomes a list of (expert, 64-token tile).
+//  gemm     : one work item = (token tile, 64 output channels of gate AND
+//             up, or 128 rows of down).  Per 64-deep K step the workgroup
+//             stages 128 weight rows (int4 -> int8 x16, exact) and 64 token
+//             rows of int8 activations in LDS in matrix-core operand order,
+//             then every wavefront issues v_mfma_i32_16x16x32_i8, one per
+//             32-value block so each block's exact int32 dot stays separate.
+//             The accumulator input is the bit pattern of 1.5*2^23, so the
+//             int32 result read as fp32 is 1.5*2^23 + 16*dot exactly; one FMA
+//             with the activation scale removes the offset and scales the
+//             block, a second applies the weight group's scale.
+//             gate/up epilogue: h = silu(g)*u, then Q8_0 of h per 32
+//             channels (one wavefront holds exactly one block per token).
+//             down epilogue: fp32 o rows.
+//  combine  : shared with decode (fixed-order weighted sum).
+#include "device_common.h"
+#include "internal.h"
+
+namespace coli {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BM = 64;    // tokens per tile
+constexpr int BR = 128;   // weight rows per tile
+constexpr int BK = 64;    // reduction depth per step (one weight scale group)
+constexpr uint32_t kMagic = 0x4B400000u;  // bits of 1.5 * 2^23
+constexpr float kMagicF = 12582912.0f;
+
+enum Mode { kGateUp = 0, kDown = 1, kDots = 2 };
+
+// --------------------------------------------------------------- Q8_0
+
+// Quantise 32 fp32 values held by one thread: q (natural order) and fp16 d.
+// d = max|v| / 127 (correctly rounded division), q = round half away from
+// zero of v / d, clamped to +-127; all-zero blocks give d = 0, q = 0.
+COLI_DEV void q8_0_block(const float v[32], uint32_t qw[8], uint16_t &d16) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+  const float d = __fdiv_rn(a, 127.0f);
+  d16 = f32_to_f16_bits(d);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int q = 0;
+      if (a != 0.0f) {
+        q = (int)roundf(__fdiv_rn(v[4 * w + j], d));
+        q = max(-127, min(127, q));
+      }
+      packed |= (uint32_t)(q & 0xff) << (8 * j);
+    }
+    qw[w] = packed;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) quantize_kernel(const void *__restrict__ src,
+                                                            int src_dtype, int64_t nblocks,
+                                                            int8_t *__restrict__ q,
+                                                            uint16_t *__restrict__ d) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblocks) return;
+  float v[32];
+  if (src_dtype == COLI_SRC_BF16) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(src) + 4 * b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = p[i];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = bf16_to_f32(w[j] & 0xffffu);
+        v[8 * i + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
+      }
+    }
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(src) + 8 * b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 f = p[i];
+      v[4 * i] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  }
+  uint32_t qw[8];
+  uint16_t d16;
+  q8_0_block(v, qw, d16);
+  uint4 *qo = reinterpret_cast<uint4 *>(q) + 2 * b;
+  qo[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+  qo[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
+  d[b] = d16;
+}
+
+// ---------------------------------------------------------------- plan
+
+// A tile of up to BM tokens of one expert.  `row0` is the first pair-major
+// row (h / o rows); routed tiles read token ids from route.pairs, shared
+// tiles (expert == E) use tokens row0 - T*k onwards.
+struct TileDesc {
+  int expert, row0, ntok, pad;
+};
+
+__global__ void __launch_bounds__(1024) plan_kernel(coli_moe_route_t r, int T, int k, int E,
+                                                    int S, int4 *__restrict__ tiles,
+                                                    int *__restrict__ ntiles) {
+  __shared__ int wsum[16];
+  __shared__ int total;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nu = r.n_union[0];
+  const int shared_tiles = S ? (T + BM - 1) / BM : 0;
+  int base_off = shared_tiles;
+  for (int u0 = 0; u0 < nu; u0 += 1024) {
+    const int u = u0 + tid;
+    int e = 0, cnt = 0, off = 0;
+    if (u < nu) {
+      e = r.union_ids[u];
+      cnt = r.counts[e];
+      off = r.offsets[e];
+    }
+    const int nt = (cnt + BM - 1) / BM;
+    int inc = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += n;
+    }
+    if (lane == 63) wsum[wid] = inc;
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int i = 0; i < 16; ++i) {
+        const int t = wsum[i];
+        wsum[i] = acc;
+        acc += t;
+      }
+      total = acc;
+    }
+    __syncthreads();
+    const int first = base_off + wsum[wid] + inc - nt;
+    for (int j = 0; j < nt; ++j)
+      tiles[first + j] = make_int4(e, off + BM * j, min(BM, cnt - BM * j), 0);
+    base_off += total;
+    __syncthreads();
+  }
+  for (int j = tid; j < shared_tiles; j += 1024)
+    tiles[j] = make_int4(E, T * k + BM * j, min(BM, T - BM * j), 0);
+  if (tid == 0) ntiles[0] = base_off;
+}
+
+// ---------------------------------------------------------------- GEMM
+
+// LDS stage: operands already in matrix-core lane order.
+struct Stage {
+  uint2 w[BR / 16][2][64];  // [row tile][32-block][lane] 8 int8 (x16) weights
+  uint2 a[BM / 16][2][64];  // [token tile][32-block][lane] 8 int8 activations
+  float sw[BR];             // weight group scale of each row
+  float4 sa[BM];            // per token: d0/16, -M*d0/16, d1/16, -M*d1/16
+};
+
+struct GemmArgs {
+  const uint8_t *wq;       // nibble matrix base (rows x K/2)
+  const uint16_t *ws;      // its scales (rows x K/64)
+  int rows;                // rows of this matrix (I or H)
+  int K;                   // reduction length
+  const int8_t *act;       // activation rows [*, K] (natural k order)
+  const uint16_t *act_d;   // their fp16 scales [*, K/32]
+  int64_t up_offset_q;     // gate/up: byte offset of the up matrix from gate
+  int64_t up_offset_s;     // and of its scales
+};
+
+// Row source of weight row r (0..BR-1) of a tile starting at n0.
+template <int MODE>
+COLI_DEV void weight_row(const GemmArgs &g, int n0, int r, const uint8_t *&q,
+                         const uint16_t *&s, bool &valid) {
+  int n;
+  int64_t oq = 0, os = 0;
+  if (MODE == kGateUp) {
+    n = n0 + (r & 63);
+    if (r >= 64) {
+      oq = g.up_offset_q;
+      os = g.up_offset_s;
+    }
+  } else {
+    n = n0 + r;
+  }
+  valid = n < g.rows;
+  const int nn = valid ? n : 0;
+  q = g.wq + oq + (int64_t)nn * (g.K / 2);
+  s = g.ws + os + (int64_t)nn * (g.K / 64);
+}
+
+// Global -> registers for K step ks.
+struct Prefetch {
+  uint4 w;      // 16 bytes of nibbles (32 values, one 32-block)
+  uint4 a;      // 16 bytes of int8 activations
+  uint16_t sc;  // a weight scale (threads 0..127) or an activation scale
+};
+
+template <int MODE>
+COLI_DEV void load_step(const GemmArgs &g, int n0, const int *rowid, int ntok, int ks,
+                        Prefetch &p) {
+  const int t = threadIdx.x;
+  {  // weights: row t/2, block t%2
+    const uint8_t *q;
+    const uint16_t *s;
+    bool v;
+    weight_row<MODE>(g, n0, t >> 1, q, s, v);
+    p.w = v ? *reinterpret_cast<const uint4 *>(q + ks * (BK / 2) + 16 * (t & 1))
+            : make_uint4(0, 0, 0, 0);
+  }
+  {  // activations: token t/4, 16-byte quarter t%4
+    const int m = t >> 2;
+    p.a = m < ntok ? *reinterpret_cast<const uint4 *>(g.act + (int64_t)rowid[m] * g.K + ks * BK +
+                                                      16 * (t & 3))
+                   : make_uint4(0, 0, 0, 0);
+  }
+  if (t < BR) {
+    const uint8_t *q;
+    const uint16_t *s;
+    bool v;
+    weight_row<MODE>(g, n0, t, q, s, v);
+    p.sc = v ? s[ks] : (uint16_t)0;
+  } else {
+    const int m = (t - BR) >> 1, b = (t - BR) & 1;
+    p.sc = (m < ntok && g.act_d) ? g.act_d[(int64_t)rowid[m] * (g.K / 32) + 2 * ks + b]
+                                 : (uint16_t)0;
+  }
+}
+
+COLI_DEV void store_step(const Prefetch &p, Stage &st) {
+  const int t = threadIdx.x;
+  {  // 32 nibbles -> 32 int8 (x16), natural k order, into 4 lanes' slots
+    const int r = t >> 1, blk = t & 1, rt = r >> 4, rr = r & 15;
+    const uint32_t w[4] = {p.w.x, p.w.y, p.w.z, p.w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t even = (w[i] << 4) & 0xf0f0f0f0u;  // k 0,2,4,6 (x16)
+      const uint32_t odd = w[i] & 0xf0f0f0f0u;          // k 1,3,5,7 (x16)
+      const uint32_t lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);
+      st.w[rt][blk][rr + 16 * i] = make_uint2(lo, hi);
+    }
+  }
+  {  // activations: token m, k [16*qq, 16*qq+16) of the step
+    const int m = t >> 2, qq = t & 3, mt = m >> 4, mm = m & 15;
+    const int blk = qq >> 1, j0 = 2 * (qq & 1);
+    st.a[mt][blk][mm + 16 * j0] = make_uint2(p.a.x, p.a.y);
+    st.a[mt][blk][mm + 16 * (j0 + 1)] = make_uint2(p.a.z, p.a.w);
+  }
+  if (t < BR) {
+    st.sw[t] = f16_to_f32(p.sc);
+  } else {
+    const int m = (t - BR) >> 1, b = (t - BR) & 1;
+    const float ds = f16_to_f32(p.sc) * 0.0625f;
+    float *sa = reinterpret_cast<float *>(&st.sa[m]);
+    sa[2 * b] = ds;
+    sa[2 * b + 1] = -kMagicF * ds;
+  }
+}
+
+COLI_DEV coli_i32x4 mfma_i8(uint2 a, uint2 b, coli_i32x4 c) {
+  const long la = (long)(((uint64_t)a.y << 32) | a.x);
+  const long lb = (long)(((uint64_t)b.y << 32) | b.x);
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(la, lb, c, 0, 0, 0);
+}
+
+// Row tiles of a wave: gate/up waves (wn) own gate tiles {2wn, 2wn+1} and up
+// tiles {4+2wn, 4+2wn+1}; down/dots waves own tiles {4wn .. 4wn+3}.
+template <int MODE>
+COLI_DEV int wave_row_tile(int wn, int a) {
+  return MODE == kGateUp ? (a < 2 ? 2 * wn + a : 4 + 2 * wn + (a - 2)) : 4 * wn + a;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g, coli_moe_route_t r,
+                                                        const int4 *__restrict__ tiles,
+                                                        const int *__restrict__ ntiles_p,
+                                                        int fixed_ntok, int fixed_expert,
+                                                        int T, int k, int n_ntiles,
+                                                        int64_t expert_stride_q,
+                                                        int64_t expert_stride_s,
+                                                        int8_t *__restrict__ qh_out,
+                                                        uint16_t *__restrict__ dh_out,
+                                                        float *__restrict__ o_out,
+                                                        int32_t *__restrict__ dots_out) {
+  __shared__ Stage st[2];
+  __shared__ int rowid[BM];
+  __shared__ int outrow[BM];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid >> 1, wm = wid & 1;
+  const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
+  const int items = ntiles * n_ntiles;
+  const int nsteps = g.K / BK;
+  // XCD-aware order: consecutive virtual ids (same weights) on one XCD
+  const int G = gridDim.x;
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  for (int item = vid; item < items; item += G) {
+    const int tile = item / n_ntiles, ntile = item % n_ntiles;
+    int expert, row0, ntok;
+    if (tiles) {
+      const int4 td = tiles[tile];
+      expert = td.x;
+      row0 = td.y;
+      ntok = td.z;
+    } else {
+      expert = fixed_expert;
+      row0 = tile * BM;
+      ntok = min(BM, fixed_ntok - row0);
+    }
+    const int n0 = ntile * (MODE == kGateUp ? 64 : BR);
+    __syncthreads();
+    if (threadIdx.x < BM) {
+      const int m = threadIdx.x;
+      int rid = 0, orow = 0;
+      if (m < ntok) {
+        orow = row0 + m;
+        if (MODE == kGateUp) {
+          rid = (row0 >= T * k) ? (row0 - T * k) + m : r.pairs[row0 + m] / k;
+        } else {
+          rid = row0 + m;
+        }
+      }
+      rowid[m] = rid;
+      outrow[m] = orow;
+    }
+    __syncthreads();
+    GemmArgs ge = g;
+    ge.wq = g.wq + (int64_t)expert * expert_stride_q;
+    ge.ws = g.ws + (int64_t)expert * expert_stride_s;
+
+    float acc[8][4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[a][i] = 0.0f;
+    const coli_i32x4 magic = {(int)kMagic, (int)kMagic, (int)kMagic, (int)kMagic};
+
+    Prefetch pf;
+    load_step<MODE>(ge, n0, rowid, ntok, 0, pf);
+    store_step(pf, st[0]);
+    __syncthreads();
+    for (int ks = 0; ks < nsteps; ++ks) {
+      Stage &cur = st[ks & 1];
+      if (ks + 1 < nsteps) load_step<MODE>(ge, n0, rowid, ntok, ks + 1, pf);
+      // 4 row tiles x 2 token tiles x 2 blocks
+      coli_i32x4 d[2][8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        uint2 bop[2];
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) bop[ms] = cur.a[2 * wm + ms][blk][lane];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const uint2 aop = cur.w[wave_row_tile<MODE>(wn, a)][blk][lane];
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms) d[blk][a * 2 + ms] = mfma_i8(aop, bop[ms], magic);
+        }
+      }
+      if (MODE == kDots) {
+        // exact block dots: (bits - magic) / 16, written [token][row][block]
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms) {
+            const int m = 32 * wm + 16 * ms + (lane & 15);
+            if (m >= ntok) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int n = n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
+              if (n >= g.rows) continue;
+              int32_t *dst = dots_out + ((int64_t)(row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks;
+              dst[0] = (d[0][a * 2 + ms][i] - (int)kMagic) >> 4;
+              dst[1] = (d[1][a * 2 + ms][i] - (int)kMagic) >> 4;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+          const float4 sa = cur.sa[32 * wm + 16 * ms + (lane & 15)];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float4 sw = *reinterpret_cast<const float4 *>(
+                &cur.sw[16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
+            const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float t0 = fmaf(__int_as_float(d[0][a * 2 + ms][i]), sa.x, sa.y);
+              const float t1 = fmaf(__int_as_float(d[1][a * 2 + ms][i]), sa.z, sa.w);
+              acc[a * 2 + ms][i] = fmaf(swv[i], t0 + t1, acc[a * 2 + ms][i]);
+            }
+          }
+        }
+      }
+      if (ks + 1 < nsteps) store_step(pf, st[(ks + 1) & 1]);
+      __syncthreads();
+    }
+
+    if (MODE == kGateUp) {
+      // acc[0..3] = gate tiles (ns = a / 2 ... ) laid out as a*2+ms with a in
+      // {0,1} gate and {2,3} up for row sub-tiles ns = a & 1.
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const int m = 32 * wm + 16 * ms + (lane & 15);
+        float hv[2][4];
+        float amax = 0.0f;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[ns][i] = silu_mul(acc[ns * 2 + ms][i], acc[(2 + ns) * 2 + ms][i]);
+            amax = fmaxf(amax, fabsf(hv[ns][i]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const float dq = __fdiv_rn(amax, 127.0f);
+        uint32_t qw[2];
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int q = 0;
+            if (amax != 0.0f) {
+              q = (int)roundf(__fdiv_rn(hv[ns][i], dq));
+              q = max(-127, min(127, q));
+            }
+            packed |= (uint32_t)(q & 0xff) << (8 * i);
+          }
+          qw[ns] = packed;
+        }
+        if (m < ntok) {
+          const int I = g.rows;
+          const int ch = n0 + 32 * wn;  // first channel of this wave's block
+          if (ch < I) {
+            int8_t *qrow = qh_out + (int64_t)outrow[m] * I + ch;
+            *reinterpret_cast<uint32_t *>(qrow + 4 * (lane >> 4)) = qw[0];
+            *reinterpret_cast<uint32_t *>(qrow + 16 + 4 * (lane >> 4)) = qw[1];
+            if ((lane >> 4) == 0) dh_out[(int64_t)outrow[m] * (I / 32) + ch / 32] = f32_to_f16_bits(dq);
+          }
+        }
+      }
+    } else if (MODE == kDown) {
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const int m = 32 * wm + 16 * ms + (lane & 15);
+        if (m >= ntok) continue;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int n = n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4);
+          if (n < g.rows)
+            *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
+                make_float4(acc[a * 2 + ms][0], acc[a * 2 + ms][1], acc[a * 2 + ms][2],
+                            acc[a * 2 + ms][3]);
+        }
+      }
+    }
+  }
+}
+
+struct PrefillWs {
+  int8_t *qx;
+  uint16_t *dx;
+  int8_t *qh;
+  uint16_t *dh;
+  float *o;
+  int4 *tiles;
+  int *ntiles;
+  size_t total;
+};
+
+int max_tiles(const Layer &L, int T) {
+  const int64_t P = (int64_t)T * L.k;
+  return (int)(P / BM + max_union(L, T) + (L.S ? (T + BM - 1) / BM : 0) + 1);
+}
+
+PrefillWs carve(const Layer &L, int T, void *base) {
+  PrefillWs w{};
+  const int64_t rows = pair_rows(L, T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return reinterpret_cast<char *>(base) + o;
+  };
+  w.qx = reinterpret_cast<int8_t *>(take((size_t)T * L.H));
+  w.dx = reinterpret_cast<uint16_t *>(take((size_t)T * (L.H / 32) * 2));
+  w.qh = reinterpret_cast<int8_t *>(take((size_t)rows * L.I));
+  w.dh = reinterpret_cast<uint16_t *>(take((size_t)rows * (L.I / 32) * 2));
+  w.o = reinterpret_cast<float *>(take((size_t)rows * L.H * 4));
+  w.tiles = reinterpret_cast<int4 *>(take((size_t)max_tiles(L, T) * sizeof(int4)));
+  w.ntiles = reinterpret_cast<int *>(take(sizeof(int)));
+  w.total = off;
+  return w;
+}
+
+// grid size: one workgroup per item up to a cap, a multiple of 8 so the
+// XCD-aware remap of workgroup ids is a bijection
+int grid_for(int64_t items) {
+  const int64_t g = items < 16384 ? items : 16384;
+  return (int)((g + 7) / 8 * 8);
+}
+
+}  // namespace
+
+size_t prefill_workspace(const Layer &L, int T) { return carve(L, T, nullptr).total; }
+
+int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *d,
+                         hipStream_t s) {
+  const int64_t nb = n / 32;
+  const int64_t grid = (nb + kThreads - 1) / kThreads;
+  quantize_kernel<<<dim3((unsigned)grid), kThreads, 0, s>>>(src, src_dtype, nb, q, d);
+  return hip_status(hipGetLastError());
+}
+
+int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T, void *y,
+                   int y_dtype, void *ws, hipStream_t s) {
+  const PrefillWs w = carve(L, T, ws);
+  int rc = launch_quantize_q8_0(x, COLI_SRC_BF16, (int64_t)T * L.H, w.qx, w.dx, s);
+  if (rc) return rc;
+  plan_kernel<<<1, 1024, 0, s>>>(r, T, L.k, L.E, L.S, w.tiles, w.ntiles);
+  if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  const int mt = max_tiles(L, T);
+  {  // gate / up + SwiGLU + Q8_0(h)
+    GemmArgs g{};
+    g.wq = L.q4;
+    g.ws = L.scales;
+    g.rows = L.I;
+    g.K = L.H;
+    g.act = w.qx;
+    g.act_d = w.dx;
+    g.up_offset_q = (int64_t)L.I * L.H / 2;
+    g.up_offset_s = (int64_t)L.I * L.H / 64;
+    const int nn = (L.I + 63) / 64;
+    gemm_kernel<kGateUp><<<grid_for((int64_t)mt * nn), kThreads, 0, s>>>(
+        g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh,
+        nullptr, nullptr);
+    if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  }
+  {  // down
+    GemmArgs g{};
+    g.wq = L.q4 + (int64_t)L.I * L.H;
+    g.ws = L.scales + (int64_t)2 * L.I * L.H / 64;
+    g.rows = L.H;
+    g.K = L.I;
+    g.act = w.qh;
+    g.act_d = w.dh;
+    const int nn = (L.H + BR - 1) / BR;
+    gemm_kernel<kDown><<<grid_for((int64_t)mt * nn), kThreads, 0, s>>>(
+        g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr,
+        nullptr, w.o, nullptr);
+    if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  }
+  launch_combine(w.o, r, T, L.H, L.k, L.S, y, y_dtype, s);
+  return hip_status(hipGetLastError());
+}
+
+int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_act, int T,
+                      int32_t *dots, hipStream_t s) {
+  GemmArgs g{};
+  const int64_t moff = (int64_t)matrix * L.I * L.H / 2;
+  g.wq = L.q4 + moff;
+  g.ws = L.scales + (int64_t)matrix * L.I * L.H / 64;
+  g.rows = matrix == 2 ? L.H : L.I;
+  g.K = matrix == 2 ? L.I : L.H;
+  g.act = q_act;
+  g.act_d = nullptr;
+  const int nn = (g.rows + BR - 1) / BR;
+  const int ntile = (T + BM - 1) / BM;
+  coli_moe_route_t none{};
+  gemm_kernel<kDots><<<grid_for((int64_t)ntile * nn), kThreads, 0, s>>>(
+      g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes, L.expert_scales, nullptr,
+      nullptr, nullptr, dots);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace coli

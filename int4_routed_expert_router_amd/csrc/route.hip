@@ -1,0 +1,259 @@
+// route.hip -- router top-k, routing weights and the batch-union grouping.
+//
+// The router's choice decides which experts a token uses (aixq.cc article on
+// colibri, section "为什么值得关注"), and a batch reads every distinct expert
+// once (tantan.ink post on colibri, section "几个关键工程动作").  Selection
+// and grouping are exact: only fp32 comparisons and integer counts, so the
+// indices and pair lists are bit-identical to any correct implementation.
+//
+// Kernels
+//  topk  : one wavefront per token; each lane holds E/64 scores; k rounds of
+//          a wave-wide (score desc, index asc) argmax.  Weights in fp32.
+//  group : one 1024-thread workgroup; LDS histogram, LDS scan, then a stable
+//          scatter whose in-expert rank comes from per-64-token bit masks:
+//          rank(t, e) = #tokens before t (in the batch) that chose e.
+//  fused : topk + group in one workgroup for T <= 16 (decode / verify).
+#include <float.h>
+#include <limits.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace coli {
+namespace {
+
+constexpr int kGroupThreads = 1024;
+constexpr int kMaskWords = 4096;  // 64-token masks held in LDS at once
+
+// ---------------------------------------------------------------- top-k
+
+template <int NPL>
+__device__ void topk_token(const float *__restrict__ lg_row, const float *__restrict__ bias,
+                           int E, int k, uint32_t flags, float routed_scale,
+                           int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  float lg[NPL], sc[NPL];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      lg[i] = lg_row[e];
+      float s = bias ? lg[i] + bias[e] : lg[i];
+      sc[i] = (s != s) ? -FLT_MAX * 2.0f : s;  // NaN sorts last (inputs should be finite)
+    } else {
+      lg[i] = 0.0f;
+      sc[i] = 0.0f;
+      taken |= 1u << i;
+    }
+  }
+  float m = -FLT_MAX, z = 0.0f;
+  if ((flags & COLI_ROUTE_SIGMOID) == 0) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (!((taken >> i) & 1u)) m = fmaxf(m, lg[i]);
+    m = wave_max(m);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (!((taken >> i) & 1u)) z += expf(lg[i] - m);
+    z = wave_sum(z);
+  }
+  float my_w = 0.0f;
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    float bs = -INFINITY;
+    int bi = INT_MAX;
+    float bl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      if (!((taken >> i) & 1u) && (sc[i] > bs || (sc[i] == bs && e < bi))) {
+        bs = sc[i];
+        bi = e;
+        bl = lg[i];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float os = __shfl_xor(bs, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      const float ol = __shfl_xor(bl, o, 64);
+      if (os > bs || (os == bs && oi < bi)) {
+        bs = os;
+        bi = oi;
+        bl = ol;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const float w = (flags & COLI_ROUTE_SIGMOID) ? 1.0f / (1.0f + expf(-bl)) : expf(bl - m) / z;
+    if (lane == j) {
+      my_w = w;
+      my_idx = bi;
+    }
+  }
+  if (flags & COLI_ROUTE_RENORM) {
+    const float sum = wave_sum(lane < k ? my_w : 0.0f);
+    my_w = my_w / sum;
+  }
+  if (lane < k) {
+    idx_out[lane] = my_idx;
+    w_out[lane] = my_w * routed_scale;
+  }
+}
+
+template <int NPL>
+__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits,
+                                                   const float *__restrict__ bias, int T, int E,
+                                                   int k, uint32_t flags, float routed_scale,
+                                                   int32_t *__restrict__ idx,
+                                                   float *__restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token<NPL>(logits + (int64_t)t * E, bias, E, k, flags, routed_scale,
+                  idx + (int64_t)t * k, w + (int64_t)t * k);
+}
+
+// ---------------------------------------------------------------- group
+
+struct GroupShared {
+  int cnt[1024];
+  int off[1025];
+  int run[1024];
+  int wsum[16];
+  unsigned long long mask[kMaskWords];
+  int cbase[kMaskWords];
+};
+
+// Exclusive scan of v over the block (1024 threads); returns the prefix and
+// writes the total to *total.
+__device__ int block_exclusive_scan(int v, int *wsum, int *total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) wsum[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int i = 0; i < kGroupThreads / 64; ++i) {
+      const int t = wsum[i];
+      wsum[i] = acc;
+      acc += t;
+    }
+    *total = acc;
+  }
+  __syncthreads();
+  const int r = wsum[wid] + inc - v;
+  __syncthreads();
+  return r;
+}
+
+__device__ void group_pairs(const int32_t *__restrict__ idx, int T, int k, int E,
+                            const coli_moe_route_t &r, GroupShared &sh) {
+  const int tid = threadIdx.x;
+  const int64_t P = (int64_t)T * k;
+  __shared__ int total;
+  for (int e = tid; e < E; e += kGroupThreads) sh.cnt[e] = 0;
+  __syncthreads();
+  for (int64_t p = tid; p < P; p += kGroupThreads) atomicAdd(&sh.cnt[idx[p]], 1);
+  __syncthreads();
+  // offsets and the batch union (E <= 1024: one expert per thread)
+  const int c = tid < E ? sh.cnt[tid] : 0;
+  const int off = block_exclusive_scan(c, sh.wsum, &total);
+  if (tid < E) {
+    sh.off[tid] = off;
+    sh.run[tid] = 0;
+    r.counts[tid] = c;
+    r.offsets[tid] = off;
+  }
+  if (tid == 0) r.offsets[E] = (int)P;
+  const int upos = block_exclusive_scan(c > 0 ? 1 : 0, sh.wsum, &total);
+  if (tid < E && c > 0) r.union_ids[upos] = tid;
+  if (tid == 0) r.n_union[0] = total;
+  __syncthreads();
+  // stable scatter, in super-chunks of 64-token chunks
+  const int max_chunks = kMaskWords / E;
+  for (int t0 = 0; t0 < T; t0 += 64 * max_chunks) {
+    const int t1 = min(T, t0 + 64 * max_chunks);
+    const int nc = (t1 - t0 + 63) >> 6;
+    for (int i = tid; i < nc * E; i += kGroupThreads) sh.mask[i] = 0ull;
+    __syncthreads();
+    for (int64_t p = (int64_t)t0 * k + tid; p < (int64_t)t1 * k; p += kGroupThreads) {
+      const int t = (int)(p / k) - t0;
+      atomicOr(&sh.mask[(t >> 6) * E + idx[p]], 1ull << (t & 63));
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kGroupThreads) {
+      int run = sh.run[e];
+      for (int ch = 0; ch < nc; ++ch) {
+        sh.cbase[ch * E + e] = run;
+        run += __popcll(sh.mask[ch * E + e]);
+      }
+      sh.run[e] = run;
+    }
+    __syncthreads();
+    for (int64_t p = (int64_t)t0 * k + tid; p < (int64_t)t1 * k; p += kGroupThreads) {
+      const int t = (int)(p / k) - t0;
+      const int e = idx[p];
+      const int w = (t >> 6) * E + e;
+      const unsigned long long below = sh.mask[w] & ((1ull << (t & 63)) - 1ull);
+      const int pos = sh.off[e] + sh.cbase[w] + __popcll(below);
+      r.pairs[pos] = (int)p;
+      r.pair_pos[p] = pos;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(kGroupThreads) group_kernel(int T, int k, int E,
+                                                              coli_moe_route_t r) {
+  __shared__ GroupShared sh;
+  group_pairs(r.topk_idx, T, k, E, r, sh);
+}
+
+template <int NPL>
+__global__ void __launch_bounds__(kGroupThreads) fused_kernel(const float *__restrict__ logits,
+                                                              const float *__restrict__ bias,
+                                                              int T, int E, int k, uint32_t flags,
+                                                              float routed_scale,
+                                                              coli_moe_route_t r) {
+  __shared__ GroupShared sh;
+  const int t = threadIdx.x >> 6;
+  if (t < T)
+    topk_token<NPL>(logits + (int64_t)t * E, bias, E, k, flags, routed_scale,
+                    r.topk_idx + (int64_t)t * k, r.topk_w + (int64_t)t * k);
+  __threadfence_block();
+  __syncthreads();
+  group_pairs(r.topk_idx, T, k, E, r, sh);
+}
+
+template <int NPL>
+int launch_npl(const Layer &L, const float *logits, const float *bias, int T,
+               const coli_moe_route_t &r, hipStream_t s) {
+  if (T <= kGroupThreads / 64) {
+    fused_kernel<NPL><<<1, kGroupThreads, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
+                                                  L.routed_scale, r);
+  } else {
+    topk_kernel<NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
+                                                 L.routed_scale, r.topk_idx, r.topk_w);
+    group_kernel<<<1, kGroupThreads, 0, s>>>(T, L.k, L.E, r);
+  }
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_route(const Layer &L, const float *logits, const float *bias, int T,
+                 const coli_moe_route_t &r, hipStream_t s) {
+  const int npl = (L.E + 63) / 64;
+  if (npl <= 1) return launch_npl<1>(L, logits, bias, T, r, s);
+  if (npl <= 2) return launch_npl<2>(L, logits, bias, T, r, s);
+  if (npl <= 4) return launch_npl<4>(L, logits, bias, T, r, s);
+  if (npl <= 8) return launch_npl<8>(L, logits, bias, T, r, s);
+  return launch_npl<16>(L, logits, bias, T, r, s);
+}
+
+}  // namespace coli

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (no GPU needed: every call here fails validation before
+any HIP call, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_routed_expert_router_amd as coli
+from int4_routed_expert_router_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coli_moe.h")
+
+FAKE = 0x100000  # a 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coli_moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("coli_moe_route", "coli_moe_forward_decode", "coli_moe_forward_prefill",
+              "coli_moe_workspace_bytes", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
+              "coli_moe_strerror", "coli_moe_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.raw_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert coli.coli_moe_version().count(".") == 2
+    assert coli.coli_moe_strerror(-3) == "workspace too small"
+
+
+def _layer(**kw):
+    args = dict(hidden=2048, inter=512, n_experts=256, n_shared=1, top_k=8,
+                flags=coli.COLI_ROUTE_SIGMOID | coli.COLI_ROUTE_RENORM, q4=FAKE, scales=FAKE)
+    args.update(kw)
+    return coli.Layer(args["hidden"], args["inter"], args["n_experts"], args["n_shared"],
+                      args["top_k"], args["flags"], args["q4"], args["scales"])
+
+
+class _FakeRoute:
+    def __init__(self, null=False):
+        self.c = binding._RouteC(*([0 if null else FAKE] * 8))
+
+
+def test_workspace_sizes():
+    L = _layer()
+    T = 16
+    rows = T * (8 + 1)
+    dec = coli.coli_moe_workspace_bytes(L, T, coli.COLI_ENTRY_DECODE)
+    assert dec == rows * 512 * 4 + rows * 2048 * 4  # h and o, fp32
+    pre = coli.coli_moe_workspace_bytes(L, T, coli.COLI_ENTRY_PREFILL)
+    assert pre > rows * 2048 * 4 + T * 2048
+    assert coli.coli_moe_workspace_bytes(L, T, coli.COLI_ENTRY_ROUTE) == 0
+    assert coli.coli_moe_workspace_bytes(L, 65, coli.COLI_ENTRY_DECODE) == 0  # T > 64
+    assert coli.coli_moe_workspace_bytes(_layer(hidden=100), T, coli.COLI_ENTRY_DECODE) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=100), -1), (dict(inter=32), -1), (dict(hidden=16384 + 64), -1),
+    (dict(n_experts=0), -1), (dict(n_experts=1025), -1), (dict(n_shared=2), -1),
+    (dict(top_k=0), -1), (dict(top_k=257), -1), (dict(n_experts=64, top_k=33), -1),
+    (dict(flags=2), -1), (dict(q4=0), -1), (dict(q4=FAKE + 8), -4), (dict(scales=FAKE + 2), -4),
+])
+def test_forward_rejects_bad_layers(kw, code):
+    L = _layer(**kw)
+    lib = binding.raw_library()
+    rc = lib.coli_moe_forward_decode(ctypes.byref(L.c), ctypes.byref(_FakeRoute().c), FAKE, 1,
+                                     FAKE, 0, FAKE, 1 << 40, None)
+    assert rc == code
+
+
+def test_forward_rejects_bad_calls():
+    L = _layer()
+    lib = binding.raw_library()
+    r = ctypes.byref(_FakeRoute().c)
+    big = 1 << 40
+    dec = lib.coli_moe_forward_decode
+    pre = lib.coli_moe_forward_prefill
+    assert dec(ctypes.byref(L.c), r, FAKE, 0, FAKE, 0, FAKE, big, None) == -1      # T = 0
+    assert dec(ctypes.byref(L.c), r, FAKE, 65, FAKE, 0, FAKE, big, None) == -1     # T > 64
+    assert pre(ctypes.byref(L.c), r, FAKE, 65537, FAKE, 0, FAKE, big, None) == -1  # T too big
+    assert dec(ctypes.byref(L.c), r, 0, 1, FAKE, 0, FAKE, big, None) == -1         # x NULL
+    assert dec(ctypes.byref(L.c), r, FAKE, 1, FAKE, 7, FAKE, big, None) == -1      # y dtype
+    assert dec(ctypes.byref(L.c), r, FAKE + 2, 1, FAKE, 0, FAKE, big, None) == -4  # x align
+    assert dec(ctypes.byref(L.c), ctypes.byref(_FakeRoute(null=True).c), FAKE, 1, FAKE, 0,
+               FAKE, big, None) == -1                                              # route
+    need = coli.coli_moe_workspace_bytes(L, 4, coli.COLI_ENTRY_DECODE)
+    assert dec(ctypes.byref(L.c), r, FAKE, 4, FAKE, 0, FAKE, need - 1, None) == -3
+    assert dec(ctypes.byref(L.c), r, FAKE, 4, FAKE, 0, FAKE + 16, need, None) == -4
+    need = coli.coli_moe_workspace_bytes(L, 300, coli.COLI_ENTRY_PREFILL)
+    assert pre(ctypes.byref(L.c), r, FAKE, 300, FAKE, 0, FAKE, need - 1, None) == -3
+
+
+def test_route_quantize_dots_reject_bad_calls():
+    L = _layer()
+    lib = binding.raw_library()
+    r = ctypes.byref(_FakeRoute().c)
+    assert lib.coli_moe_route(None, FAKE, None, 4, r, None, 0, None) == -1
+    assert lib.coli_moe_route(ctypes.byref(L.c), 0, None, 4, r, None, 0, None) == -1
+    assert lib.coli_moe_route(ctypes.byref(L.c), FAKE, None, 0, r, None, 0, None) == -1
+    assert lib.coli_moe_route(ctypes.byref(L.c), FAKE + 1, None, 4, r, None, 0, None) == -4
+    assert lib.coli_moe_route(ctypes.byref(L.c), FAKE, None, 65537, r, None, 0, None) == -1
+    q = lib.coli_moe_quantize_q8_0
+    assert q(FAKE, 0, 33, FAKE, FAKE, None) == -1
+    assert q(FAKE, 2, 64, FAKE, FAKE, None) == -1
+    assert q(FAKE + 2, 0, 64, FAKE, FAKE, None) == -4
+    bd = lib.coli_moe_block_dots
+    assert bd(ctypes.byref(L.c), 257, 0, FAKE, 4, FAKE, None) == -1   # expert out of range
+    assert bd(ctypes.byref(L.c), 0, 3, FAKE, 4, FAKE, None) == -1     # matrix out of range
+    assert bd(ctypes.byref(L.c), 0, 0, FAKE, 0, FAKE, None) == -1     # T = 0
+
+
+def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        binding.raw_library()

@@ -1,0 +1,130 @@
+"""GPU parity of the integer (Q8_0, int8 matrix-core) prefill path."""
+import numpy as np
+import pytest
+import torch
+
+import int4_routed_expert_router_amd as coli
+import oracle
+import synth
+from gpu_util import (REL_TOL, bf16_ulp_distance, forward, gpu_layer, oracle_layer, rel_err,
+                      route_host, run_route)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ Q8_0
+
+def _q8(src: torch.Tensor, dtype):
+    n = src.numel()
+    q = torch.empty(n, dtype=torch.int8, device="cuda")
+    d = torch.empty(n // 32, dtype=torch.int16, device="cuda")
+    coli.coli_moe_quantize_q8_0(src, dtype, n, q, d)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), d.cpu().numpy().view(np.uint16)
+
+
+def test_quantize_q8_0_bit_exact():
+    g = torch.Generator().manual_seed(5)
+    nb = 4096
+    mags = 10.0 ** (torch.rand(nb, generator=g) * 12 - 8)  # 1e-8 .. 1e4
+    v = (torch.randn(nb, 32, generator=g) * mags[:, None]).to(torch.float32)
+    v[3] = 0.0
+    v[4, :] = 0.5
+    v[5, ::2] = -1.5e-5
+    # fp32 source
+    q, d = _q8(v.reshape(-1).cuda(), coli.COLI_SRC_F32)
+    qo, do = oracle.quantize_q8_0(v.reshape(-1).numpy())
+    assert np.array_equal(q, qo)
+    assert np.array_equal(d, do)
+    # bf16 source
+    vb = v.to(torch.bfloat16)
+    q, d = _q8(vb.reshape(-1).cuda(), coli.COLI_SRC_BF16)
+    qo, do = oracle.quantize_q8_0(vb.to(torch.float32).reshape(-1).numpy())
+    assert np.array_equal(q, qo)
+    assert np.array_equal(d, do)
+
+
+# ------------------------------------------------------------ block dots
+
+@pytest.mark.parametrize("spec,T,experts", [
+    (synth.LayerSpec(256, 128, 8, 0, 2, False, False), 4, (0, 7)),
+    (synth.LayerSpec(192, 320, 3, 1, 2, True, True), 37, (0, 3)),
+    (synth.LayerSpec(2048, 512, 4, 1, 2, True, True), 100, (2, 4)),
+    (synth.WORKLOADS["glm"].spec, 64, (17,)),
+])
+def test_block_dots_bit_exact(spec, T, experts):
+    print("block dots case: H=%d I=%d T=%d" % (spec.hidden, spec.inter, T), flush=True)
+    n_exp = max(experts) + 1 if spec.hidden < 6144 else spec.n_total
+    q4, sc = synth.make_weights(spec, seed=2, device="cuda", experts=n_exp)
+    L = coli.Layer(spec.hidden, spec.inter, n_exp - spec.n_shared, spec.n_shared, 1,
+                   spec.flags, q4, sc) if spec.hidden < 6144 else coli.Layer.from_spec(spec, q4, sc)
+    g = torch.Generator().manual_seed(T)
+    for e in experts:
+        for m in (0, 1, 2):
+            K = spec.inter if m == 2 else spec.hidden
+            rows = spec.hidden if m == 2 else spec.inter
+            a = torch.randint(-127, 128, (T, K), generator=g, dtype=torch.int8)
+            a[0] = 127
+            if T > 1:
+                a[1] = -127
+            dots = torch.empty(T, rows, K // 32, dtype=torch.int32, device="cuda")
+            coli.coli_moe_block_dots(L, e, m, a.cuda(), T, dots)
+            torch.cuda.synchronize()
+            qh, sh = synth.expert_slice(spec, q4, sc, [e])
+            want = oracle.block_dots(spec.hidden, spec.inter, 1, 0, qh, sh, 0, m, a.numpy())
+            assert np.array_equal(dots.cpu().numpy(), want), (e, m)
+
+
+# ---------------------------------------------------------- layer output
+
+def _prefill_case(spec, T, seed=0, zipf=0.0, tokens=None):
+    print("prefill case: H=%d I=%d E=%d S=%d k=%d T=%d" % (
+        spec.hidden, spec.inter, spec.n_experts, spec.n_shared, spec.top_k, T), flush=True)
+    L = gpu_layer(spec, seed=seed)
+    lg = synth.make_logits(spec, T, seed=seed, zipf_alpha=zipf).cuda()
+    x = synth.make_x(spec, T, seed=seed).cuda()
+    r = run_route(L, lg)
+    y = forward(L, r, x, "prefill")
+    g = route_host(r, T, spec.top_k)
+    toks = list(range(T)) if tokens is None else list(tokens)
+    ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, toks, "prefill")
+    err = rel_err(y.cpu().numpy()[toks], ref)
+    print("  rel err %.3g" % err, flush=True)
+    assert err < REL_TOL
+    return L, r, x, y, ref, toks
+
+
+def test_prefill_tiny():
+    w = synth.WORKLOADS["tiny"]
+    _prefill_case(w.spec, 4)
+
+
+def test_prefill_olmoe_512_sampled():
+    w = synth.WORKLOADS["olmoe"]
+    _prefill_case(w.spec, 512, tokens=[0, 1, 63, 64, 200, 333, 510, 511])
+
+
+def test_prefill_glm_2048_sampled():
+    w = synth.WORKLOADS["glm_prefill"]
+    _prefill_case(w.spec, 2048, zipf=w.zipf_alpha, tokens=[0, 777, 2047])
+
+
+@pytest.mark.parametrize("spec,T", [
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True), 70),
+    (synth.LayerSpec(2048, 512, 256, 1, 8, sigmoid=True, renorm=True), 16),
+    (synth.LayerSpec(64, 64, 1, 0, 1, sigmoid=False, renorm=False), 1),
+    (synth.LayerSpec(1024, 448, 32, 0, 4, sigmoid=False, renorm=True), 129),
+])
+def test_prefill_edge_shapes(spec, T):
+    _prefill_case(spec, T, seed=3, zipf=0.6)
+
+
+def test_prefill_deterministic_bf16_and_zero_scales():
+    spec = synth.WORKLOADS["a3b"].spec
+    L, r, x, y, ref, toks = _prefill_case(spec, 96, zipf=synth.ZIPF_ALPHA)
+    y2 = forward(L, r, x, "prefill")
+    assert torch.equal(y, y2)
+    yb = forward(L, r, x, "prefill", y_dtype=coli.COLI_OUT_BF16)
+    assert torch.equal(yb, y.to(torch.bfloat16))
+    Lz = coli.Layer.from_spec(spec, L.q4, torch.zeros_like(L.scales))
+    assert not forward(Lz, r, x, "prefill").any()
