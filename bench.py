@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the GLM-5.2-shaped decode stack -- 12 resident layers of
+H=6144, 256 routed experts of I=2048 + 1 shared expert (int4, gs64 fp16
+scales, about 58 GiB in HBM), top-8 sigmoid routing with renormalised
+weights and a Zipf-skewed router, one token.  A step is one pass of the hot
+path through all 12 layers: route (top-k + grouping) and the decode forward
+(gate/up GEMV + SwiGLU, down GEMV, combine) per layer, captured once in HIP
+graphs and replayed; router logits rotate across 8 pre-generated sets so
+successive steps stream different experts (the 12-layer working set of
+2.2 GB per step dwarfs the 256 MB Infinity Cache).
+
+value = MoE-layer tokens/s = tokens x layers / step time.  Also reported:
+int4 weight GB/s of the whole step (algorithmic bytes: every distinct expert
+of each layer's batch union, plus the shared expert, read once), the
+roofline of the dominant kernel (decode gate/up GEMV: algorithmic bytes per
+launch over its average duration from HIP events), the CPU oracle on a
+bounded sample, and secondary workloads (decode at 4 tokens, the 2048-token
+GLM prefill on int8 matrix cores, OLMoE-like and 35B-A3B-class layers).
+
+Prints ONE JSON line.  Inputs are synthetic (seeded generator module
+`synth`); all inputs are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak (POP/s -> TOPS)
+METRIC = "MoE-layer tokens/s + int4 weight GB/s (decode) / int8 TOPS (prefill)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class DecodeStack:
+    """L resident layers of one shape; captures one graph per logit rotation."""
+
+    def __init__(self, spec, layers, T, zipf, rotations=8, seed=0, layer_weights=None):
+        import torch
+
+        import int4_routed_expert_router_amd as coli
+        import synth
+
+        self.spec, self.L, self.T = spec, layers, T
+        self.layers = layer_weights or [
+            coli.Layer.from_spec(spec, *synth.make_weights(spec, seed=seed, layer=l, device="cuda"))
+            for l in range(layers)]
+        self.x = [synth.make_x(spec, T, seed=seed, layer=l).cuda() for l in range(layers)]
+        self.logits = [[synth.make_logits(spec, T, seed=seed, layer=l, zipf_alpha=zipf,
+                                          step=r).cuda() for l in range(layers)]
+                       for r in range(rotations)]
+        self.route = coli.Route(self.layers[0], T)
+        self.ws = coli.workspace(self.layers[0], T, coli.COLI_ENTRY_DECODE)
+        self.y = [torch.empty(T, spec.hidden, dtype=torch.bfloat16, device="cuda")
+                  for _ in range(layers)]
+        self.graphs = []
+        self.coli = coli
+
+    def step_eager(self, rot):
+        c = self.coli
+        for l in range(self.L):
+            c.coli_moe_route(self.layers[l], self.logits[rot][l], None, self.T, self.route)
+            c.coli_moe_forward_decode(self.layers[l], self.route, self.x[l], self.T, self.y[l],
+                                      c.COLI_OUT_BF16, self.ws)
+
+    def capture(self):
+        import torch
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.step_eager(0)  # warm the launch path before capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for r in range(len(self.logits)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step_eager(r)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self, i):
+        self.graphs[i % len(self.graphs)].replay()
+
+
+def union_bytes(spec, logits_list, k):
+    """Algorithmic weight bytes of one step: per layer, every distinct routed
+    expert of the batch plus the shared expert, each read once."""
+    import torch
+
+    total = 0
+    for lg in logits_list:
+        idx = torch.topk(lg.float(), k, dim=1).indices  # selection only: counts experts
+        n = int(torch.unique(idx).numel()) + spec.n_shared
+        total += n * spec.expert_total_bytes
+    return total
+
+
+def time_graph(stack, warmup, steps):
+    import torch
+
+    for i in range(warmup):
+        stack.replay(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        stack.replay(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def busy_gpu(ms=20.0):
+    """Queue ~ms of GPU work so that later eager launches queue up behind it
+    and the per-kernel events measure kernels, not host launch gaps."""
+    import torch
+
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(max(1, int(ms / 0.4))):
+        buf.fill_(1)
+    return buf
+
+
+def traced_kernels(fn, reps):
+    """Run fn() reps times eagerly under the library's kernel timer."""
+    import torch
+
+    import int4_routed_expert_router_amd as coli
+
+    timer = coli.KernelTimer(capacity=4096)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(reps):
+        keep = busy_gpu()
+        with timer:
+            fn()
+        torch.cuda.synchronize()
+        res.extend(timer.results())
+        del keep
+    timer.close()
+    by = {}
+    for name, ms in res:
+        by.setdefault(name, []).append(ms)
+    return {k: {"n": len(v), "avg_us": 1e3 * statistics.mean(v)} for k, v in by.items()}
+
+
+def cpu_baseline_decode(spec, layers_obj, x_list, logits_list, budget_s=12.0):
+    """The CPU oracle on a bounded sample of the decode stack (T = 1)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    done, t_total = 0, 0.0
+    T = x_list[0].shape[0]
+    for l in range(len(layers_obj)):
+        lg = logits_list[l].cpu().numpy()
+        r = oracle.route(lg, spec.top_k, spec.flags, spec.routed_scale)
+        used = sorted(set(int(e) for e in r["topk_idx"].ravel()))
+        experts = used + ([spec.n_experts] if spec.n_shared else [])
+        q4h, sch = synth.expert_slice(spec, layers_obj[l].q4, layers_obj[l].scales, experts)
+        remap = np.zeros(spec.n_experts, np.int32)
+        remap[used] = np.arange(len(used), dtype=np.int32)
+        xb = synth.bf16_bits(x_list[l])
+        t0 = time.perf_counter()
+        oracle.forward_decode(spec.hidden, spec.inter, len(used), spec.n_shared, spec.top_k,
+                              q4h, sch, remap[r["topk_idx"]], r["topk_w"], xb)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    # the oracle parallelises over tokens (OpenMP), so it uses min(T, cores)
+    cores = min(T, oracle.threads())
+    return {"value": T * done / t_total, "unit": "MoE-layer tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of the 12 layers, %d token(s) each, route + decode-mode layer in fp64 "
+                      "(%.1f s)" % (done, T, t_total)}
+
+
+def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=None):
+    stack = DecodeStack(spec, layers, T, zipf, layer_weights=layer_weights)
+    stack.capture()
+    ms, _ = time_graph(stack, warmup, steps)
+    nbytes = statistics.mean(union_bytes(spec, stack.logits[r], spec.top_k)
+                             for r in range(len(stack.logits)))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "path": "decode", "tokens": T, "layers": layers,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(T * layers / (ms * 1e-3), 1),
+            "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
+    import torch
+
+    import int4_routed_expert_router_amd as coli
+    import synth
+
+    Ls = [layer] if layer is not None else [
+        coli.Layer.from_spec(spec, *synth.make_weights(spec, seed=0, layer=c, device="cuda"))
+        for c in range(copies)]
+    lg = synth.make_logits(spec, T, seed=0, zipf_alpha=zipf).cuda()
+    x = synth.make_x(spec, T, seed=0).cuda()
+    r = coli.Route(Ls[0], T)
+    ws = coli.workspace(Ls[0], T, coli.COLI_ENTRY_PREFILL)
+    y = torch.empty(T, spec.hidden, dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        L = Ls[i % len(Ls)]
+        coli.coli_moe_route(L, lg, None, T, r)
+        coli.coli_moe_forward_prefill(L, r, x, T, y, coli.COLI_OUT_BF16, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kern = traced_kernels(lambda: step(0), reps=2)
+    nbytes = union_bytes(spec, [lg], spec.top_k)
+    ops = 2.0 * 3 * spec.hidden * spec.inter * T * (spec.top_k + spec.n_shared)
+    gemm_us = sum(kern.get(k, {"avg_us": 0})["avg_us"] for k in ("gemm_gateup", "gemm_down"))
+    out = {"workload": name, "path": "prefill", "tokens": T, "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
+           "int8_frac": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+           "gemm_int8_TOPS": round(ops / (gemm_us * 1e-6) / 1e12, 2) if gemm_us else None,
+           "weight_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="main workload only")
+    ap.add_argument("--trace-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this routed-expert layer is built and timed on a "
+              "single MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS["glm"]
+    spec, T, layers = w.spec, 1, w.layers
+    log("generating %d layers (%.1f GiB of int4 experts)" % (layers, synth.container_gib(spec, layers)))
+    stack = DecodeStack(spec, layers, T, w.zipf_alpha)
+    torch.cuda.synchronize()
+    log("capturing graphs")
+    stack.capture()
+    log("timing %d steps" % args.steps)
+    ms, wall = time_graph(stack, args.warmup, args.steps)
+    nbytes = statistics.mean(union_bytes(spec, stack.logits[r], spec.top_k)
+                             for r in range(len(stack.logits)))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    value = T * layers / (ms * 1e-3)
+    log("decode stack: %.3f ms/step, %.0f layer-tokens/s, %.0f GB/s" % (ms, value, gbps))
+
+    # dominant kernel: the gate/up GEMV (two thirds of the weight bytes)
+    kern = traced_kernels(lambda: stack.step_eager(0), reps=args.trace_reps)
+    gu = kern["decode_gateup"]
+    n_slots = spec.top_k * T if T == 1 else None  # T=1: the union is exactly k experts
+    gu_bytes = (n_slots + spec.n_shared) * 2 * spec.inter * spec.hidden * (0.5 + 2 / 64)
+    gu_gbps = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "decode_gateup", "bytes_per_launch": int(gu_bytes),
+                "avg_us": round(gu["avg_us"], 3),
+                "kernels_us": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
+    log("kernels (us):", roofline["kernels_us"])
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline_decode(spec, stack.layers, stack.x, stack.logits[0])
+
+    secondary = []
+    if not args.no_secondary:
+        log("secondary workloads")
+        secondary.append(secondary_decode("glm_decode_stack_T4", spec, 4, w.zipf_alpha, layers,
+                                          max(10, args.steps // 2), 3, layer_weights=stack.layers))
+        pw = synth.WORKLOADS["glm_prefill"]
+        secondary.append(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
+                                           10, 2, layer=stack.layers[0]))
+        del stack
+        torch.cuda.empty_cache()
+        ow = synth.WORKLOADS["olmoe"]
+        secondary.append(secondary_decode("olmoe_decode_T1", ow.spec, 1, 0.0, 4, 200, 10))
+        secondary.append(secondary_prefill("olmoe_prefill_T512", ow.spec, 512, 0.0, 20, 3, copies=4))
+        aw = synth.WORKLOADS["a3b"]
+        for t in aw.tokens:
+            secondary.append(secondary_decode("a3b_decode_T%d" % t, aw.spec, t, aw.zipf_alpha, 4,
+                                              200, 10))
+        for s in secondary:
+            log(json.dumps(s))
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "MoE-layer tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights, bf16 x bf16 dot products, f32 accumulation",
+        "data": "synthetic (seeded; shapes of the GLM-5.2 MoE layer)",
+        "config": {"workload": "glm52_decode_stack", "hidden": spec.hidden, "inter": spec.inter,
+                   "routed_experts": spec.n_experts, "shared_experts": spec.n_shared,
+                   "top_k": spec.top_k, "routing": "sigmoid+renorm, Zipf-skewed logits",
+                   "layers": layers, "tokens": T, "weights_GiB": round(synth.container_gib(spec, layers), 2)},
+        "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "stack_tokens_per_s": round(T / (ms * 1e-3), 1), "wall_s": round(wall, 3),
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -208,6 +208,29 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert,
                         int32_t matrix, const int8_t *q_act, int32_t T,
                         int32_t *dots, void *stream);
 
+/* ---- optional kernel timing ----------------------------------------------
+ * For benchmarks and profilers.  After coli_moe_set_trace(t) with t != NULL,
+ * every later launch records t->start[i] just before and t->stop[i] just
+ * after its i-th kernel on the call's stream, stores the kernel's COLI_K_*
+ * id in t->kernel[i] (host memory) and increments t->count, until count
+ * reaches capacity (further kernels are not timed).  start/stop hold
+ * hipEvent_t handles created by the caller.  coli_moe_set_trace(NULL) turns
+ * timing off.  The trace pointer is process-wide: set it from one thread,
+ * with no call in flight. */
+enum {
+  COLI_K_ROUTE_FUSED = 0, COLI_K_TOPK = 1, COLI_K_GROUP = 2, COLI_K_DECODE_GATEUP = 3,
+  COLI_K_DECODE_DOWN = 4, COLI_K_COMBINE = 5, COLI_K_QUANTIZE = 6, COLI_K_PLAN = 7,
+  COLI_K_GEMM_GATEUP = 8, COLI_K_GEMM_DOWN = 9, COLI_K_BLOCK_DOTS = 10, COLI_K_COUNT = 11
+};
+typedef struct coli_moe_trace {
+  void **start;     /* hipEvent_t[capacity] */
+  void **stop;      /* hipEvent_t[capacity] */
+  int32_t *kernel;  /* host [capacity]: COLI_K_* of each timed kernel */
+  int32_t capacity;
+  int32_t count;    /* kernels timed so far */
+} coli_moe_trace_t;
+int coli_moe_set_trace(coli_moe_trace_t *trace);
+
 /* Static description of a status code. */
 const char *coli_moe_strerror(int status);
 

@@ -33,6 +33,16 @@ class _LayerC(ctypes.Structure):
     ]
 
 
+class _TraceC(ctypes.Structure):
+    _fields_ = [("start", ctypes.POINTER(ctypes.c_void_p)), ("stop", ctypes.POINTER(ctypes.c_void_p)),
+                ("kernel", ctypes.POINTER(ctypes.c_int32)), ("capacity", ctypes.c_int32),
+                ("count", ctypes.c_int32)]
+
+
+KERNEL_NAMES = ["route_fused", "route_topk", "route_group", "decode_gateup", "decode_down",
+                "combine", "quantize_q8_0", "plan", "gemm_gateup", "gemm_down", "block_dots"]
+
+
 class _RouteC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_idx", "topk_w", "counts", "offsets", "pairs", "pair_pos", "union_ids", "n_union")]
@@ -64,6 +74,8 @@ def _load():
         lib.coli_moe_block_dots.argtypes = [P(_LayerC), i32, i32, vp, i32, vp, vp]
         lib.coli_moe_strerror.argtypes = [ctypes.c_int]
         lib.coli_moe_strerror.restype = ctypes.c_char_p
+        lib.coli_moe_set_trace.argtypes = [ctypes.POINTER(_TraceC)]
+        lib.coli_moe_set_trace.restype = ctypes.c_int
         lib.coli_moe_version.argtypes = []
         lib.coli_moe_version.restype = ctypes.c_char_p
         for f in ("coli_moe_route", "coli_moe_forward_decode", "coli_moe_forward_prefill",
@@ -183,6 +195,67 @@ def coli_moe_block_dots(layer: Layer, expert: int, matrix: int, q_act, T: int, d
                         stream=None):
     _check("coli_moe_block_dots", _load().coli_moe_block_dots(
         ctypes.byref(layer.c), expert, matrix, _ptr(q_act), T, _ptr(dots), _stream(stream)))
+
+
+def _hip_runtime():
+    """The HIP runtime already loaded in this process (torch's or the system's)."""
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    return ctypes.CDLL(path or "libamdhip64.so")
+
+
+class KernelTimer:
+    """Times every kernel the library launches while active (hipEvents)."""
+
+    def __init__(self, capacity: int = 4096):
+        _load()
+        self.hip = _hip_runtime()
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.start = (ctypes.c_void_p * capacity)()
+        self.stop = (ctypes.c_void_p * capacity)()
+        self.kernel = (ctypes.c_int32 * capacity)()
+        for arr in (self.start, self.stop):
+            for i in range(capacity):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev
+        self.c = _TraceC(ctypes.cast(self.start, ctypes.POINTER(ctypes.c_void_p)),
+                         ctypes.cast(self.stop, ctypes.POINTER(ctypes.c_void_p)),
+                         ctypes.cast(self.kernel, ctypes.POINTER(ctypes.c_int32)), capacity, 0)
+
+    def __enter__(self):
+        self.c.count = 0
+        _check("coli_moe_set_trace", _load().coli_moe_set_trace(ctypes.byref(self.c)))
+        return self
+
+    def __exit__(self, *exc):
+        _load().coli_moe_set_trace(None)
+        return False
+
+    def results(self):
+        """[(kernel name, milliseconds)] of every timed kernel, in launch order."""
+        out = []
+        for i in range(self.c.count):
+            self.hip.hipEventSynchronize(self.stop[i])
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((KERNEL_NAMES[self.kernel[i]], ms.value))
+        return out
+
+    def close(self):
+        for arr in (self.start, self.stop):
+            for ev in arr:
+                if ev:
+                    self.hip.hipEventDestroy(ev)
 
 
 def raw_library():

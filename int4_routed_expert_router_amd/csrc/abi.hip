@@ -91,6 +91,10 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
 }  // namespace
 }  // namespace coli
 
+namespace coli {
+coli_moe_trace_t *g_trace = nullptr;
+}
+
 using namespace coli;
 
 extern "C" {
@@ -162,6 +166,13 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t m
   if (T < 1 || T > 4096 || !q_act || !dots) return COLI_E_INVALID;
   if (!aligned(q_act, 16) || !aligned(dots, 16)) return COLI_E_ALIGN;
   return launch_block_dots(L, expert, matrix, q_act, T, dots, reinterpret_cast<hipStream_t>(stream));
+}
+
+int coli_moe_set_trace(coli_moe_trace_t *trace) {
+  if (trace && (!trace->start || !trace->stop || !trace->kernel || trace->capacity < 0))
+    return COLI_E_INVALID;
+  g_trace = trace;
+  return COLI_OK;
 }
 
 const char *coli_moe_strerror(int status) {

@@ -108,21 +108,20 @@ __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_rout
       __syncthreads();
       for (int i = threadIdx.x; i < TG * NCH; i += kThreads) {
         const int tt = i / NCH, c = i % NCH;
-        float s = 0.0f;
+        float nb = 0.0f;
         if (tt < nt) {
           const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)si.tok[t0 + tt] * H) + 4 * c;
+          uint32_t p[16];
 #pragma unroll
           for (int dw = 0; dw < 4; ++dw) {
             const uint4 v = src[dw];
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-            uint32_t p[4];
-            x8_to_pairs(d, p);
-            xs[(tt * 4 + dw) * NCH + c] = make_uint4(p[0], p[1], p[2], p[3]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s += bf16_to_f32(d[q] & 0xffffu) + bf16_to_f32(d[q] >> 16);
+            x8_to_pairs(d, &p[4 * dw]);
+            xs[(tt * 4 + dw) * NCH + c] = make_uint4(p[4 * dw], p[4 * dw + 1], p[4 * dw + 2], p[4 * dw + 3]);
           }
+          nb = chunk_bias(p);
         }
-        corr[tt * NCH + c] = (float)kNibBias * s;
+        corr[tt * NCH + c] = -nb;
       }
       __syncthreads();
 
@@ -243,9 +242,10 @@ __global__ void __launch_bounds__(kThreads) down_kernel(Layer L, coli_moe_route_
       __syncthreads();
       for (int i = threadIdx.x; i < TG * NCH; i += kThreads) {
         const int tt = i / NCH, c = i % NCH;
-        float s = 0.0f;
+        float nb = 0.0f;
         if (tt < nt) {
           const float4 *src = reinterpret_cast<const float4 *>(h_in + (int64_t)si.pos[t0 + tt] * I) + 8 * c;
+          uint32_t ph[16], pl[16];
 #pragma unroll
           for (int dw = 0; dw < 4; ++dw) {
             const float4 a = src[2 * dw], b = src[2 * dw + 1];
@@ -258,16 +258,15 @@ __global__ void __launch_bounds__(kThreads) down_kernel(Layer L, coli_moe_route_
               const uint32_t l0 = f32_to_bf16_bits(r0), l1 = f32_to_bf16_bits(r1);
               hi[q] = h0 | (h1 << 16);
               lo[q] = l0 | (l1 << 16);
-              s += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
             }
-            uint32_t ph[4], pl[4];
-            x8_to_pairs(hi, ph);
-            x8_to_pairs(lo, pl);
-            xs[(tt * 8 + dw) * NCH + c] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-            xs[(tt * 8 + 4 + dw) * NCH + c] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+            x8_to_pairs(hi, &ph[4 * dw]);
+            x8_to_pairs(lo, &pl[4 * dw]);
+            xs[(tt * 8 + dw) * NCH + c] = make_uint4(ph[4 * dw], ph[4 * dw + 1], ph[4 * dw + 2], ph[4 * dw + 3]);
+            xs[(tt * 8 + 4 + dw) * NCH + c] = make_uint4(pl[4 * dw], pl[4 * dw + 1], pl[4 * dw + 2], pl[4 * dw + 3]);
           }
+          nb = chunk_bias2(ph, pl);
         }
-        corr[tt * NCH + c] = (float)kNibBias * s;
+        corr[tt * NCH + c] = -nb;
       }
       __syncthreads();
 
@@ -446,6 +445,7 @@ int pick_tg(int T, int K, int bytes_per_value) {
 void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int k, int S,
                     void *y, int y_dtype, hipStream_t s) {
   const dim3 grid((H / 4 + kThreads - 1) / kThreads, T);
+  TraceScope ts(COLI_K_COMBINE, s);
   combine_kernel<<<grid, kThreads, 0, s>>>(o, r.pair_pos, r.topk_w, T, H, k, S, y, y_dtype);
 }
 
@@ -460,7 +460,13 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
   float *h = reinterpret_cast<float *>(ws);
   float *o = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + align_up((size_t)rows * L.I * 4));
   const int nslots = max_union(L, T) + L.S;
-  hipError_t err;
+  hipError_t err = hipSuccess;
+
+  if (T == 1 && launch_decode_single(L, r, x, h, o, s, &err)) {
+    if (err != hipSuccess) return COLI_E_HIP;
+    launch_combine(o, r, T, L.H, L.k, L.S, y, y_dtype, s);
+    return hip_status(hipGetLastError());
+  }
 
   {  // gate / up
     const Shape sh = pick_shape(L.H);
@@ -469,6 +475,7 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
     const dim3 grid(items < 8192 ? items : 8192);
     const int tg = pick_tg(T, L.H, 2);
     const size_t lds = (size_t)tg * (L.H / 32) * (64 + 4);
+    TraceScope ts(COLI_K_DECODE_GATEUP, s);
     err = tg == 1 ? launch_gateup<1>(sh, grid, lds, s, L, r, x, T, h, nrb, items)
                   : launch_gateup<4>(sh, grid, lds, s, L, r, x, T, h, nrb, items);
     if (err != hipSuccess) return COLI_E_HIP;
@@ -480,6 +487,7 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
     const dim3 grid(items < 8192 ? items : 8192);
     const int tg = pick_tg(T, L.I, 4);
     const size_t lds = (size_t)tg * (L.I / 32) * (128 + 4);
+    TraceScope ts(COLI_K_DECODE_DOWN, s);
     err = tg == 1 ? launch_down<1>(sh, grid, lds, s, L, r, T, h, o, nrb, items)
                   : launch_down<4>(sh, grid, lds, s, L, r, T, h, o, nrb, items);
     if (err != hipSuccess) return COLI_E_HIP;

@@ -44,13 +44,18 @@ COLI_DEV float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // value 128 + (q + 8) = 136 + q, exact, so a dot with activations carries a
 // bias of 136 * sum(x) that the caller removes.
 constexpr uint32_t kNibBias = 136;
+// (a & b) ^ c as a v_bitop3_b32 truth table (a = 0xF0, b = 0xCC, c = 0xAA).
+constexpr uint32_t kAndXor = 0x6Au;
 COLI_DEV void nib8_to_bf16x4(uint32_t w, uint32_t &p0, uint32_t &p1, uint32_t &p2,
                              uint32_t &p3) {
-  const uint32_t v = w ^ 0x88888888u;  // two's complement -> offset binary
-  p0 = (v & 0x000f000fu) | 0x43004300u;
-  p1 = ((v >> 4) & 0x000f000fu) | 0x43004300u;
-  p2 = ((v >> 8) & 0x000f000fu) | 0x43004300u;
-  p3 = ((v >> 12) & 0x000f000fu) | 0x43004300u;
+  // (nibble & 15) ^ 8 turns two's complement into offset binary q + 8; the
+  // upper bits 0x4300 make the bf16 value 128 + (q + 8).  Both in one
+  // bitop3: ((w >> s) & 0x000f000f) ^ 0x43084308.
+  constexpr uint32_t M = 0x000f000fu, K = 0x43084308u;
+  p0 = __builtin_amdgcn_bitop3_b32(w, M, K, kAndXor);
+  p1 = __builtin_amdgcn_bitop3_b32(w >> 4, M, K, kAndXor);
+  p2 = __builtin_amdgcn_bitop3_b32(w >> 8, M, K, kAndXor);
+  p3 = __builtin_amdgcn_bitop3_b32(w >> 12, M, K, kAndXor);
 }
 
 // Eight consecutive bf16 activations (x0..x7 packed in four dwords, low half
@@ -61,6 +66,27 @@ COLI_DEV void x8_to_pairs(const uint32_t d[4], uint32_t out[4]) {
   out[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
   out[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
   out[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+}
+
+// -136 * (sum of a chunk's 32 activations), from its 16 paired dwords, in one
+// fixed order.  Every kernel that removes the nibble bias uses these, so a
+// token's result is the same whichever kernel handled it.
+constexpr uint32_t kBf16Ones = 0x3f803f80u;  // bf16 (1.0, 1.0)
+COLI_DEV float chunk_bias(const uint32_t p[16]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) s = dot2_bf16(p[q], kBf16Ones, s);
+  return -(float)kNibBias * s;
+}
+// the same for an activation split into bf16 hi + lo halves
+COLI_DEV float chunk_bias2(const uint32_t hp[16], const uint32_t lp[16]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    s = dot2_bf16(hp[q], kBf16Ones, s);
+    s = dot2_bf16(lp[q], kBf16Ones, s);
+  }
+  return -(float)kNibBias * s;
 }
 
 template <int W>

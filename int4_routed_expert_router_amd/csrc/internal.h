@@ -42,6 +42,8 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
                   void *y, int y_dtype, void *ws, hipStream_t s);
 int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                    void *y, int y_dtype, void *ws, hipStream_t s);
+bool launch_decode_single(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
+                          float *h, float *o, hipStream_t s, hipError_t *err);
 void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int k, int S,
                     void *y, int y_dtype, hipStream_t s);
 int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *d,
@@ -50,5 +52,24 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
                       int32_t *dots, hipStream_t s);
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_E_HIP; }
+
+// Optional per-kernel event timing (coli_moe_set_trace).  A launcher wraps
+// each kernel in a TraceScope; with no trace set it does nothing.
+extern coli_moe_trace_t *g_trace;
+struct TraceScope {
+  int slot = -1;
+  hipStream_t s;
+  TraceScope(int kernel_id, hipStream_t stream) : s(stream) {
+    coli_moe_trace_t *t = g_trace;
+    if (t && t->count < t->capacity) {
+      slot = t->count++;
+      t->kernel[slot] = kernel_id;
+      (void)hipEventRecord(reinterpret_cast<hipEvent_t>(t->start[slot]), s);
+    }
+  }
+  ~TraceScope() {
+    if (slot >= 0) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(g_trace->stop[slot]), s);
+  }
+};
 
 }  // namespace coli

@@ -27,10 +27,11 @@ constexpr int kMaskWords = 4096;  // 64-token masks held in LDS at once
 
 // ---------------------------------------------------------------- top-k
 
+// Returns, in lane j < k, the j-th chosen expert (also written to idx_out).
 template <int NPL>
-__device__ void topk_token(const float *__restrict__ lg_row, const float *__restrict__ bias,
-                           int E, int k, uint32_t flags, float routed_scale,
-                           int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+__device__ int topk_token(const float *__restrict__ lg_row, const float *__restrict__ bias,
+                          int E, int k, uint32_t flags, float routed_scale,
+                          int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   float lg[NPL], sc[NPL];
   uint32_t taken = 0;
@@ -99,6 +100,7 @@ __device__ void topk_token(const float *__restrict__ lg_row, const float *__rest
     idx_out[lane] = my_idx;
     w_out[lane] = my_w * routed_scale;
   }
+  return my_idx;
 }
 
 template <int NPL>
@@ -214,31 +216,108 @@ __global__ void __launch_bounds__(kGroupThreads) group_kernel(int T, int k, int 
   group_pairs(r.topk_idx, T, k, E, r, sh);
 }
 
+// Small batches (T <= 16, decode / verify): top-k and grouping in one
+// workgroup with every intermediate in LDS, so the only global read is the
+// logits.  A token picks an expert at most once, so the stable in-expert
+// rank of token t is the number of earlier tokens in the expert's 64-bit
+// token mask.
+constexpr int kSmallT = 16;
+
 template <int NPL>
 __global__ void __launch_bounds__(kGroupThreads) fused_kernel(const float *__restrict__ logits,
                                                               const float *__restrict__ bias,
                                                               int T, int E, int k, uint32_t flags,
                                                               float routed_scale,
                                                               coli_moe_route_t r) {
-  __shared__ GroupShared sh;
-  const int t = threadIdx.x >> 6;
-  if (t < T)
-    topk_token<NPL>(logits + (int64_t)t * E, bias, E, k, flags, routed_scale,
-                    r.topk_idx + (int64_t)t * k, r.topk_w + (int64_t)t * k);
-  __threadfence_block();
+  __shared__ int s_idx[kSmallT * 32];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ unsigned long long s_mask[1024];
+  __shared__ int wsum[16];
+  __shared__ int total;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int e = tid; e < E; e += nthr) {
+    s_cnt[e] = 0;
+    s_mask[e] = 0ull;
+  }
+  const int t = tid >> 6;
+  if (t < T) {
+    const int mine = topk_token<NPL>(logits + (int64_t)t * E, bias, E, k, flags, routed_scale,
+                                     r.topk_idx + (int64_t)t * k, r.topk_w + (int64_t)t * k);
+    const int lane = tid & 63;
+    if (lane < k) s_idx[t * k + lane] = mine;
+  }
   __syncthreads();
-  group_pairs(r.topk_idx, T, k, E, r, sh);
+  const int P = T * k;
+  for (int p = tid; p < P; p += nthr) {
+    const int e = s_idx[p];
+    atomicAdd(&s_cnt[e], 1);
+    atomicOr(&s_mask[e], 1ull << (p / k));
+  }
+  __syncthreads();
+  // offsets and the batch union: one expert per thread (E <= blockDim)
+  const int lane = tid & 63, wid = tid >> 6, nw = nthr >> 6;
+  const int c = tid < E ? s_cnt[tid] : 0;
+  int inc_c = c, inc_u = c > 0 ? 1 : 0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int nc = __shfl_up(inc_c, o, 64), nu = __shfl_up(inc_u, o, 64);
+    if (lane >= o) {
+      inc_c += nc;
+      inc_u += nu;
+    }
+  }
+  if (lane == 63) wsum[wid] = inc_c | (inc_u << 16);  // both fit in 16 bits (P, E <= 1024)
+  __syncthreads();
+  if (tid == 0) {
+    int ac = 0, au = 0;
+    for (int i = 0; i < nw; ++i) {
+      const int v = wsum[i];
+      wsum[i] = ac | (au << 16);
+      ac += v & 0xffff;
+      au += v >> 16;
+    }
+    total = au;
+  }
+  __syncthreads();
+  const int off = (wsum[wid] & 0xffff) + inc_c - c;
+  const int upos = (wsum[wid] >> 16) + inc_u - (c > 0 ? 1 : 0);
+  if (tid < E) {
+    s_off[tid] = off;
+    r.counts[tid] = c;
+    r.offsets[tid] = off;
+    if (c > 0) r.union_ids[upos] = tid;
+  }
+  if (tid == 0) {
+    r.offsets[E] = P;
+    r.n_union[0] = total;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += nthr) {
+    const int e = s_idx[p], tok = p / k;
+    const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << tok) - 1ull));
+    r.pairs[pos] = p;
+    r.pair_pos[p] = pos;
+  }
 }
 
 template <int NPL>
 int launch_npl(const Layer &L, const float *logits, const float *bias, int T,
                const coli_moe_route_t &r, hipStream_t s) {
-  if (T <= kGroupThreads / 64) {
-    fused_kernel<NPL><<<1, kGroupThreads, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
-                                                  L.routed_scale, r);
+  if (T <= kSmallT) {
+    // enough wavefronts for one token each and one thread per expert
+    const int need = max(64 * T, L.E);
+    const int threads = need <= 256 ? 256 : (need <= 512 ? 512 : 1024);
+    TraceScope ts(COLI_K_ROUTE_FUSED, s);
+    fused_kernel<NPL><<<1, threads, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
+                                            L.routed_scale, r);
   } else {
-    topk_kernel<NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
-                                                 L.routed_scale, r.topk_idx, r.topk_w);
+    {
+      TraceScope ts(COLI_K_TOPK, s);
+      topk_kernel<NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
+                                                   L.routed_scale, r.topk_idx, r.topk_w);
+    }
+    TraceScope ts(COLI_K_GROUP, s);
     group_kernel<<<1, kGroupThreads, 0, s>>>(T, L.k, L.E, r);
   }
   return hip_status(hipGetLastError());
