@@ -32,6 +32,7 @@ constexpr int kThreads = 256;
 constexpr int BM = 64;    // tokens per tile
 constexpr int BR = 128;   // weight rows per tile
 constexpr int BK = 64;    // reduction depth per step (one weight scale group)
+constexpr int kDepth = 4; // K steps of global loads kept in flight per thread
 constexpr uint32_t kMagic = 0x4B400000u;  // bits of 1.5 * 2^23
 constexpr float kMagicF = 12582912.0f;
 
@@ -284,7 +285,7 @@ COLI_DEV int wave_row_tile(int wn, int a) {
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g, coli_moe_route_t r,
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_kernel(GemmArgs g, coli_moe_route_t r,
                                                         const int4 *__restrict__ tiles,
                                                         const int *__restrict__ ntiles_p,
                                                         int fixed_ntok, int fixed_expert,
@@ -348,17 +349,12 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g, coli_moe_rou
       for (int i = 0; i < 4; ++i) acc[a][i] = 0.0f;
     const coli_i32x4 magic = {(int)kMagic, (int)kMagic, (int)kMagic, (int)kMagic};
 
-    Prefetch pf;
-    load_step<MODE>(ge, n0, rowid, ntok, 0, pf);
-    store_step(pf, st[0]);
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ++ks) {
-      Stage &cur = st[ks & 1];
-      if (ks + 1 < nsteps) load_step<MODE>(ge, n0, rowid, ntok, ks + 1, pf);
-      // 4 row tiles x 2 token tiles x 2 blocks
-      coli_i32x4 d[2][8];
+    // One K step on LDS stage `cur`: for each of the two 32-blocks, 4 row
+    // tiles x 2 token tiles of MFMAs, then that block's scales.
+    auto step = [&](const Stage &cur, int ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
+        coli_i32x4 d[8];
         uint2 bop[2];
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) bop[ms] = cur.a[2 * wm + ms][blk][lane];
@@ -366,46 +362,65 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g, coli_moe_rou
         for (int a = 0; a < 4; ++a) {
           const uint2 aop = cur.w[wave_row_tile<MODE>(wn, a)][blk][lane];
 #pragma unroll
-          for (int ms = 0; ms < 2; ++ms) d[blk][a * 2 + ms] = mfma_i8(aop, bop[ms], magic);
+          for (int ms = 0; ms < 2; ++ms) d[a * 2 + ms] = mfma_i8(aop, bop[ms], magic);
         }
-      }
-      if (MODE == kDots) {
-        // exact block dots: (bits - magic) / 16, written [token][row][block]
+        if (MODE == kDots) {
+          // exact block dots: (bits - magic) / 16, written [token][row][block]
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+              const int m = 32 * wm + 16 * ms + (lane & 15);
+              if (m >= ntok) continue;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int n = n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
+                if (n >= g.rows) continue;
+                dots_out[((int64_t)(row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks + blk] =
+                    (d[a * 2 + ms][i] - (int)kMagic) >> 4;
+              }
+            }
+        } else {
 #pragma unroll
           for (int ms = 0; ms < 2; ++ms) {
-            const int m = 32 * wm + 16 * ms + (lane & 15);
-            if (m >= ntok) continue;
+            const float2 sa = reinterpret_cast<const float2 *>(
+                &cur.sa[32 * wm + 16 * ms + (lane & 15)])[blk];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int n = n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
-              if (n >= g.rows) continue;
-              int32_t *dst = dots_out + ((int64_t)(row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks;
-              dst[0] = (d[0][a * 2 + ms][i] - (int)kMagic) >> 4;
-              dst[1] = (d[1][a * 2 + ms][i] - (int)kMagic) >> 4;
-            }
-          }
-      } else {
+            for (int a = 0; a < 4; ++a) {
+              const float4 sw = *reinterpret_cast<const float4 *>(
+                  &cur.sw[16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
+              const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-          const float4 sa = cur.sa[32 * wm + 16 * ms + (lane & 15)];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const float4 sw = *reinterpret_cast<const float4 *>(
-                &cur.sw[16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
-            const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float t0 = fmaf(__int_as_float(d[0][a * 2 + ms][i]), sa.x, sa.y);
-              const float t1 = fmaf(__int_as_float(d[1][a * 2 + ms][i]), sa.z, sa.w);
-              acc[a * 2 + ms][i] = fmaf(swv[i], t0 + t1, acc[a * 2 + ms][i]);
+              for (int i = 0; i < 4; ++i)
+                acc[a * 2 + ms][i] = fmaf(swv[i], fmaf(__int_as_float(d[a * 2 + ms][i]), sa.x, sa.y),
+                                          acc[a * 2 + ms][i]);
             }
           }
         }
       }
-      if (ks + 1 < nsteps) store_step(pf, st[(ks + 1) & 1]);
-      __syncthreads();
+    };
+
+    // Pipeline: a register ring holds the raw global data of the next P
+    // steps (loads in flight), LDS holds two unpacked stages.  Step ks
+    // computes on stage ks & 1, refills the ring slot it freed with step
+    // ks + P, and unpacks step ks + 1 into the other stage.
+    Prefetch pf[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i)
+      if (i < nsteps) load_step<MODE>(ge, n0, rowid, ntok, i, pf[i]);
+    store_step(pf[0], st[0]);
+    __syncthreads();
+    for (int ks0 = 0; ks0 < nsteps; ks0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int ks = ks0 + u;
+        if (ks < nsteps) {
+          if (ks + kDepth < nsteps) load_step<MODE>(ge, n0, rowid, ntok, ks + kDepth, pf[u]);
+          step(st[ks & 1], ks);
+          if (ks + 1 < nsteps) store_step(pf[(u + 1) % kDepth], st[(ks + 1) & 1]);
+          __syncthreads();
+        }
+      }
     }
 
     if (MODE == kGateUp) {

@@ -27,80 +27,159 @@ constexpr int kMaskWords = 4096;  // 64-token masks held in LDS at once
 
 // ---------------------------------------------------------------- top-k
 
+// Selection key of expert e with score s: the order-preserving unsigned image
+// of s in the high word, ~e in the low word, so one unsigned max picks the
+// largest score and, among equal scores, the lower index.  -0 is folded
+// onto +0 (they compare equal as floats); NaN scores rank below -inf.
+COLI_DEV uint64_t select_key(float s, int e) {
+  uint32_t u = __float_as_uint(s + 0.0f);
+  uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if (s != s) hi = 0x007ffffeu;  // just below -inf, whose image is 0x007fffff
+  return ((uint64_t)hi << 32) | (uint32_t)(~(uint32_t)e);
+}
+
+COLI_DEV uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// DPP move of a 64-bit value within rows of 16 lanes.
+template <int CTRL>
+COLI_DEV uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Wave-wide maximum of a 64-bit key: four DPP steps inside each 16-lane row
+// (swap neighbours, swap pairs, mirror halves of 8, mirror the row), then
+// the four row maxima are read into scalar registers.
+COLI_DEV uint64_t wave_max_key(uint64_t k) {
+  k = umax64(k, dpp64<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = umax64(k, dpp64<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = umax64(k, dpp64<0x141>(k));  // row_half_mirror
+  k = umax64(k, dpp64<0x140>(k));  // row_mirror
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
+    r = umax64(r, ((uint64_t)hi << 32) | lo);
+  }
+  return r;
+}
+
+// One wavefront selects the k experts of one token.  Lane j < k ends with
+// the j-th chosen expert (*my_e) and its routing weight (returned); the
+// weights use the raw logits (see COLI_ROUTE_*).
+template <int NPL>
+COLI_DEV float topk_wave(const float *__restrict__ lg_row, const float *__restrict__ bias, int E,
+                         int k, uint32_t flags, float routed_scale, int *my_e) {
+  const int lane = threadIdx.x & 63;
+  float lg[NPL];
+  uint64_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    lg[i] = e < E ? lg_row[e] : 0.0f;
+    key[i] = e < E ? select_key(bias ? lg[i] + bias[e] : lg[i], e) : 0ull;
+  }
+  float m = -FLT_MAX, z = 0.0f;
+  if ((flags & COLI_ROUTE_SIGMOID) == 0) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i < E) m = fmaxf(m, lg[i]);
+    m = wave_max(m);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i < E) z += expf(lg[i] - m);
+    z = wave_sum(z);
+  }
+  float my_l = 0.0f;
+  int me = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) best = umax64(best, key[i]);
+    const uint64_t win = wave_max_key(best);
+    const int e = (int)(~(uint32_t)win);
+    const int owner = e & 63, slot = e >> 6;
+    float wl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      if (i == slot) {
+        wl = lg[i];
+        if (lane == owner) key[i] = 0ull;  // taken
+      }
+    }
+    wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), owner));
+    if (lane == j) {
+      me = e;
+      my_l = wl;
+    }
+  }
+  float w = (flags & COLI_ROUTE_SIGMOID) ? 1.0f / (1.0f + expf(-my_l)) : expf(my_l - m) / z;
+  if (flags & COLI_ROUTE_RENORM) w = w / wave_sum(lane < k ? w : 0.0f);
+  *my_e = me;
+  return w * routed_scale;
+}
+
 // Returns, in lane j < k, the j-th chosen expert (also written to idx_out).
 template <int NPL>
 __device__ int topk_token(const float *__restrict__ lg_row, const float *__restrict__ bias,
                           int E, int k, uint32_t flags, float routed_scale,
                           int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
   const int lane = threadIdx.x & 63;
-  float lg[NPL], sc[NPL];
-  uint32_t taken = 0;
+  int me;
+  const float w = topk_wave<NPL>(lg_row, bias, E, k, flags, routed_scale, &me);
+  if (lane < k) {
+    idx_out[lane] = me;
+    w_out[lane] = w;
+  }
+  return me;
+}
+
+// Single token: one wavefront does the selection and the grouping, which
+// for one token has a closed form -- pair j's position is the rank of its
+// expert among the k winners, and offsets[e] counts the winners below e.
+template <int NPL>
+__global__ void __launch_bounds__(64) single_kernel(const float *__restrict__ logits,
+                                                    const float *__restrict__ bias, int E, int k,
+                                                    uint32_t flags, float routed_scale,
+                                                    coli_moe_route_t r) {
+  const int lane = threadIdx.x;
+  int me;
+  const float w = topk_wave<NPL>(logits, bias, E, k, flags, routed_scale, &me);
+  int rank = 0;
+  int cnt_lt[NPL], hit[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) cnt_lt[i] = hit[i] = 0;
+  for (int j = 0; j < k; ++j) {
+    const int ej = __builtin_amdgcn_readlane(me, j);
+    rank += ej < me;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      cnt_lt[i] += ej < e;
+      hit[i] |= ej == e;
+    }
+  }
+  if (lane < k) {
+    r.topk_idx[lane] = me;
+    r.topk_w[lane] = w;
+    r.pairs[rank] = lane;
+    r.pair_pos[lane] = rank;
+    r.union_ids[rank] = me;
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      lg[i] = lg_row[e];
-      float s = bias ? lg[i] + bias[e] : lg[i];
-      sc[i] = (s != s) ? -FLT_MAX * 2.0f : s;  // NaN sorts last (inputs should be finite)
-    } else {
-      lg[i] = 0.0f;
-      sc[i] = 0.0f;
-      taken |= 1u << i;
+      r.counts[e] = hit[i];
+      r.offsets[e] = cnt_lt[i];
     }
   }
-  float m = -FLT_MAX, z = 0.0f;
-  if ((flags & COLI_ROUTE_SIGMOID) == 0) {
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (!((taken >> i) & 1u)) m = fmaxf(m, lg[i]);
-    m = wave_max(m);
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (!((taken >> i) & 1u)) z += expf(lg[i] - m);
-    z = wave_sum(z);
+  if (lane == 0) {
+    r.offsets[E] = k;
+    r.n_union[0] = k;
   }
-  float my_w = 0.0f;
-  int my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    float bs = -INFINITY;
-    int bi = INT_MAX;
-    float bl = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (sc[i] > bs || (sc[i] == bs && e < bi))) {
-        bs = sc[i];
-        bi = e;
-        bl = lg[i];
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float os = __shfl_xor(bs, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      const float ol = __shfl_xor(bl, o, 64);
-      if (os > bs || (os == bs && oi < bi)) {
-        bs = os;
-        bi = oi;
-        bl = ol;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    const float w = (flags & COLI_ROUTE_SIGMOID) ? 1.0f / (1.0f + expf(-bl)) : expf(bl - m) / z;
-    if (lane == j) {
-      my_w = w;
-      my_idx = bi;
-    }
-  }
-  if (flags & COLI_ROUTE_RENORM) {
-    const float sum = wave_sum(lane < k ? my_w : 0.0f);
-    my_w = my_w / sum;
-  }
-  if (lane < k) {
-    idx_out[lane] = my_idx;
-    w_out[lane] = my_w * routed_scale;
-  }
-  return my_idx;
 }
 
 template <int NPL>
@@ -304,7 +383,10 @@ __global__ void __launch_bounds__(kGroupThreads) fused_kernel(const float *__res
 template <int NPL>
 int launch_npl(const Layer &L, const float *logits, const float *bias, int T,
                const coli_moe_route_t &r, hipStream_t s) {
-  if (T <= kSmallT) {
+  if (T == 1) {
+    TraceScope ts(COLI_K_ROUTE_FUSED, s);
+    single_kernel<NPL><<<1, 64, 0, s>>>(logits, bias, L.E, L.k, L.flags, L.routed_scale, r);
+  } else if (T <= kSmallT) {
     // enough wavefronts for one token each and one thread per expert
     const int need = max(64 * T, L.E);
     const int threads = need <= 256 ? 256 : (need <= 512 ? 512 : 1024);
