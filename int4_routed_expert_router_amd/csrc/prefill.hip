@@ -162,12 +162,17 @@ __global__ void __launch_bounds__(1024) plan_kernel(coli_moe_route_t r, int T, i
 
 // ---------------------------------------------------------------- GEMM
 
-// LDS stage: operands already in matrix-core lane order.
+// LDS stage: operands already in matrix-core lane order.  Each 16-row x
+// 32-deep operand tile is 64 lanes x 8 bytes; consecutive tiles are kPad
+// entries apart (64 + 16), which puts the two 32-blocks of a row tile (and
+// of a token tile) in opposite halves of the 256-byte bank window, so the
+// unpacking writes below hit distinct banks within each half-wavefront.
+constexpr int kPad = 80;
 struct Stage {
-  uint2 w[BR / 16][2][64];  // [row tile][32-block][lane] 8 int8 (x16) weights
-  uint2 a[BM / 16][2][64];  // [token tile][32-block][lane] 8 int8 activations
-  float sw[BR];             // weight group scale of each row
-  float4 sa[BM];            // per token: d0/16, -M*d0/16, d1/16, -M*d1/16
+  uint2 w[BR / 16][2][kPad];  // [row tile][32-block][lane] 8 int8 (x16) weights
+  uint2 a[BM / 16][2][kPad];  // [token tile][32-block][lane] 8 int8 activations
+  float sw[BR];               // weight group scale of each row (0 on padding steps)
+  float4 sa[BM];              // per token: d0/16, -M*d0/16, d1/16, -M*d1/16
 };
 
 struct GemmArgs {
@@ -181,10 +186,11 @@ struct GemmArgs {
   int64_t up_offset_s;     // and of its scales
 };
 
-// Row source of weight row r (0..BR-1) of a tile starting at n0.
+// Row source of weight row r (0..BR-1) of a tile starting at n0.  Rows past
+// the matrix are clamped to row 0: they are computed and never stored.
 template <int MODE>
 COLI_DEV void weight_row(const GemmArgs &g, int n0, int r, const uint8_t *&q,
-                         const uint16_t *&s, bool &valid) {
+                         const uint16_t *&s) {
   int n;
   int64_t oq = 0, os = 0;
   if (MODE == kGateUp) {
@@ -196,54 +202,45 @@ COLI_DEV void weight_row(const GemmArgs &g, int n0, int r, const uint8_t *&q,
   } else {
     n = n0 + r;
   }
-  valid = n < g.rows;
-  const int nn = valid ? n : 0;
+  const int nn = n < g.rows ? n : 0;
   q = g.wq + oq + (int64_t)nn * (g.K / 2);
   s = g.ws + os + (int64_t)nn * (g.K / 64);
 }
 
-// Global -> registers for K step ks.
+// What one thread moves from global memory per K step, and where from.
+// Thread t: weights of row 16*(t>>5) + (t&15), 32-block (t>>4)&1; int8
+// activations of token 16*(t>>6) + (t&15), 16-byte quarter 2*((t>>4)&1) +
+// ((t>>5)&1); two fp16 scales: a weight row's group scale (t < 128, twice)
+// or token (t-128)&63's two block scales.  Every thread issues the same
+// four unconditional loads, so the compiler can count them in flight.
+struct Src {
+  const uint8_t *w;
+  const int8_t *a;
+  const uint16_t *s;
+  int s_step;  // scale elements per K step (1 weight, 2 activation)
+  int s_next;  // offset of the second scale
+};
+
 struct Prefetch {
   uint4 w;      // 16 bytes of nibbles (32 values, one 32-block)
   uint4 a;      // 16 bytes of int8 activations
-  uint16_t sc;  // a weight scale (threads 0..127) or an activation scale
+  uint32_t s;   // two fp16 scales, first in the low half
 };
 
-template <int MODE>
-COLI_DEV void load_step(const GemmArgs &g, int n0, const int *rowid, int ntok, int ks,
-                        Prefetch &p) {
-  const int t = threadIdx.x;
-  {  // weights: row t/2, block t%2
-    const uint8_t *q;
-    const uint16_t *s;
-    bool v;
-    weight_row<MODE>(g, n0, t >> 1, q, s, v);
-    p.w = v ? *reinterpret_cast<const uint4 *>(q + ks * (BK / 2) + 16 * (t & 1))
-            : make_uint4(0, 0, 0, 0);
-  }
-  {  // activations: token t/4, 16-byte quarter t%4
-    const int m = t >> 2;
-    p.a = m < ntok ? *reinterpret_cast<const uint4 *>(g.act + (int64_t)rowid[m] * g.K + ks * BK +
-                                                      16 * (t & 3))
-                   : make_uint4(0, 0, 0, 0);
-  }
-  if (t < BR) {
-    const uint8_t *q;
-    const uint16_t *s;
-    bool v;
-    weight_row<MODE>(g, n0, t, q, s, v);
-    p.sc = v ? s[ks] : (uint16_t)0;
-  } else {
-    const int m = (t - BR) >> 1, b = (t - BR) & 1;
-    p.sc = (m < ntok && g.act_d) ? g.act_d[(int64_t)rowid[m] * (g.K / 32) + 2 * ks + b]
-                                 : (uint16_t)0;
-  }
+COLI_DEV void load_step(const Src &src, int ks, Prefetch &p) {
+  p.w = *reinterpret_cast<const uint4 *>(src.w + ks * (BK / 2));
+  p.a = *reinterpret_cast<const uint4 *>(src.a + ks * BK);
+  const uint16_t *s = src.s + ks * src.s_step;
+  p.s = (uint32_t)s[0] | ((uint32_t)s[src.s_next] << 16);
 }
 
-COLI_DEV void store_step(const Prefetch &p, Stage &st) {
+// Registers -> LDS for one step.  `live` is false on the padding steps past
+// the end of K: their weight scales become 0, so they add exactly nothing.
+template <int MODE>
+COLI_DEV void store_step(const Prefetch &p, Stage &st, int wid, bool live) {
   const int t = threadIdx.x;
   {  // 32 nibbles -> 32 int8 (x16), natural k order, into 4 lanes' slots
-    const int r = t >> 1, blk = t & 1, rt = r >> 4, rr = r & 15;
+    const int rt = t >> 5, blk = (t >> 4) & 1, rr = t & 15;
     const uint32_t w[4] = {p.w.x, p.w.y, p.w.z, p.w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -254,20 +251,18 @@ COLI_DEV void store_step(const Prefetch &p, Stage &st) {
       st.w[rt][blk][rr + 16 * i] = make_uint2(lo, hi);
     }
   }
-  {  // activations: token m, k [16*qq, 16*qq+16) of the step
-    const int m = t >> 2, qq = t & 3, mt = m >> 4, mm = m & 15;
-    const int blk = qq >> 1, j0 = 2 * (qq & 1);
-    st.a[mt][blk][mm + 16 * j0] = make_uint2(p.a.x, p.a.y);
-    st.a[mt][blk][mm + 16 * (j0 + 1)] = make_uint2(p.a.z, p.a.w);
+  {  // activations: token tile wid, k [16*qq, 16*qq+16) of the step
+    const int blk = (t >> 4) & 1, j0 = 2 * ((t >> 5) & 1), mm = t & 15;
+    st.a[wid][blk][mm + 16 * j0] = make_uint2(p.a.x, p.a.y);
+    st.a[wid][blk][mm + 16 * (j0 + 1)] = make_uint2(p.a.z, p.a.w);
   }
-  if (t < BR) {
-    st.sw[t] = f16_to_f32(p.sc);
-  } else {
-    const int m = (t - BR) >> 1, b = (t - BR) & 1;
-    const float ds = f16_to_f32(p.sc) * 0.0625f;
-    float *sa = reinterpret_cast<float *>(&st.sa[m]);
-    sa[2 * b] = ds;
-    sa[2 * b + 1] = -kMagicF * ds;
+  if (MODE == kDots) return;
+  if (wid < 2) {
+    st.sw[t] = live ? f16_to_f32((uint16_t)p.s) : 0.0f;
+  } else if (wid == 2) {
+    const float d0 = f16_to_f32((uint16_t)p.s) * 0.0625f;
+    const float d1 = f16_to_f32((uint16_t)(p.s >> 16)) * 0.0625f;
+    st.sa[t - BR] = make_float4(d0, -kMagicF * d0, d1, -kMagicF * d1);
   }
 }
 
@@ -285,25 +280,23 @@ COLI_DEV int wave_row_tile(int wn, int a) {
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_kernel(GemmArgs g, coli_moe_route_t r,
-                                                        const int4 *__restrict__ tiles,
-                                                        const int *__restrict__ ntiles_p,
-                                                        int fixed_ntok, int fixed_expert,
-                                                        int T, int k, int n_ntiles,
-                                                        int64_t expert_stride_q,
-                                                        int64_t expert_stride_s,
-                                                        int8_t *__restrict__ qh_out,
-                                                        uint16_t *__restrict__ dh_out,
-                                                        float *__restrict__ o_out,
-                                                        int32_t *__restrict__ dots_out) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
+            const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
+            int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
+            int8_t *__restrict__ qh_out, uint16_t *__restrict__ dh_out,
+            float *__restrict__ o_out, int32_t *__restrict__ dots_out) {
   __shared__ Stage st[2];
   __shared__ int rowid[BM];
   __shared__ int outrow[BM];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wid >> 1, wm = wid & 1;
   const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
   const int items = ntiles * n_ntiles;
   const int nsteps = g.K / BK;
+  // K steps rounded up to the prefetch depth; the extra steps are padding
+  const int nsteps_pad = (nsteps + kDepth - 1) / kDepth * kDepth;
   // XCD-aware order: consecutive virtual ids (same weights) on one XCD
   const int G = gridDim.x;
   const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
@@ -334,13 +327,34 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
           rid = row0 + m;
         }
       }
-      rowid[m] = rid;
+      rowid[m] = rid;  // tokens past ntok read row 0 and are never stored
       outrow[m] = orow;
     }
     __syncthreads();
     GemmArgs ge = g;
     ge.wq = g.wq + (int64_t)expert * expert_stride_q;
     ge.ws = g.ws + (int64_t)expert * expert_stride_s;
+
+    Src src;
+    {
+      const int t = threadIdx.x;
+      const uint16_t *s_row;
+      weight_row<MODE>(ge, n0, 16 * (t >> 5) + (t & 15), src.w, s_row);
+      src.w += 16 * ((t >> 4) & 1);
+      const int m = 16 * wid + (t & 15);
+      const int qq = 2 * ((t >> 4) & 1) + ((t >> 5) & 1);
+      src.a = ge.act + (int64_t)rowid[m] * ge.K + 16 * qq;
+      if (MODE == kDots || wid < 2) {
+        const uint8_t *unused;
+        weight_row<MODE>(ge, n0, (MODE == kDots ? t & 127 : t), unused, src.s);
+        src.s_step = 1;
+        src.s_next = 0;
+      } else {
+        src.s = ge.act_d + (int64_t)rowid[(t - BR) & 63] * (ge.K / 32);
+        src.s_step = 2;
+        src.s_next = 1;
+      }
+    }
 
     float acc[8][4];
 #pragma unroll
@@ -349,8 +363,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       for (int i = 0; i < 4; ++i) acc[a][i] = 0.0f;
     const coli_i32x4 magic = {(int)kMagic, (int)kMagic, (int)kMagic, (int)kMagic};
 
-    // One K step on LDS stage `cur`: for each of the two 32-blocks, 4 row
-    // tiles x 2 token tiles of MFMAs, then that block's scales.
+    // One K step on LDS stage `cur`: for each 32-block, 4 row tiles x 2
+    // token tiles of MFMAs, then per output (D - M) * d as one FMA (exact
+    // product, one rounding) and acc += s_w * that.  Folding both blocks'
+    // offsets into one constant would save an FMA but leaves the sum
+    // rounded at the offset's magnitude (~1.3e7 * d), about 500x coarser.
     auto step = [&](const Stage &cur, int ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -365,6 +382,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
           for (int ms = 0; ms < 2; ++ms) d[a * 2 + ms] = mfma_i8(aop, bop[ms], magic);
         }
         if (MODE == kDots) {
+          if (ks >= nsteps) continue;
           // exact block dots: (bits - magic) / 16, written [token][row][block]
 #pragma unroll
           for (int a = 0; a < 4; ++a)
@@ -392,34 +410,39 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
               const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                acc[a * 2 + ms][i] = fmaf(swv[i], fmaf(__int_as_float(d[a * 2 + ms][i]), sa.x, sa.y),
-                                          acc[a * 2 + ms][i]);
+                acc[a * 2 + ms][i] = fmaf(
+                    swv[i], fmaf(__int_as_float(d[a * 2 + ms][i]), sa.x, sa.y), acc[a * 2 + ms][i]);
             }
           }
+          // The accumulators are final for this block: without this the
+          // compiler sinks every step's epilogue to the end of the unrolled
+          // loop and keeps all of their MFMA results live at once.
+#pragma unroll
+          for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[a][i]));
         }
       }
     };
 
-    // Pipeline: a register ring holds the raw global data of the next P
-    // steps (loads in flight), LDS holds two unpacked stages.  Step ks
-    // computes on stage ks & 1, refills the ring slot it freed with step
-    // ks + P, and unpacks step ks + 1 into the other stage.
+    // Pipeline: a register ring holds the raw global data of the next
+    // kDepth steps (loads in flight), LDS holds two unpacked stages.  Step
+    // ks computes on stage ks & 1, refills the ring slot it freed with step
+    // ks + kDepth (clamped to the last step, so every load is in bounds and
+    // unconditional), and unpacks step ks + 1 into the other stage.
     Prefetch pf[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i)
-      if (i < nsteps) load_step<MODE>(ge, n0, rowid, ntok, i, pf[i]);
-    store_step(pf[0], st[0]);
+    for (int i = 0; i < kDepth; ++i) load_step(src, min(i, nsteps - 1), pf[i]);
+    store_step<MODE>(pf[0], st[0], wid, true);
     __syncthreads();
-    for (int ks0 = 0; ks0 < nsteps; ks0 += kDepth) {
+    for (int ks0 = 0; ks0 < nsteps_pad; ks0 += kDepth) {
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
         const int ks = ks0 + u;
-        if (ks < nsteps) {
-          if (ks + kDepth < nsteps) load_step<MODE>(ge, n0, rowid, ntok, ks + kDepth, pf[u]);
-          step(st[ks & 1], ks);
-          if (ks + 1 < nsteps) store_step(pf[(u + 1) % kDepth], st[(ks + 1) & 1]);
-          __syncthreads();
-        }
+        load_step(src, min(ks + kDepth, nsteps - 1), pf[u]);
+        step(st[u & 1], ks);
+        store_step<MODE>(pf[(u + 1) % kDepth], st[(u + 1) & 1], wid, ks + 1 < nsteps);
+        __syncthreads();
       }
     }
 
