@@ -127,38 +127,106 @@ def time_graph(stack, warmup, steps):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def busy_gpu(ms=20.0):
-    """Queue ~ms of GPU work so that later eager launches queue up behind it
-    and the per-kernel events measure kernels, not host launch gaps."""
-    import torch
-
-    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    for _ in range(max(1, int(ms / 0.4))):
-        buf.fill_(1)
-    return buf
-
-
 def traced_kernels(fn, reps):
-    """Run fn() reps times eagerly under the library's kernel timer."""
+    """Run fn() reps times eagerly with the library's kernel timer on: each
+    kernel's dispatch stamps its own start/stop events, so the spans are the
+    kernels' execution times (they agree with rocprofv3's kernel trace)."""
     import torch
 
     import int4_routed_expert_router_amd as coli
 
-    timer = coli.KernelTimer(capacity=4096)
+    timer = coli.KernelTimer(capacity=max(4096, 64 * reps))
     torch.cuda.synchronize()
-    res = []
-    for _ in range(reps):
-        keep = busy_gpu()
-        with timer:
+    with timer:
+        for _ in range(reps):
             fn()
-        torch.cuda.synchronize()
-        res.extend(timer.results())
-        del keep
+    torch.cuda.synchronize()
+    res = timer.results()
     timer.close()
     by = {}
     for name, ms in res:
         by.setdefault(name, []).append(ms)
     return {k: {"n": len(v), "avg_us": 1e3 * statistics.mean(v)} for k, v in by.items()}
+
+
+# ------------------------------------------------------ measured HBM traffic
+
+TRAFFIC_PROFILE = os.path.join(_ROOT, "profiles", "decode_gateup_glm52_stack_traffic.md")
+KERNEL_SOURCES = ("int4_routed_expert_router_amd/csrc/decode_single.hip",
+                  "int4_routed_expert_router_amd/csrc/device_common.h",
+                  "int4_routed_expert_router_amd/csrc/internal.h")
+
+
+def kernel_digest():
+    """sha256 over the sources of the single-token decode kernels."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(_ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, or None if it is missing or the kernel changed since."""
+    import re
+
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    dig = re.search(r"kernel source digest:\s*`?([0-9a-f]{16})", text)
+    val = re.search(r"traffic bytes per launch:\s*`?([0-9]+)", text)
+    if not dig or not val or dig.group(1) != kernel_digest():
+        return None
+    return int(val.group(1))
+
+
+def calibrate_copy(mib=256, reps=5):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def summarize_rocprof(path):
+    """Per-kernel summary (markdown) of a rocprofv3 csv output directory:
+    kernel-trace stats, or the mean of each counter per dispatch."""
+    import collections
+    import csv
+    import glob
+    import re
+
+    def short(n):
+        n = n.replace("coli::(anonymous namespace)::", "").replace("void ", "")
+        return re.sub(r"\(.*", "", n)
+
+    stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    pmc = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        print("| kernel | calls | average (us) | min (us) | max (us) | share |")
+        print("|---|---|---|---|---|---|")
+        for r in csv.DictReader(open(stats[0])):
+            print("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+                short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    for f in pmc:
+        acc = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(f)):
+            acc[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        print("| kernel | dispatches | counter | mean per dispatch |")
+        print("|---|---|---|---|")
+        for k, cs in acc.items():
+            for c, v in cs.items():
+                print("| `%s` | %d | %s | %.1f |" % (k, len(v), c, statistics.mean(v)))
 
 
 def cpu_baseline_decode(spec, layers_obj, x_list, logits_list, budget_s=12.0):
@@ -258,8 +326,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="main workload only")
-    ap.add_argument("--trace-reps", type=int, default=3)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the 2048-token GLM prefill workload (for profiling it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 csv output directory")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this routed-expert layer is built and timed on a "
               "single MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -271,6 +347,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.prefill_only:
+        pw = synth.WORKLOADS["glm_prefill"]
+        print(json.dumps(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
+                                           args.steps, args.warmup, copies=1)), flush=True)
+        return
     w = synth.WORKLOADS["glm"]
     spec, T, layers = w.spec, 1, w.layers
     log("generating %d layers (%.1f GiB of int4 experts)" % (layers, synth.container_gib(spec, layers)))
@@ -286,16 +370,21 @@ def main():
     value = T * layers / (ms * 1e-3)
     log("decode stack: %.3f ms/step, %.0f layer-tokens/s, %.0f GB/s" % (ms, value, gbps))
 
-    # dominant kernel: the gate/up GEMV (two thirds of the weight bytes)
-    kern = traced_kernels(lambda: stack.step_eager(0), reps=args.trace_reps)
+    # dominant kernel: the gate/up GEMV (two thirds of the weight bytes),
+    # timed by its own dispatch events over K more steps of the same stack
+    log("timing kernels over %d eager steps" % args.steps)
+    kern = traced_kernels(lambda: stack.step_eager(0), reps=args.steps)
     gu = kern["decode_gateup"]
-    n_slots = spec.top_k * T if T == 1 else None  # T=1: the union is exactly k experts
-    gu_bytes = (n_slots + spec.n_shared) * 2 * spec.inter * spec.hidden * (0.5 + 2 / 64)
+    # T = 1: one launch reads exactly k routed experts + the shared expert
+    gu_bytes = (spec.top_k + spec.n_shared) * 2 * spec.inter * spec.hidden * (0.5 + 2 / 64)
     gu_gbps = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
+    traffic = measured_traffic()
     roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "decode_gateup", "bytes_per_launch": int(gu_bytes),
-                "avg_us": round(gu["avg_us"], 3),
+                "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "traffic_over_algorithmic": round(traffic / gu_bytes, 4) if traffic else None,
+                "kernel": "decode_gateup (gateup_single_kernel)", "bytes_per_launch": int(gu_bytes),
+                "avg_us": round(gu["avg_us"], 3), "launches_timed": gu["n"],
+                "kernel_source_digest": kernel_digest(),
                 "kernels_us": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
     log("kernels (us):", roofline["kernels_us"])
 

@@ -210,13 +210,15 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert,
 
 /* ---- optional kernel timing ----------------------------------------------
  * For benchmarks and profilers.  After coli_moe_set_trace(t) with t != NULL,
- * every later launch records t->start[i] just before and t->stop[i] just
- * after its i-th kernel on the call's stream, stores the kernel's COLI_K_*
+ * every later launch hands t->start[i] and t->stop[i] to the dispatch of its
+ * i-th kernel (hipExtLaunchKernel), so the two events carry that kernel's own
+ * start and end times on the call's stream; it stores the kernel's COLI_K_*
  * id in t->kernel[i] (host memory) and increments t->count, until count
- * reaches capacity (further kernels are not timed).  start/stop hold
- * hipEvent_t handles created by the caller.  coli_moe_set_trace(NULL) turns
- * timing off.  The trace pointer is process-wide: set it from one thread,
- * with no call in flight. */
+ * reaches capacity (further kernels launch untimed).  start/stop hold
+ * hipEvent_t handles created by the caller.  Timed launches cannot be
+ * captured into a HIP graph; coli_moe_set_trace(NULL) turns timing off.  The
+ * trace pointer is process-wide: set it from one thread, with no call in
+ * flight. */
 enum {
   COLI_K_ROUTE_FUSED = 0, COLI_K_TOPK = 1, COLI_K_GROUP = 2, COLI_K_DECODE_GATEUP = 3,
   COLI_K_DECODE_DOWN = 4, COLI_K_COMBINE = 5, COLI_K_QUANTIZE = 6, COLI_K_PLAN = 7,

@@ -209,7 +209,8 @@ def _hip_runtime():
 
 
 class KernelTimer:
-    """Times every kernel the library launches while active (hipEvents)."""
+    """Times every kernel the library launches while active: each dispatch
+    stamps its own start and stop event (hipExtLaunchKernel)."""
 
     def __init__(self, capacity: int = 4096):
         _load()

@@ -397,8 +397,9 @@ template <int TG>
 hipError_t launch_gateup(Shape sh, dim3 grid, size_t lds, hipStream_t s, const Layer &L,
                          const coli_moe_route_t &r, const uint16_t *x, int T, float *h,
                          int nrb, int items) {
-#define COLI_GU(LPR, CPL) \
-  gateup_kernel<LPR, CPL, TG><<<grid, kThreads, lds, s>>>(L, r, x, T, h, nrb, items)
+#define COLI_GU(LPR, CPL)                                                                \
+  launch_k(COLI_K_DECODE_GATEUP, gateup_kernel<LPR, CPL, TG>, grid, dim3(kThreads), lds, s, L, \
+           r, x, T, h, nrb, items)
   switch (sh.lpr * 10 + sh.cpl) {
     case 81: COLI_GU(8, 1); break;
     case 161: COLI_GU(16, 1); break;
@@ -417,8 +418,9 @@ template <int TG>
 hipError_t launch_down(Shape sh, dim3 grid, size_t lds, hipStream_t s, const Layer &L,
                        const coli_moe_route_t &r, int T, const float *h, float *o, int nrb,
                        int items) {
-#define COLI_DN(LPR, CPL) \
-  down_kernel<LPR, CPL, TG><<<grid, kThreads, lds, s>>>(L, r, T, h, o, nrb, items)
+#define COLI_DN(LPR, CPL)                                                                 \
+  launch_k(COLI_K_DECODE_DOWN, down_kernel<LPR, CPL, TG>, grid, dim3(kThreads), lds, s, L, r, \
+           T, h, o, nrb, items)
   switch (sh.lpr * 10 + sh.cpl) {
     case 81: COLI_DN(8, 1); break;
     case 161: COLI_DN(16, 1); break;
@@ -445,8 +447,8 @@ int pick_tg(int T, int K, int bytes_per_value) {
 void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int k, int S,
                     void *y, int y_dtype, hipStream_t s) {
   const dim3 grid((H / 4 + kThreads - 1) / kThreads, T);
-  TraceScope ts(COLI_K_COMBINE, s);
-  combine_kernel<<<grid, kThreads, 0, s>>>(o, r.pair_pos, r.topk_w, T, H, k, S, y, y_dtype);
+  launch_k(COLI_K_COMBINE, combine_kernel, grid, dim3(kThreads), 0, s, o, r.pair_pos, r.topk_w, T,
+           H, k, S, y, y_dtype);
 }
 
 size_t decode_workspace(const Layer &L, int T) {
@@ -475,7 +477,6 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
     const dim3 grid(items < 8192 ? items : 8192);
     const int tg = pick_tg(T, L.H, 2);
     const size_t lds = (size_t)tg * (L.H / 32) * (64 + 4);
-    TraceScope ts(COLI_K_DECODE_GATEUP, s);
     err = tg == 1 ? launch_gateup<1>(sh, grid, lds, s, L, r, x, T, h, nrb, items)
                   : launch_gateup<4>(sh, grid, lds, s, L, r, x, T, h, nrb, items);
     if (err != hipSuccess) return COLI_E_HIP;
@@ -487,7 +488,6 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
     const dim3 grid(items < 8192 ? items : 8192);
     const int tg = pick_tg(T, L.I, 4);
     const size_t lds = (size_t)tg * (L.I / 32) * (128 + 4);
-    TraceScope ts(COLI_K_DECODE_DOWN, s);
     err = tg == 1 ? launch_down<1>(sh, grid, lds, s, L, r, T, h, o, nrb, items)
                   : launch_down<4>(sh, grid, lds, s, L, r, T, h, o, nrb, items);
     if (err != hipSuccess) return COLI_E_HIP;

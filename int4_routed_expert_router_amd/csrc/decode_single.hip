@@ -263,8 +263,8 @@ hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t 
                       int nslots, hipStream_t s) {
   constexpr int RPW = 2;
   const int waves = nslots * (L.I / RPW);
-  TraceScope ts(COLI_K_DECODE_GATEUP, s);
-  gateup_single_kernel<CPL, RPW><<<(waves + kWaves - 1) / kWaves, kThreads, 0, s>>>(L, r, x, h);
+  launch_k(COLI_K_DECODE_GATEUP, gateup_single_kernel<CPL, RPW>,
+           dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0, s, L, r, x, h);
   return hipGetLastError();
 }
 
@@ -279,9 +279,8 @@ template <int LPR, int CPL>
 hipError_t down_shape(const Layer &L, const coli_moe_route_t &r, const float *h, float *o,
                       int nslots, hipStream_t s) {
   const int waves = nslots * (L.H / down_rows_wave<LPR, CPL>());
-  TraceScope ts(COLI_K_DECODE_DOWN, s);
-  down_single_kernel<LPR, CPL, down_rg<LPR, CPL>()>
-      <<<(waves + kWaves - 1) / kWaves, kThreads, 0, s>>>(L, r, h, o);
+  launch_k(COLI_K_DECODE_DOWN, down_single_kernel<LPR, CPL, down_rg<LPR, CPL>()>,
+           dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0, s, L, r, h, o);
   return hipGetLastError();
 }
 

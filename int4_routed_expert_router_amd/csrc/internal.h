@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -53,23 +54,25 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_E_HIP; }
 
-// Optional per-kernel event timing (coli_moe_set_trace).  A launcher wraps
-// each kernel in a TraceScope; with no trace set it does nothing.
+// Optional per-kernel timing (coli_moe_set_trace).  Every kernel goes out
+// through launch_k: with a trace set and a free slot, the dispatch itself
+// stamps the slot's start and stop events (hipExtLaunchKernel), so the
+// recorded span is the kernel's own execution and nothing is queued between
+// kernels; otherwise it is a plain launch (which a HIP graph can capture).
 extern coli_moe_trace_t *g_trace;
-struct TraceScope {
-  int slot = -1;
-  hipStream_t s;
-  TraceScope(int kernel_id, hipStream_t stream) : s(stream) {
-    coli_moe_trace_t *t = g_trace;
-    if (t && t->count < t->capacity) {
-      slot = t->count++;
-      t->kernel[slot] = kernel_id;
-      (void)hipEventRecord(reinterpret_cast<hipEvent_t>(t->start[slot]), s);
-    }
+template <typename... P, typename... A>
+void launch_k(int kernel_id, void (*kernel)(P...), dim3 grid, dim3 block, size_t lds,
+              hipStream_t s, A... args) {
+  coli_moe_trace_t *t = g_trace;
+  if (t && t->count < t->capacity) {
+    const int slot = t->count++;
+    t->kernel[slot] = kernel_id;
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s,
+                          reinterpret_cast<hipEvent_t>(t->start[slot]),
+                          reinterpret_cast<hipEvent_t>(t->stop[slot]), 0u, static_cast<P>(args)...);
+  } else {
+    kernel<<<grid, block, lds, s>>>(static_cast<P>(args)...);
   }
-  ~TraceScope() {
-    if (slot >= 0) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(g_trace->stop[slot]), s);
-  }
-};
+}
 
 }  // namespace coli

@@ -559,8 +559,8 @@ int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, u
                          hipStream_t s) {
   const int64_t nb = n / 32;
   const int64_t grid = (nb + kThreads - 1) / kThreads;
-  TraceScope ts(COLI_K_QUANTIZE, s);
-  quantize_kernel<<<dim3((unsigned)grid), kThreads, 0, s>>>(src, src_dtype, nb, q, d);
+  launch_k(COLI_K_QUANTIZE, quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, src,
+           src_dtype, nb, q, d);
   return hip_status(hipGetLastError());
 }
 
@@ -569,10 +569,8 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
   const PrefillWs w = carve(L, T, ws);
   int rc = launch_quantize_q8_0(x, COLI_SRC_BF16, (int64_t)T * L.H, w.qx, w.dx, s);
   if (rc) return rc;
-  {
-    TraceScope ts(COLI_K_PLAN, s);
-    plan_kernel<<<1, 1024, 0, s>>>(r, T, L.k, L.E, L.S, w.tiles, w.ntiles);
-  }
+  launch_k(COLI_K_PLAN, plan_kernel, dim3(1), dim3(1024), 0, s, r, T, L.k, L.E, L.S, w.tiles,
+           w.ntiles);
   if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   const int mt = max_tiles(L, T);
   {  // gate / up + SwiGLU + Q8_0(h)
@@ -586,10 +584,9 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.up_offset_q = (int64_t)L.I * L.H / 2;
     g.up_offset_s = (int64_t)L.I * L.H / 64;
     const int nn = (L.I + 63) / 64;
-    TraceScope ts(COLI_K_GEMM_GATEUP, s);
-    gemm_kernel<kGateUp><<<grid_for((int64_t)mt * nn), kThreads, 0, s>>>(
-        g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh,
-        nullptr, nullptr);
+    launch_k(COLI_K_GEMM_GATEUP, gemm_kernel<kGateUp>, dim3(grid_for((int64_t)mt * nn)),
+             dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes,
+             L.expert_scales, w.qh, w.dh, nullptr, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
   {  // down
@@ -601,10 +598,9 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.act = w.qh;
     g.act_d = w.dh;
     const int nn = (L.H + BR - 1) / BR;
-    TraceScope ts(COLI_K_GEMM_DOWN, s);
-    gemm_kernel<kDown><<<grid_for((int64_t)mt * nn), kThreads, 0, s>>>(
-        g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr,
-        nullptr, w.o, nullptr);
+    launch_k(COLI_K_GEMM_DOWN, gemm_kernel<kDown>, dim3(grid_for((int64_t)mt * nn)),
+             dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes,
+             L.expert_scales, nullptr, nullptr, w.o, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
   launch_combine(w.o, r, T, L.H, L.k, L.S, y, y_dtype, s);
@@ -624,10 +620,9 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
   const int nn = (g.rows + BR - 1) / BR;
   const int ntile = (T + BM - 1) / BM;
   coli_moe_route_t none{};
-  TraceScope ts(COLI_K_BLOCK_DOTS, s);
-  gemm_kernel<kDots><<<grid_for((int64_t)ntile * nn), kThreads, 0, s>>>(
-      g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes, L.expert_scales, nullptr,
-      nullptr, nullptr, dots);
+  launch_k(COLI_K_BLOCK_DOTS, gemm_kernel<kDots>, dim3(grid_for((int64_t)ntile * nn)),
+           dim3(kThreads), 0, s, g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes,
+           L.expert_scales, nullptr, nullptr, nullptr, dots);
   return hip_status(hipGetLastError());
 }
 

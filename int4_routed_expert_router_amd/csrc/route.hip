@@ -384,23 +384,18 @@ template <int NPL>
 int launch_npl(const Layer &L, const float *logits, const float *bias, int T,
                const coli_moe_route_t &r, hipStream_t s) {
   if (T == 1) {
-    TraceScope ts(COLI_K_ROUTE_FUSED, s);
-    single_kernel<NPL><<<1, 64, 0, s>>>(logits, bias, L.E, L.k, L.flags, L.routed_scale, r);
+    launch_k(COLI_K_ROUTE_FUSED, single_kernel<NPL>, dim3(1), dim3(64), 0, s, logits, bias, L.E,
+             L.k, L.flags, L.routed_scale, r);
   } else if (T <= kSmallT) {
     // enough wavefronts for one token each and one thread per expert
     const int need = max(64 * T, L.E);
     const int threads = need <= 256 ? 256 : (need <= 512 ? 512 : 1024);
-    TraceScope ts(COLI_K_ROUTE_FUSED, s);
-    fused_kernel<NPL><<<1, threads, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
-                                            L.routed_scale, r);
+    launch_k(COLI_K_ROUTE_FUSED, fused_kernel<NPL>, dim3(1), dim3(threads), 0, s, logits, bias, T,
+             L.E, L.k, L.flags, L.routed_scale, r);
   } else {
-    {
-      TraceScope ts(COLI_K_TOPK, s);
-      topk_kernel<NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, L.E, L.k, L.flags,
-                                                   L.routed_scale, r.topk_idx, r.topk_w);
-    }
-    TraceScope ts(COLI_K_GROUP, s);
-    group_kernel<<<1, kGroupThreads, 0, s>>>(T, L.k, L.E, r);
+    launch_k(COLI_K_TOPK, topk_kernel<NPL>, dim3((T + 3) / 4), dim3(256), 0, s, logits, bias, T,
+             L.E, L.k, L.flags, L.routed_scale, r.topk_idx, r.topk_w);
+    launch_k(COLI_K_GROUP, group_kernel, dim3(1), dim3(kGroupThreads), 0, s, T, L.k, L.E, r);
   }
   return hip_status(hipGetLastError());
 }
