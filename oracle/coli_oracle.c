@@ -26,6 +26,9 @@
  *
  * Pins: every function here is checked by tests against an independent
  * numpy brute force, closed forms, invariants and hand-derived fixtures.
+ * Parity unpinned: for softmax-routed layers, whether the k selected
+ * probabilities are renormalised.  No page decides it; both readings are
+ * implemented (the RENORM flag) and each is pinned to its own definition.
  */
 #include <math.h>
 #include <stdint.h>
