@@ -152,7 +152,7 @@ def traced_kernels(fn, reps):
 # ------------------------------------------------------ measured HBM traffic
 
 TRAFFIC_PROFILE = os.path.join(_ROOT, "profiles", "decode_gateup_glm52_stack_traffic.md")
-KERNEL_SOURCES = ("int4_routed_expert_router_amd/csrc/decode_single.hip",
+KERNEL_SOURCES = ("int4_routed_expert_router_amd/csrc/decode_stream.hip",
                   "int4_routed_expert_router_amd/csrc/device_common.h",
                   "int4_routed_expert_router_amd/csrc/internal.h")
 

@@ -464,7 +464,7 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
   const int nslots = max_union(L, T) + L.S;
   hipError_t err = hipSuccess;
 
-  if (T == 1 && launch_decode_single(L, r, x, h, o, s, &err)) {
+  if (launch_decode_stream(L, r, x, T, h, o, s, &err)) {
     if (err != hipSuccess) return COLI_E_HIP;
     launch_combine(o, r, T, L.H, L.k, L.S, y, y_dtype, s);
     return hip_status(hipGetLastError());

@@ -1,0 +1,434 @@
+// decode_stream.hip -- decode GEMVs for small batches (T <= 16).
+//
+// Work is cut into union slots: one expert of the batch union (or the
+// shared expert) together with the tokens routed to it, whose pair-major
+// h / o rows are consecutive.  A slot's rows are split into short runs (2
+// gate/up row pairs or about 8 KB of down rows), one per wavefront.  A
+// wavefront requests all of its weights at once, then fetches activation
+// chunks and computes for each of the slot's tokens in turn, so an expert's
+// weights cross HBM once per batch however many tokens chose it: many short
+// independent wavefronts keep the most bytes in flight.  Gate/up stages the
+// slot's activations per workgroup in LDS, up to four tokens at a time; down
+// reads its chunks of each token's h directly, as gate/up wrote them.
+// Nibbles become exact bf16 values 136 + q (one v_bitop3 per pair after a
+// shift) and meet the activations in v_dot2_f32_bf16; each 32-chunk's bias
+// 136 * sum(x) is removed before its fp16 group scale.  Lane partials of
+// several rows are combined with a reduce-scatter (each shuffle step halves
+// the values a lane carries).  A token's arithmetic does not depend on the
+// other tokens of the batch.
+#include "device_common.h"
+#include "internal.h"
+
+namespace coli {
+namespace {
+
+constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kWaves = kThreads / 64;
+
+// Sum NV values over groups of W lanes (W, NV powers of two, NV <= W).
+// Every lane ends with the total of value value_index<NV, W>(lane).
+template <int NV, int W>
+COLI_DEV float reduce_scatter(float (&v)[NV], int lane) {
+  int stride = W / 2;
+#pragma unroll
+  for (int nv = NV; nv > 1; nv >>= 1, stride >>= 1) {
+    const bool upper = (lane & stride) != 0;
+#pragma unroll
+    for (int i = 0; i < nv / 2; ++i) {
+      const float keep = upper ? v[i + nv / 2] : v[i];
+      const float send = upper ? v[i] : v[i + nv / 2];
+      v[i] = keep + __shfl_xor(send, stride, 64);
+    }
+  }
+#pragma unroll
+  for (; stride > 0; stride >>= 1) v[0] += __shfl_xor(v[0], stride, 64);
+  return v[0];
+}
+
+template <int NV, int W>
+COLI_DEV int value_index(int lane) {
+  int idx = 0, stride = W / 2;
+#pragma unroll
+  for (int nv = NV; nv > 1; nv >>= 1, stride >>= 1)
+    if (lane & stride) idx += nv / 2;
+  return idx;
+}
+
+// Union slot `slot`: slots 0 .. S-1 are the shared expert (all T tokens, rows
+// T*k + t), then one slot per routed expert of the union (counts[e] tokens,
+// rows offsets[e] + i).  Token i of a slot has pair-major row pos0 + i.
+struct Slot {
+  int e, cnt, pos0;
+  bool shared;
+};
+// ONE: a single-token batch, where every slot holds token 0 and the routed
+// slots' rows are their offsets (no counts or pair lists to read).
+template <bool ONE>
+COLI_DEV Slot slot_of(const coli_moe_route_t &r, const Layer &L, int T, int slot) {
+  Slot s;
+  if (ONE) {
+    s.shared = slot < L.S;
+    s.e = s.shared ? L.E : r.union_ids[slot - L.S];
+    s.cnt = 1;
+    s.pos0 = s.shared ? L.k : r.offsets[s.e];
+    return s;
+  }
+  if (slot < L.S) {
+    s.e = L.E;
+    s.cnt = T;
+    s.pos0 = T * L.k;
+    s.shared = true;
+  } else {
+    s.e = r.union_ids[slot - L.S];
+    s.cnt = r.counts[s.e];
+    s.pos0 = r.offsets[s.e];
+    s.shared = false;
+  }
+  return s;
+}
+template <bool ONE>
+COLI_DEV int token_of(const coli_moe_route_t &r, const Layer &L, const Slot &s, int i) {
+  if (ONE) return 0;
+  return s.shared ? i : r.pairs[s.pos0 + i] / L.k;
+}
+
+// Paired activations of chunk c in LDS: four 16-byte quads, stored
+// quad-major so that consecutive lanes (consecutive chunks) read
+// consecutive 16 bytes.
+struct XChunk {
+  uint32_t p[16];
+};
+COLI_DEV void lds_chunk(const uint4 *xs, int nch, int c, XChunk &out) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = xs[q * nch + c];
+    out.p[4 * q] = v.x;
+    out.p[4 * q + 1] = v.y;
+    out.p[4 * q + 2] = v.z;
+    out.p[4 * q + 3] = v.w;
+  }
+}
+
+// Makes a packed weight quad opaque to the optimiser at this point.  Called
+// once per token inside the token loops: otherwise the (loop-invariant)
+// nibble unpacking is hoisted out of the loop, or above the activation
+// staging, and the unpacked values (four times the registers of the packed
+// ones) stay live across it.
+COLI_DEV void opaque(uint4 &w) {
+  asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+}
+
+// 32 weights of one chunk (a 16-byte load) dotted with paired activations;
+// the accumulator starts at -bias.
+COLI_DEV float chunk_dot(const uint4 w, const uint32_t *xp, float neg_bias) {
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  float a = neg_bias;
+#pragma unroll
+  for (int dw = 0; dw < 4; ++dw) {
+    uint32_t p[4];
+    nib8_to_bf16x4(wv[dw], p[0], p[1], p[2], p[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a = dot2_bf16(p[q], xp[4 * dw + q], a);
+  }
+  return a;
+}
+
+// The down GEMV consumes h as bf16 hi + lo halves (16 significant bits),
+// already paired to the nibble order.  Row layout (I values, 4 bytes each):
+// chunk c of 32 values holds 16 hi dwords then 16 lo dwords; dword 4*o + q
+// of a half pairs values 8o + q (low 16 bits) and 8o + q + 4 (high 16 bits).
+COLI_DEV void store_h_pair(float *row, int n, float h) {
+  const uint32_t hi = f32_to_bf16_bits(h);
+  const uint32_t lo = f32_to_bf16_bits(h - bf16_to_f32(hi));
+  const int c = n >> 5, w = n & 31, o = w >> 3, k = w & 7;
+  uint16_t *base = reinterpret_cast<uint16_t *>(row + 32 * c);
+  const int half = 2 * (4 * o + (k & 3)) + (k >> 2);
+  base[half] = (uint16_t)hi;
+  base[32 + half] = (uint16_t)lo;
+}
+
+// ----------------------------------------------------------- gate / up
+
+// H = 2048 * CPL: lane owns chunks lane + 64 i (i < CPL) of every row.  A
+// wavefront computes RPW rows n of one slot for each of the slot's tokens;
+// all their weights are requested at once, before the workgroup's activation
+// staging, so the loads of every resident wavefront overlap.  The four
+// wavefronts of a workgroup share the slot (I / RPW is a multiple of 4), so
+// the staging loop and its barriers are uniform over the workgroup.  Dynamic
+// LDS holds tg tokens: tg x 4 x NCH quads of paired bf16, then tg x NCH
+// chunk biases.
+template <int CPL, int RPW, bool ONE>
+__global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
+    Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
+    float *__restrict__ h_out) {
+  constexpr int NCH = 64 * CPL;
+  extern __shared__ uint4 smem[];
+  float *xbias = reinterpret_cast<float *>(smem + tg * 4 * NCH);
+  const int lane = threadIdx.x & 63;
+  const int H = L.H, I = L.I;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int waves_per_slot = I / RPW;
+  const int slot = wave / waves_per_slot;
+  // (one token always has exactly k distinct experts: every slot is live)
+  if (!ONE && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
+  const Slot sl = slot_of<ONE>(r, L, T, slot);
+  const int n0 = (wave % waves_per_slot) * RPW;
+  const uint8_t *qg = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)n0 * (H / 2) + 16 * lane;
+  const uint8_t *qu = qg + (int64_t)I * H / 2;
+  const uint16_t *sgp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)n0 * (H / 64) + lane / 2;
+  const uint16_t *sup = sgp + (int64_t)I * H / 64;
+  // One token: this thread's activation chunk (c = threadIdx.x < NCH) is
+  // requested before the weights, so that staging it waits for it alone
+  // (the memory counter retires loads in issue order).
+  uint4 xpre[4];
+  if (ONE && threadIdx.x < NCH) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(x) + 4 * threadIdx.x;
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) xpre[dw] = src[dw];
+  }
+  uint4 wg[RPW][CPL], wu[RPW][CPL];
+  uint16_t sg[RPW][CPL], su[RPW][CPL];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t ob = (int64_t)j * (H / 2) + 1024 * i;
+      const int64_t os = (int64_t)j * (H / 64) + 32 * i;
+      wg[j][i] = *reinterpret_cast<const uint4 *>(qg + ob);
+      wu[j][i] = *reinterpret_cast<const uint4 *>(qu + ob);
+      sg[j][i] = sgp[os];
+      su[j][i] = sup[os];
+    }
+    // a single token collapses to straight-line code, so the staging loads
+  // below are issued while the weight loads are still in flight
+  const int cnt = ONE ? 1 : sl.cnt;
+  const int step = ONE ? 1 : tg;
+#pragma unroll 1
+  for (int g0 = 0; g0 < cnt; g0 += step) {
+    const int nt = ONE ? 1 : min(tg, cnt - g0);
+    if (g0) __syncthreads();  // the previous group's activations are consumed
+    // stage x: chunk c of token g0 + ti -> four quads of paired bf16 + bias
+    for (int idx = threadIdx.x; idx < nt * NCH; idx += kThreads) {
+      const int ti = idx / NCH, c = idx - ti * NCH;
+      const int t = token_of<ONE>(r, L, sl, g0 + ti);
+      const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)t * H) + 4 * c;
+      uint4 *xs = smem + ti * 4 * NCH;
+      uint32_t p[16];
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const uint4 v = ONE ? xpre[dw] : src[dw];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        x8_to_pairs(d, &p[4 * dw]);
+        xs[dw * NCH + c] = make_uint4(p[4 * dw], p[4 * dw + 1], p[4 * dw + 2], p[4 * dw + 3]);
+      }
+      xbias[ti * NCH + c] = chunk_bias(p);
+    }
+    __syncthreads();
+    #pragma unroll 1
+    for (int ti = 0; ti < nt; ++ti) {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          opaque(wg[j][i]);
+          opaque(wu[j][i]);
+        }
+      const uint4 *xs = smem + ti * 4 * NCH;
+      float v[2 * RPW];
+#pragma unroll
+      for (int j = 0; j < 2 * RPW; ++j) v[j] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        XChunk xc;
+        lds_chunk(xs, NCH, lane + 64 * i, xc);
+        const float nb = xbias[ti * NCH + lane + 64 * i];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+          v[2 * j] = fmaf(f16_to_f32(sg[j][i]), chunk_dot(wg[j][i], xc.p, nb), v[2 * j]);
+          v[2 * j + 1] = fmaf(f16_to_f32(su[j][i]), chunk_dot(wu[j][i], xc.p, nb), v[2 * j + 1]);
+        }
+      }
+      // value 2j is the gate of row j, 2j+1 its up; bring them to one lane
+      const float tot = reduce_scatter<2 * RPW, 64>(v, lane);
+      const int vi = value_index<2 * RPW, 64>(lane);
+      constexpr int kSpan = 64 / (2 * RPW);  // lanes holding one value
+      const float up = __shfl_down(tot, kSpan, 64);
+      if ((lane % kSpan) == 0 && (vi & 1) == 0)
+        store_h_pair(h_out + (int64_t)(sl.pos0 + g0 + ti) * I, n0 + vi / 2, silu_mul(tot, up));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down
+
+// K = I: LPR lanes per row (LPR = I/32 when I < 2048, else 64 with CPL
+// chunks each); RPI = 64/LPR rows share a wave instruction; a wavefront
+// computes RG such row groups (RPI * RG rows m) of one slot, for each of the
+// slot's tokens with the same weights in registers.  Each lane reads its
+// chunks of the token's h (hi + lo pairs, written by gate/up).
+template <int LPR, int CPL, int RG, bool ONE>
+__global__ void __launch_bounds__(kThreads) down_stream_kernel(
+    Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
+    float *__restrict__ o_out) {
+  constexpr int RPI = 64 / LPR;
+  constexpr int RPW = RPI * RG;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane / LPR, lc = lane % LPR;
+  const int H = L.H, I = L.I;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int waves_per_slot = H / RPW;
+  const int slot = wave / waves_per_slot;
+  if (!ONE && slot >= L.S + r.n_union[0]) return;
+  const Slot sl = slot_of<ONE>(r, L, T, slot);
+  const int m0 = (wave % waves_per_slot) * RPW;
+  const uint8_t *qd = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)I * H +
+                      (int64_t)(m0 + lr) * (I / 2) + 16 * lc;
+  const uint16_t *sdp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64 +
+                        (int64_t)(m0 + lr) * (I / 64) + lc / 2;
+  uint4 w[RG][CPL];
+  uint16_t sc[RG][CPL];
+#pragma unroll
+  for (int j = 0; j < RG; ++j)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t row = RPI * j;
+      w[j][i] = *reinterpret_cast<const uint4 *>(qd + row * (I / 2) + 16 * LPR * i);
+      sc[j][i] = sdp[row * (I / 64) + LPR / 2 * i];
+    }
+    const int cnt = ONE ? 1 : sl.cnt;
+#pragma unroll 1
+  for (int ti = 0; ti < cnt; ++ti) {
+    if (!ONE) {
+#pragma unroll
+      for (int j = 0; j < RG; ++j)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) opaque(w[j][i]);
+    }
+    const int64_t pos = sl.pos0 + ti;
+    float v[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) v[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(h_in + pos * I + 32 * (lc + LPR * i));
+      XChunk hi, lo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 a = src[q], b = src[4 + q];
+        hi.p[4 * q] = a.x, hi.p[4 * q + 1] = a.y, hi.p[4 * q + 2] = a.z, hi.p[4 * q + 3] = a.w;
+        lo.p[4 * q] = b.x, lo.p[4 * q + 1] = b.y, lo.p[4 * q + 2] = b.z, lo.p[4 * q + 3] = b.w;
+      }
+      const float nb = chunk_bias2(hi.p, lo.p);
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        const uint32_t wv[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
+        float a = nb;
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          uint32_t p[4];
+          nib8_to_bf16x4(wv[dw], p[0], p[1], p[2], p[3]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a = dot2_bf16(p[q], hi.p[4 * dw + q], a);
+            a = dot2_bf16(p[q], lo.p[4 * dw + q], a);
+          }
+        }
+        v[j] = fmaf(f16_to_f32(sc[j][i]), a, v[j]);
+      }
+    }
+    const float tot = reduce_scatter<RG, LPR>(v, lc);
+    constexpr int kSpan = LPR / RG;
+    if ((lc % kSpan) == 0)
+      o_out[pos * H + m0 + lr + RPI * value_index<RG, LPR>(lc)] = tot;
+  }
+}
+
+constexpr int kMaxStage = 4;  // tokens of one slot staged in LDS at once
+
+template <int CPL>
+hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                      float *h, int nslots, hipStream_t s) {
+  constexpr int RPW = 2;
+  const int waves = nslots * (L.I / RPW);
+  // up to kMaxStage tokens per LDS stage, within 64 KB
+  const size_t per_token = (size_t)64 * CPL * (4 * sizeof(uint4) + sizeof(float));
+  int tg = T < kMaxStage ? T : kMaxStage;
+  while (tg > 1 && tg * per_token > 65536) --tg;
+  const size_t lds = tg * per_token;
+  const dim3 grid((waves + kWaves - 1) / kWaves);
+  if (T == 1)
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, true>, grid, dim3(kThreads),
+             lds, s, L, r, x, T, tg, h);
+  else
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, false>, grid, dim3(kThreads),
+             lds, s, L, r, x, T, tg, h);
+  return hipGetLastError();
+}
+
+// row groups per wavefront of the down GEMV: about eight 16-byte loads per
+// lane (8 rows of 1 KB when I = 2048)
+template <int LPR, int CPL>
+constexpr int down_rg() { return CPL == 1 ? 8 : (CPL == 2 ? 4 : 2); }
+template <int LPR, int CPL>
+constexpr int down_rows_wave() { return (64 / LPR) * down_rg<LPR, CPL>(); }
+
+template <int LPR, int CPL>
+hipError_t down_shape(const Layer &L, const coli_moe_route_t &r, int T, const float *h,
+                      float *o, int nslots, hipStream_t s) {
+  const int waves = nslots * (L.H / down_rows_wave<LPR, CPL>());
+  const dim3 grid((waves + kWaves - 1) / kWaves);
+  constexpr int RG = down_rg<LPR, CPL>();
+  if (T == 1)
+    launch_k(COLI_K_DECODE_DOWN, down_stream_kernel<LPR, CPL, RG, true>, grid, dim3(kThreads), 0,
+             s, L, r, T, h, o);
+  else
+    launch_k(COLI_K_DECODE_DOWN, down_stream_kernel<LPR, CPL, RG, false>, grid, dim3(kThreads),
+             0, s, L, r, T, h, o);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Launches gate/up and down for T <= kMaxStreamT tokens when the shape has a
+// streaming path (H a multiple of 2048 up to 8192; I in {512, 1024} or a
+// multiple of 2048 up to 8192; H a multiple of a down wavefront's rows).
+// Returns false, launching nothing, otherwise.
+bool launch_decode_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                          float *h, float *o, hipStream_t s, hipError_t *err) {
+  if (T > kMaxStreamT) return false;
+  const int nslots = max_union(L, T) + L.S;
+  const int hc = L.H / 2048;
+  if (L.H % 2048 || hc < 1 || hc > 4) return false;
+  int lpr, cpl, rows_wave;
+  if (L.I == 512) {
+    lpr = 16, cpl = 1, rows_wave = down_rows_wave<16, 1>();
+  } else if (L.I == 1024) {
+    lpr = 32, cpl = 1, rows_wave = down_rows_wave<32, 1>();
+  } else if (L.I % 2048 == 0 && L.I / 2048 <= 4) {
+    lpr = 64, cpl = L.I / 2048;
+    rows_wave = cpl == 1 ? down_rows_wave<64, 1>() : cpl == 2 ? down_rows_wave<64, 2>()
+                : cpl == 3 ? down_rows_wave<64, 3>() : down_rows_wave<64, 4>();
+  } else {
+    return false;
+  }
+  if (L.I % 8 || L.H % rows_wave) return false;
+  hipError_t e = hipSuccess;
+  switch (hc) {
+    case 1: e = gateup_cpl<1>(L, r, x, T, h, nslots, s); break;
+    case 2: e = gateup_cpl<2>(L, r, x, T, h, nslots, s); break;
+    case 3: e = gateup_cpl<3>(L, r, x, T, h, nslots, s); break;
+    default: e = gateup_cpl<4>(L, r, x, T, h, nslots, s); break;
+  }
+  if (e == hipSuccess) {
+    if (lpr == 16) e = down_shape<16, 1>(L, r, T, h, o, nslots, s);
+    else if (lpr == 32) e = down_shape<32, 1>(L, r, T, h, o, nslots, s);
+    else if (cpl == 1) e = down_shape<64, 1>(L, r, T, h, o, nslots, s);
+    else if (cpl == 2) e = down_shape<64, 2>(L, r, T, h, o, nslots, s);
+    else if (cpl == 3) e = down_shape<64, 3>(L, r, T, h, o, nslots, s);
+    else e = down_shape<64, 4>(L, r, T, h, o, nslots, s);
+  }
+  *err = e;
+  return true;
+}
+
+}  // namespace coli

@@ -43,7 +43,10 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
                   void *y, int y_dtype, void *ws, hipStream_t s);
 int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                    void *y, int y_dtype, void *ws, hipStream_t s);
-bool launch_decode_single(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
+// Streaming gate/up + down GEMVs for decode batches of up to kMaxStreamT
+// tokens (decode_stream.hip); false if the shape has no streaming path.
+constexpr int kMaxStreamT = 16;
+bool launch_decode_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                           float *h, float *o, hipStream_t s, hipError_t *err);
 void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int k, int S,
                     void *y, int y_dtype, hipStream_t s);
