@@ -166,7 +166,8 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
   float *xbias = reinterpret_cast<float *>(smem + tg * 4 * NCH);
   const int lane = threadIdx.x & 63;
   const int H = L.H, I = L.I;
-  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  // wave-uniform: the slot lookups become scalar loads, weight bases scalar
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
   const int waves_per_slot = I / RPW;
   const int slot = wave / waves_per_slot;
   // (one token always has exactly k distinct experts: every slot is live)
@@ -275,7 +276,7 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
   const int lane = threadIdx.x & 63;
   const int lr = lane / LPR, lc = lane % LPR;
   const int H = L.H, I = L.I;
-  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
   const int waves_per_slot = H / RPW;
   const int slot = wave / waves_per_slot;
   if (!ONE && slot >= L.S + r.n_union[0]) return;

@@ -279,6 +279,120 @@ COLI_DEV int wave_row_tile(int wn, int a) {
   return MODE == kGateUp ? (a < 2 ? 2 * wn + a : 4 + 2 * wn + (a - 2)) : 4 * wn + a;
 }
 
+// One work item of the grouped GEMM: a tile of up to BM token rows of one
+// expert, times one block of output rows.  Fills the token row ids (input
+// rows) and pair-major output rows of the tile in LDS; tokens past ntok read
+// row 0 and are never stored.
+struct Item {
+  int expert, row0, ntok, n0;
+};
+
+template <int MODE>
+COLI_DEV Item setup_item(int item, int n_ntiles, const int4 *tiles, int fixed_ntok,
+                         int fixed_expert, const coli_moe_route_t &r, int T, int k,
+                         int *rowid, int *outrow) {
+  Item it;
+  const int tile = item / n_ntiles, ntile = item % n_ntiles;
+  if (tiles) {
+    const int4 td = tiles[tile];
+    it.expert = td.x;
+    it.row0 = td.y;
+    it.ntok = td.z;
+  } else {
+    it.expert = fixed_expert;
+    it.row0 = tile * BM;
+    it.ntok = min(BM, fixed_ntok - it.row0);
+  }
+  it.n0 = ntile * (MODE == kGateUp ? 64 : BR);
+  __syncthreads();  // the previous item's epilogue has read rowid / outrow
+  if (threadIdx.x < BM) {
+    const int m = threadIdx.x;
+    int rid = 0, orow = 0;
+    if (m < it.ntok) {
+      orow = it.row0 + m;
+      if (MODE == kGateUp) {
+        rid = (it.row0 >= T * k) ? (it.row0 - T * k) + m : r.pairs[it.row0 + m] / k;
+      } else {
+        rid = it.row0 + m;
+      }
+    }
+    rowid[m] = rid;
+    outrow[m] = orow;
+  }
+  __syncthreads();
+  return it;
+}
+
+// Epilogue of a work item from the per-wave accumulators (8 16x16 tiles:
+// a*2+ms = row tile a of the wave, token tile ms).
+//  gate/up: h = silu(g) * u, then Q8_0 of h per 32 channels -- one wave
+//           holds exactly the 32 channels of one block for its 32 tokens.
+//  down   : fp32 o rows.
+template <int MODE>
+COLI_DEV void epilogue(const float (&acc)[8][4], const GemmArgs &g, const Item &it,
+                       const int *outrow, int wn, int wm, int lane, int8_t *qh_out,
+                       uint16_t *dh_out, float *o_out) {
+  if (MODE == kGateUp) {
+    // acc[a*2+ms]: a in {0,1} gate row tiles, {2,3} the up tiles of the same
+    // channels (row sub-tile ns = a & 1)
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const int m = 32 * wm + 16 * ms + (lane & 15);
+      float hv[2][4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hv[ns][i] = silu_mul(acc[ns * 2 + ms][i], acc[(2 + ns) * 2 + ms][i]);
+          amax = fmaxf(amax, fabsf(hv[ns][i]));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const float dq = __fdiv_rn(amax, 127.0f);
+      uint32_t qw[2];
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int q = 0;
+          if (amax != 0.0f) {
+            q = (int)roundf(__fdiv_rn(hv[ns][i], dq));
+            q = max(-127, min(127, q));
+          }
+          packed |= (uint32_t)(q & 0xff) << (8 * i);
+        }
+        qw[ns] = packed;
+      }
+      if (m < it.ntok) {
+        const int I = g.rows;
+        const int ch = it.n0 + 32 * wn;  // first channel of this wave's block
+        if (ch < I) {
+          int8_t *qrow = qh_out + (int64_t)outrow[m] * I + ch;
+          *reinterpret_cast<uint32_t *>(qrow + 4 * (lane >> 4)) = qw[0];
+          *reinterpret_cast<uint32_t *>(qrow + 16 + 4 * (lane >> 4)) = qw[1];
+          if ((lane >> 4) == 0) dh_out[(int64_t)outrow[m] * (I / 32) + ch / 32] = f32_to_f16_bits(dq);
+        }
+      }
+    }
+  } else if (MODE == kDown) {
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const int m = 32 * wm + 16 * ms + (lane & 15);
+      if (m >= it.ntok) continue;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int n = it.n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4);
+        if (n < g.rows)
+          *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
+              make_float4(acc[a * 2 + ms][0], acc[a * 2 + ms][1], acc[a * 2 + ms][2],
+                          acc[a * 2 + ms][3]);
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
@@ -302,35 +416,9 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
   const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   for (int item = vid; item < items; item += G) {
-    const int tile = item / n_ntiles, ntile = item % n_ntiles;
-    int expert, row0, ntok;
-    if (tiles) {
-      const int4 td = tiles[tile];
-      expert = td.x;
-      row0 = td.y;
-      ntok = td.z;
-    } else {
-      expert = fixed_expert;
-      row0 = tile * BM;
-      ntok = min(BM, fixed_ntok - row0);
-    }
-    const int n0 = ntile * (MODE == kGateUp ? 64 : BR);
-    __syncthreads();
-    if (threadIdx.x < BM) {
-      const int m = threadIdx.x;
-      int rid = 0, orow = 0;
-      if (m < ntok) {
-        orow = row0 + m;
-        if (MODE == kGateUp) {
-          rid = (row0 >= T * k) ? (row0 - T * k) + m : r.pairs[row0 + m] / k;
-        } else {
-          rid = row0 + m;
-        }
-      }
-      rowid[m] = rid;  // tokens past ntok read row 0 and are never stored
-      outrow[m] = orow;
-    }
-    __syncthreads();
+    const Item it = setup_item<MODE>(item, n_ntiles, tiles, fixed_ntok, fixed_expert, r, T, k,
+                                     rowid, outrow);
+    const int expert = it.expert, row0 = it.row0, ntok = it.ntok, n0 = it.n0;
     GemmArgs ge = g;
     ge.wq = g.wq + (int64_t)expert * expert_stride_q;
     ge.ws = g.ws + (int64_t)expert * expert_stride_s;
@@ -446,65 +534,279 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
       }
     }
 
-    if (MODE == kGateUp) {
-      // acc[0..3] = gate tiles (ns = a / 2 ... ) laid out as a*2+ms with a in
-      // {0,1} gate and {2,3} up for row sub-tiles ns = a & 1.
+    epilogue<MODE>(acc, g, it, outrow, wn, wm, lane, qh_out, dh_out, o_out);
+  }
+}
+
+// ----------------------------------------------- GEMM, K a multiple of 256
+
+// The same work items, epilogues and arithmetic as gemm_kernel, with one
+// LDS stage holding four K steps (256 k).  Global loads then move whole
+// 128-byte lines: per 16-byte load instruction a wavefront covers 8 weight
+// rows x 128 bytes (4 steps of one row) or 4 token rows x 256 bytes, and the
+// scales of 4 steps arrive in one 8-byte load per thread.  That keeps the
+// number of distinct cache lines a wavefront touches per K step low, which
+// is what the per-step loads of gemm_kernel are limited by.  One group of
+// loads is in flight while the previous group is computed; two barriers per
+// group.
+constexpr int kGroup = 4;   // K steps per LDS stage
+struct Stage4 {
+  uint2 w[BR / 16][kGroup][2][64];  // [row tile][step][32-block][lane ^ swz]
+  uint2 a[BM / 16][kGroup][2][64];  // [token tile][step][32-block][lane ^ swz]
+  float sw[kGroup][BR];             // weight group scales
+  float2 sa[kGroup][BM];            // d0/16, d1/16 of each token
+};
+// Operand entry e of the tile of (step s, block b) sits at e ^ swz(s, b).
+// The XOR permutes each tile, so a wavefront reading all 64 entries still
+// reads one contiguous 512-byte tile; the unpacking writes, where the lanes
+// of a half-wavefront cover 8 (step, block) pairs x 4 consecutive entries,
+// land on 32 distinct 8-byte bank pairs.  (52.5 KB per workgroup: three
+// workgroups per compute unit.)
+COLI_DEV int swz(int s, int b) { return 4 * (2 * s + b); }
+
+// Per thread: four 16-byte weight loads (load j: row 32*wave + 8j +
+// 4*(lane>>5) + (lane&3), 16-byte chunk (lane>>2)&7 of the row's 128 bytes),
+// four 16-byte activation loads (load j: token 16*wave + 4j + (lane&3),
+// chunk 4*step + quarter of the token's 256 bytes with step (lane>>2)&3 and
+// quarter 2*((lane>>4)&1) + (lane>>5)), and one 8-byte scale load.
+struct Src4 {
+  const uint8_t *wbase;  // the expert's matrix (wave-uniform)
+  const int8_t *abase;   // activation rows (wave-uniform)
+  uint32_t w[4];         // byte offsets of the four weight loads from wbase
+  uint32_t a[4];         // byte offsets of the four activation loads from abase
+  const uint16_t *s;
+  int s_group;  // scale elements per group: 4 (a weight row) or 8 (a token)
+};
+struct Group4 {
+  uint4 w[4], a[4];
+  uint2 s;
+};
+
+COLI_DEV void load_group(const Src4 &src, int gi, Group4 &G) {
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
-        const int m = 32 * wm + 16 * ms + (lane & 15);
-        float hv[2][4];
-        float amax = 0.0f;
+  for (int j = 0; j < 4; ++j)
+    G.w[j] = *reinterpret_cast<const uint4 *>(src.wbase + (src.w[j] + gi * 128));
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
+  for (int j = 0; j < 4; ++j)
+    G.a[j] = *reinterpret_cast<const uint4 *>(src.abase + (src.a[j] + gi * 256));
+  G.s = *reinterpret_cast<const uint2 *>(src.s + gi * src.s_group);
+}
+
+// Registers -> LDS.  Within each half-wavefront the 8-byte writes land on
+// distinct banks: lane bits 0-1 pick consecutive entries and the (step,
+// block) pair moves the address by a multiple of 4 entries (mod 32).
+template <int MODE>
+COLI_DEV void store_group(const Group4 &G, Stage4 &st, int wid) {
+  const int l = threadIdx.x & 63;
+  {
+    const int c = (l >> 2) & 7, s = c >> 1, b = c & 1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hv[ns][i] = silu_mul(acc[ns * 2 + ms][i], acc[(2 + ns) * 2 + ms][i]);
-            amax = fmaxf(amax, fabsf(hv[ns][i]));
-          }
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const float dq = __fdiv_rn(amax, 127.0f);
-        uint32_t qw[2];
+    for (int j = 0; j < 4; ++j) {
+      const int rt = 2 * wid + (j >> 1), rr = 8 * (j & 1) + 4 * (l >> 5) + (l & 3);
+      const uint32_t w[4] = {G.w[j].x, G.w[j].y, G.w[j].z, G.w[j].w};
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            int q = 0;
-            if (amax != 0.0f) {
-              q = (int)roundf(__fdiv_rn(hv[ns][i], dq));
-              q = max(-127, min(127, q));
-            }
-            packed |= (uint32_t)(q & 0xff) << (8 * i);
-          }
-          qw[ns] = packed;
-        }
-        if (m < ntok) {
-          const int I = g.rows;
-          const int ch = n0 + 32 * wn;  // first channel of this wave's block
-          if (ch < I) {
-            int8_t *qrow = qh_out + (int64_t)outrow[m] * I + ch;
-            *reinterpret_cast<uint32_t *>(qrow + 4 * (lane >> 4)) = qw[0];
-            *reinterpret_cast<uint32_t *>(qrow + 16 + 4 * (lane >> 4)) = qw[1];
-            if ((lane >> 4) == 0) dh_out[(int64_t)outrow[m] * (I / 32) + ch / 32] = f32_to_f16_bits(dq);
-          }
-        }
-      }
-    } else if (MODE == kDown) {
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
-        const int m = 32 * wm + 16 * ms + (lane & 15);
-        if (m >= ntok) continue;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int n = n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4);
-          if (n < g.rows)
-            *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
-                make_float4(acc[a * 2 + ms][0], acc[a * 2 + ms][1], acc[a * 2 + ms][2],
-                            acc[a * 2 + ms][3]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t even = (w[i] << 4) & 0xf0f0f0f0u;  // k 0,2,4,6 (x16)
+        const uint32_t odd = w[i] & 0xf0f0f0f0u;          // k 1,3,5,7 (x16)
+        st.w[rt][s][b][(rr + 16 * i) ^ swz(s, b)] =
+            make_uint2(__builtin_amdgcn_perm(odd, even, 0x05010400u),
+                       __builtin_amdgcn_perm(odd, even, 0x07030602u));
       }
     }
+  }
+  {
+    const int s = (l >> 2) & 3, blk = (l >> 4) & 1, j0 = 2 * (l >> 5);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int mm = 4 * j + (l & 3);
+      st.a[wid][s][blk][(mm + 16 * j0) ^ swz(s, blk)] = make_uint2(G.a[j].x, G.a[j].y);
+      st.a[wid][s][blk][(mm + 16 * (j0 + 1)) ^ swz(s, blk)] = make_uint2(G.a[j].z, G.a[j].w);
+    }
+  }
+  if (MODE == kDots) return;
+  const int t = threadIdx.x;
+  const uint16_t h[4] = {(uint16_t)G.s.x, (uint16_t)(G.s.x >> 16), (uint16_t)G.s.y,
+                         (uint16_t)(G.s.y >> 16)};
+  if (wid < 2) {  // weight row t: the scales of steps 0..3
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) st.sw[s][t] = f16_to_f32(h[s]);
+  } else {  // token (t-128)/2: steps 2*(t&1) and 2*(t&1)+1, two blocks each
+    const int m = (t - BR) >> 1, s0 = 2 * (t & 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      st.sa[s0 + u][m] =
+          make_float2(f16_to_f32(h[2 * u]) * 0.0625f, f16_to_f32(h[2 * u + 1]) * 0.0625f);
+  }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
+             const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
+             int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
+             int8_t *__restrict__ qh_out, uint16_t *__restrict__ dh_out,
+             float *__restrict__ o_out, int32_t *__restrict__ dots_out) {
+  __shared__ Stage4 st;
+  __shared__ int rowid[BM];
+  __shared__ int outrow[BM];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wid >> 1, wm = wid & 1;
+  const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
+  const int items = ntiles * n_ntiles;
+  const int ngroups = g.K / (kGroup * BK);
+  const int G = gridDim.x;
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  for (int item = vid; item < items; item += G) {
+    const Item it = setup_item<MODE>(item, n_ntiles, tiles, fixed_ntok, fixed_expert, r, T, k,
+                                     rowid, outrow);
+    GemmArgs ge = g;
+    ge.wq = g.wq + (int64_t)it.expert * expert_stride_q;
+    ge.ws = g.ws + (int64_t)it.expert * expert_stride_s;
+
+    Src4 src;
+    {
+      const int t = threadIdx.x;
+      const uint16_t *unused;
+      src.wbase = ge.wq;
+      src.abase = ge.act;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t *q;
+        weight_row<MODE>(ge, it.n0, 32 * wid + 8 * j + 4 * (lane >> 5) + (lane & 3), q, unused);
+        src.w[j] = (uint32_t)(q - ge.wq) + 16 * ((lane >> 2) & 7);
+        const int m = 16 * wid + 4 * j + (lane & 3);
+        const int c = 4 * ((lane >> 2) & 3) + 2 * ((lane >> 4) & 1) + (lane >> 5);
+        src.a[j] = (uint32_t)rowid[m] * (uint32_t)ge.K + 16 * c;
+      }
+      if (MODE == kDots || wid < 2) {
+        const uint8_t *unused_q;
+        weight_row<MODE>(ge, it.n0, t & 127, unused_q, src.s);
+        src.s_group = kGroup;
+      } else {
+        src.s = ge.act_d + (int64_t)rowid[(t - BR) >> 1] * (ge.K / 32) + 4 * (t & 1);
+        src.s_group = 2 * kGroup;
+      }
+    }
+
+    float acc[8][4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[a][i] = 0.0f;
+    coli_i32x4 magic = {(int)kMagic, (int)kMagic, (int)kMagic, (int)kMagic};
+    // held in registers (not rebuilt from a constant before every MFMA)
+    asm volatile("" : "+v"(magic));
+
+    // The 8 (step, 32-block) blocks of a stage run as a software pipeline:
+    // while block q's epilogue runs on the vector ALUs, block q+1's MFMAs run
+    // on the matrix core and block q+2's operands are on their way from LDS.
+    // Each step's scales are read with the operands of its first block.
+    struct Ops {
+      uint2 a[4], b[2];
+    };
+    struct Scl {
+      float w[4][4];
+      float d[2][2];
+    };
+    auto load_ops = [&](int q, Ops &o) {
+      const int s = q >> 1, blk = q & 1;
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) o.b[ms] = st.a[2 * wm + ms][s][blk][lane ^ swz(s, blk)];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        o.a[a] = st.w[wave_row_tile<MODE>(wn, a)][s][blk][lane ^ swz(s, blk)];
+    };
+    auto load_scl = [&](int s, Scl &c) {
+      if (MODE == kDots) return;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float4 w4 = *reinterpret_cast<const float4 *>(
+            &st.sw[s][16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
+        c.w[a][0] = w4.x, c.w[a][1] = w4.y, c.w[a][2] = w4.z, c.w[a][3] = w4.w;
+      }
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const float2 d2 = st.sa[s][32 * wm + 16 * ms + (lane & 15)];
+        c.d[ms][0] = d2.x, c.d[ms][1] = d2.y;
+      }
+    };
+    auto mfmas = [&](const Ops &o, coli_i32x4 (&d)[8]) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) d[a * 2 + ms] = mfma_i8(o.a[a], o.b[ms], magic);
+    };
+    // block q of group gi: epilogue (or, for the block-dot export, the dots)
+    auto finish = [&](int gi, int q, const Scl &c, const coli_i32x4 (&d)[8]) {
+      const int blk = q & 1, ks = kGroup * gi + (q >> 1);
+      if (MODE == kDots) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms) {
+            const int m = 32 * wm + 16 * ms + (lane & 15);
+            if (m >= it.ntok) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int n = it.n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
+              if (n >= g.rows) continue;
+              dots_out[((int64_t)(it.row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks + blk] =
+                  (d[a * 2 + ms][i] - (int)kMagic) >> 4;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+          const float da = c.d[ms][blk], ca = -kMagicF * da;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[a * 2 + ms][i] = fmaf(c.w[a][i], fmaf(__int_as_float(d[a * 2 + ms][i]), da, ca),
+                                        acc[a * 2 + ms][i]);
+        }
+        // keep this block's epilogue here (see gemm_kernel)
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[a][i]));
+      }
+    };
+    auto compute_stage = [&](int gi) {
+      Ops o0, o1;
+      Scl c0, c1;
+      coli_i32x4 d0[8], d1[8];
+      load_scl(0, c0);
+      load_ops(0, o0);
+      load_ops(1, o1);
+      mfmas(o0, d0);
+#pragma unroll
+      for (int q = 0; q < 2 * kGroup; ++q) {
+        // block q's results are in d[q & 1], block q+1's operands in o[(q+1) & 1]
+        if (q + 1 < 2 * kGroup) mfmas((q & 1) ? o0 : o1, (q & 1) ? d0 : d1);
+        if (q + 2 < 2 * kGroup) load_ops(q + 2, (q & 1) ? o1 : o0);
+        if ((q & 1) == 0 && q + 2 < 2 * kGroup) load_scl((q >> 1) + 1, ((q >> 1) & 1) ? c0 : c1);
+        finish(gi, q, ((q >> 1) & 1) ? c1 : c0, (q & 1) ? d1 : d0);
+      }
+    };
+
+    Group4 grp;
+    load_group(src, 0, grp);
+    store_group<MODE>(grp, st, wid);
+    __syncthreads();
+    if (ngroups > 1) load_group(src, 1, grp);
+    for (int gi = 0; gi < ngroups; ++gi) {
+      compute_stage(gi);
+      if (gi + 1 < ngroups) {
+        __syncthreads();  // every wavefront is done with the stage
+        store_group<MODE>(grp, st, wid);
+        __syncthreads();
+        if (gi + 2 < ngroups) load_group(src, gi + 2, grp);
+      }
+    }
+    epilogue<MODE>(acc, g, it, outrow, wn, wm, lane, qh_out, dh_out, o_out);
   }
 }
 
@@ -584,9 +886,9 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.up_offset_q = (int64_t)L.I * L.H / 2;
     g.up_offset_s = (int64_t)L.I * L.H / 64;
     const int nn = (L.I + 63) / 64;
-    launch_k(COLI_K_GEMM_GATEUP, gemm_kernel<kGateUp>, dim3(grid_for((int64_t)mt * nn)),
-             dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes,
-             L.expert_scales, w.qh, w.dh, nullptr, nullptr);
+    launch_k(COLI_K_GEMM_GATEUP, L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp>,
+             dim3(grid_for((int64_t)mt * nn)), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
+             0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh, nullptr, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
   {  // down
@@ -598,9 +900,9 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.act = w.qh;
     g.act_d = w.dh;
     const int nn = (L.H + BR - 1) / BR;
-    launch_k(COLI_K_GEMM_DOWN, gemm_kernel<kDown>, dim3(grid_for((int64_t)mt * nn)),
-             dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes,
-             L.expert_scales, nullptr, nullptr, w.o, nullptr);
+    launch_k(COLI_K_GEMM_DOWN, L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown>,
+             dim3(grid_for((int64_t)mt * nn)), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
+             0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr, nullptr, w.o, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
   launch_combine(w.o, r, T, L.H, L.k, L.S, y, y_dtype, s);
@@ -620,7 +922,8 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
   const int nn = (g.rows + BR - 1) / BR;
   const int ntile = (T + BM - 1) / BM;
   coli_moe_route_t none{};
-  launch_k(COLI_K_BLOCK_DOTS, gemm_kernel<kDots>, dim3(grid_for((int64_t)ntile * nn)),
+  launch_k(COLI_K_BLOCK_DOTS, g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots>,
+           dim3(grid_for((int64_t)ntile * nn)),
            dim3(kThreads), 0, s, g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes,
            L.expert_scales, nullptr, nullptr, nullptr, dots);
   return hip_status(hipGetLastError());
