@@ -287,12 +287,27 @@ struct Item {
   int expert, row0, ntok, n0;
 };
 
+// Work items are ordered in bands of kBand consecutive token tiles: within a
+// band, the tiles at one block of output rows, then the next block.  Tiles of
+// one expert are consecutive, so the tiles that share a weight slice run at
+// about the same time and read it from L2, while a band's activations (at
+// most kBand x 64 rows) stay in L2 across its row blocks.
+constexpr int kBand = 4;
+COLI_DEV int band_items(int ntiles, int n_ntiles) {
+  return (ntiles + kBand - 1) / kBand * kBand * n_ntiles;
+}
+COLI_DEV void item_coords(int item, int n_ntiles, int &tile, int &ntile) {
+  const int per_band = kBand * n_ntiles;
+  const int band = item / per_band, rem = item - band * per_band;
+  ntile = rem / kBand;
+  tile = band * kBand + (rem - ntile * kBand);
+}
+
 template <int MODE>
-COLI_DEV Item setup_item(int item, int n_ntiles, const int4 *tiles, int fixed_ntok,
+COLI_DEV Item setup_item(int tile, int ntile, const int4 *tiles, int fixed_ntok,
                          int fixed_expert, const coli_moe_route_t &r, int T, int k,
                          int *rowid, int *outrow) {
   Item it;
-  const int tile = item / n_ntiles, ntile = item % n_ntiles;
   if (tiles) {
     const int4 td = tiles[tile];
     it.expert = td.x;
@@ -407,7 +422,7 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wid >> 1, wm = wid & 1;
   const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
-  const int items = ntiles * n_ntiles;
+  const int items = band_items(ntiles, n_ntiles);
   const int nsteps = g.K / BK;
   // K steps rounded up to the prefetch depth; the extra steps are padding
   const int nsteps_pad = (nsteps + kDepth - 1) / kDepth * kDepth;
@@ -416,7 +431,10 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
   const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   for (int item = vid; item < items; item += G) {
-    const Item it = setup_item<MODE>(item, n_ntiles, tiles, fixed_ntok, fixed_expert, r, T, k,
+    int tile, ntile;
+    item_coords(item, n_ntiles, tile, ntile);
+    if (tile >= ntiles) continue;  // past the last tile of the last band
+    const Item it = setup_item<MODE>(tile, ntile, tiles, fixed_ntok, fixed_expert, r, T, k,
                                      rowid, outrow);
     const int expert = it.expert, row0 = it.row0, ntok = it.ntok, n0 = it.n0;
     GemmArgs ge = g;
@@ -653,13 +671,16 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wid >> 1, wm = wid & 1;
   const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
-  const int items = ntiles * n_ntiles;
+  const int items = band_items(ntiles, n_ntiles);
   const int ngroups = g.K / (kGroup * BK);
   const int G = gridDim.x;
   const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   for (int item = vid; item < items; item += G) {
-    const Item it = setup_item<MODE>(item, n_ntiles, tiles, fixed_ntok, fixed_expert, r, T, k,
+    int tile, ntile;
+    item_coords(item, n_ntiles, tile, ntile);
+    if (tile >= ntiles) continue;  // past the last tile of the last band
+    const Item it = setup_item<MODE>(tile, ntile, tiles, fixed_ntok, fixed_expert, r, T, k,
                                      rowid, outrow);
     GemmArgs ge = g;
     ge.wq = g.wq + (int64_t)it.expert * expert_stride_q;
@@ -848,6 +869,10 @@ PrefillWs carve(const Layer &L, int T, void *base) {
 
 // grid size: one workgroup per item up to a cap, a multiple of 8 so the
 // XCD-aware remap of workgroup ids is a bijection
+int64_t band_items_host(int64_t ntiles, int64_t n_ntiles) {
+  return (ntiles + kBand - 1) / kBand * kBand * n_ntiles;
+}
+
 int grid_for(int64_t items) {
   const int64_t g = items < 16384 ? items : 16384;
   return (int)((g + 7) / 8 * 8);
@@ -887,7 +912,7 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.up_offset_s = (int64_t)L.I * L.H / 64;
     const int nn = (L.I + 63) / 64;
     launch_k(COLI_K_GEMM_GATEUP, L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp>,
-             dim3(grid_for((int64_t)mt * nn)), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
+             dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh, nullptr, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
@@ -901,7 +926,7 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.act_d = w.dh;
     const int nn = (L.H + BR - 1) / BR;
     launch_k(COLI_K_GEMM_DOWN, L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown>,
-             dim3(grid_for((int64_t)mt * nn)), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
+             dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr, nullptr, w.o, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
@@ -923,7 +948,7 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
   const int ntile = (T + BM - 1) / BM;
   coli_moe_route_t none{};
   launch_k(COLI_K_BLOCK_DOTS, g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots>,
-           dim3(grid_for((int64_t)ntile * nn)),
+           dim3(grid_for(band_items_host(ntile, nn))),
            dim3(kThreads), 0, s, g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes,
            L.expert_scales, nullptr, nullptr, nullptr, dots);
   return hip_status(hipGetLastError());
