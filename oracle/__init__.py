@@ -41,10 +41,11 @@ def _bind(path):
     lib.oracle_forward_prefill.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p, p]
     lib.oracle_quantize_q8_0.argtypes = [p, i64, p, p]
     lib.oracle_block_dots.argtypes = [i64, i64, i64, i64, p, p, i64, ctypes.c_int, p, i64, p]
+    lib.oracle_router_logits.argtypes = [i64, i64, i64, p, p, p]
     lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_f16.restype = ctypes.c_uint16
     for f in ("oracle_route", "oracle_forward_decode", "oracle_forward_prefill",
-              "oracle_quantize_q8_0", "oracle_block_dots"):
+              "oracle_quantize_q8_0", "oracle_block_dots", "oracle_router_logits"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -119,6 +120,21 @@ def route(logits, top_k: int, flags: int, routed_scale: float = 1.0, sel_bias=No
         raise ValueError("oracle_route: invalid arguments")
     out["topk_idx"] = out["topk_idx"].reshape(T, top_k)
     out["topk_w"] = out["topk_w"].reshape(T, top_k)
+    return out
+
+
+def router_logits(w_bf16, x_bf16):
+    """Router logits fp32 [T, E] = x [T, H] . w [E, H]^T (bf16 bit patterns in)."""
+    lib = _load()
+    w = _c(w_bf16, np.uint16)
+    x = _c(x_bf16, np.uint16)
+    E, H = w.shape
+    T = x.shape[0]
+    if x.shape[1] != H:
+        raise ValueError("router_logits: x and w disagree on H")
+    out = np.zeros((T, E), np.float32)
+    if lib.oracle_router_logits(T, E, H, _ptr(w), _ptr(x), _ptr(out)) != 0:
+        raise ValueError("oracle_router_logits: invalid arguments")
     return out
 
 

@@ -122,6 +122,28 @@ static const uint16_t *or_sc(const or_layer *L, int64_t e, int m) {
   return L->scales + e * (3 * L->I * L->H / 64) + (int64_t)m * (L->I * L->H / 64);
 }
 
+/* --------------------------------------------------------- router logits */
+
+/* Router logits of T tokens: logit[t][e] = sum over k < H of x[t][k] *
+ * w[e][k], with bf16 inputs (exact in fp64), the sum in fp64 in k order,
+ * rounded once to fp32.  The router decides which experts a token loads and
+ * runs ahead of the expert loads (aixq.cc article, sections "为什么值得关注"
+ * and "我的真实看法"); the pages give no formula, so it is read as a dense
+ * linear layer without bias over the layer input, with bf16 weights stored
+ * row-major [E][H]. */
+int oracle_router_logits(int64_t T, int64_t E, int64_t H, const uint16_t *w,
+                         const uint16_t *x, float *logits) {
+  if (T < 1 || E < 1 || H < 1 || !w || !x || !logits) return OR_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k]) * or_bf16(w[e * H + k]);
+      logits[t * E + e] = (float)acc;
+    }
+  return OR_OK;
+}
+
 /* ------------------------------------------------------------------ route */
 
 /* Top-k selection, weights and grouping for T tokens.

@@ -17,7 +17,8 @@ CHECKS = [
     pins.check_decode_vs_bruteforce, pins.check_decode_mean_invariant,
     pins.check_decode_zero_scales, pins.check_decode_swiglu_mlp, pins.check_decode_closed_form,
     pins.check_block_dots_vs_bruteforce, pins.check_prefill_vs_bruteforce,
-    pins.check_prefill_zero_scales,
+    pins.check_prefill_zero_scales, pins.check_router_logits_closed_form,
+    pins.check_router_logits_vs_bruteforce,
 ]
 
 # (name, text in the oracle, replacement)
@@ -58,6 +59,13 @@ MUTANTS = [
     ("prefill h not requantised", "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *",
      "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[0]) *"),
     ("f16 rounding truncates", "double m = nearbyint(ldexp(a, 10 - E));", "double m = floor(ldexp(a, 10 - E));"),
+    ("router weight transposed", "acc += or_bf16(x[t * H + k]) * or_bf16(w[e * H + k]);",
+     "acc += or_bf16(x[t * H + k]) * or_bf16(w[k * E + e]);"),
+    ("router drops the last column", "for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])",
+     "for (int64_t k = 0; k < H - 1; ++k) acc += or_bf16(x[t * H + k])"),
+    ("router accumulates in fp32",
+     "double acc = 0.0;\n      for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])",
+     "float acc = 0.0f;\n      for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])"),
 ]
 
 

@@ -363,6 +363,49 @@ def test_prefill_zero_scales():
     check_prefill_zero_scales()
 
 
+# ----------------------------------------------------------- router logits
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+
+
+def check_router_logits_closed_form():
+    """Integer inputs make every partial sum exact: the logits are the exact
+    integer matrix product.  A one-hot activation selects a weight column."""
+    rng = np.random.default_rng(21)
+    T, E, H = 4, 7, 160
+    xi = rng.integers(-8, 9, size=(T, H))
+    wi = rng.integers(-8, 9, size=(E, H))
+    lg = oracle.router_logits(synth.bf16_bits(_bf16(wi)), synth.bf16_bits(_bf16(xi)))
+    assert np.array_equal(lg, (xi @ wi.T).astype(np.float32))
+    onehot = np.zeros((1, H), np.float32)
+    onehot[0, 37] = 1.0
+    w = rng.standard_normal((E, H)).astype(np.float32)
+    wb = _bf16(w)
+    lg1 = oracle.router_logits(synth.bf16_bits(wb), synth.bf16_bits(_bf16(onehot)))
+    assert np.array_equal(lg1[0], wb.float().numpy()[:, 37])
+
+
+def check_router_logits_vs_bruteforce():
+    """Random bf16 inputs against a dense fp64 product (summation order may
+    differ, so the fp32 results agree to one unit in the last place)."""
+    rng = np.random.default_rng(22)
+    T, E, H = 5, 12, 192
+    xb = _bf16(rng.standard_normal((T, H)))
+    wb = _bf16(rng.standard_normal((E, H)) * 0.05)
+    lg = oracle.router_logits(synth.bf16_bits(wb), synth.bf16_bits(xb))
+    ref = (xb.double().numpy() @ wb.double().numpy().T).astype(np.float32)
+    assert np.all(np.abs(lg - ref) <= np.spacing(np.abs(ref)))
+
+
+def test_router_logits_closed_form():
+    check_router_logits_closed_form()
+
+
+def test_router_logits_vs_bruteforce():
+    check_router_logits_vs_bruteforce()
+
+
 # ------------------------------------------------------- container identity
 
 def test_container_sizes_match_the_pages():
