@@ -155,6 +155,25 @@ int coli_moe_route(const coli_moe_layer_t *layer, const float *logits,
                    const coli_moe_route_t *route, void *ws, size_t ws_bytes,
                    void *stream);
 
+/* Route T tokens from the layer input: router logits, then exactly what
+ * coli_moe_route does with them.
+ *   logits[t][e] = sum over k < H of x[t][k] * w_router[e][k]
+ *  w_router [E*H] bf16 row-major (no bias);  x [T*H] bf16;  both 16-byte
+ *           aligned.
+ *  logits   [T*E] fp32, written (device memory owned by the caller).
+ *  sel_bias, T, route, ws: as for coli_moe_route.
+ * The products are exact in fp32 and summed in fp32 in one fixed order per
+ * (token, expert) -- lane chunks of 8 values, 64 chunks per 512-value tile,
+ * tiles in order, then a fixed butterfly -- whatever T is, so a token's
+ * logits and its expert choice do not depend on the rest of the batch.
+ * Source: aixq.cc article, sections "为什么值得关注" and "我的真实看法" (the
+ * router picks the experts and runs ahead of their loads); the pages give
+ * no formula, so the router is read as a dense linear layer without bias. */
+int coli_moe_route_hidden(const coli_moe_layer_t *layer, const uint16_t *w_router,
+                          const uint16_t *x, const float *sel_bias, int32_t T,
+                          float *logits, const coli_moe_route_t *route, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* Decode-shaped forward, T in [1, 64] tokens (single-token decode and
  * multi-token verify); needs I <= 15360 (COLI_E_UNSUPPORTED otherwise).  Activations stay bf16 -> fp32; weights are
  * dequantised in registers (w = q*s exactly); products are accumulated in
@@ -222,7 +241,8 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert,
 enum {
   COLI_K_ROUTE_FUSED = 0, COLI_K_TOPK = 1, COLI_K_GROUP = 2, COLI_K_DECODE_GATEUP = 3,
   COLI_K_DECODE_DOWN = 4, COLI_K_COMBINE = 5, COLI_K_QUANTIZE = 6, COLI_K_PLAN = 7,
-  COLI_K_GEMM_GATEUP = 8, COLI_K_GEMM_DOWN = 9, COLI_K_BLOCK_DOTS = 10, COLI_K_COUNT = 11
+  COLI_K_GEMM_GATEUP = 8, COLI_K_GEMM_DOWN = 9, COLI_K_BLOCK_DOTS = 10,
+  COLI_K_ROUTER_LOGITS = 11, COLI_K_COUNT = 12
 };
 typedef struct coli_moe_trace {
   void **start;     /* hipEvent_t[capacity] */

@@ -40,7 +40,8 @@ class _TraceC(ctypes.Structure):
 
 
 KERNEL_NAMES = ["route_fused", "route_topk", "route_group", "decode_gateup", "decode_down",
-                "combine", "quantize_q8_0", "plan", "gemm_gateup", "gemm_down", "block_dots"]
+                "combine", "quantize_q8_0", "plan", "gemm_gateup", "gemm_down", "block_dots",
+                "router_logits"]
 
 
 class _RouteC(ctypes.Structure):
@@ -68,6 +69,8 @@ def _load():
         lib.coli_moe_workspace_bytes.argtypes = [P(_LayerC), i32, i32]
         lib.coli_moe_workspace_bytes.restype = sz
         lib.coli_moe_route.argtypes = [P(_LayerC), vp, vp, i32, P(_RouteC), vp, sz, vp]
+        lib.coli_moe_route_hidden.argtypes = [P(_LayerC), vp, vp, vp, i32, vp, P(_RouteC), vp,
+                                              sz, vp]
         lib.coli_moe_forward_decode.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
         lib.coli_moe_forward_prefill.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
         lib.coli_moe_quantize_q8_0.argtypes = [vp, i32, i64, vp, vp, vp]
@@ -78,8 +81,8 @@ def _load():
         lib.coli_moe_set_trace.restype = ctypes.c_int
         lib.coli_moe_version.argtypes = []
         lib.coli_moe_version.restype = ctypes.c_char_p
-        for f in ("coli_moe_route", "coli_moe_forward_decode", "coli_moe_forward_prefill",
-                  "coli_moe_quantize_q8_0", "coli_moe_block_dots"):
+        for f in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
+                  "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -170,6 +173,14 @@ def coli_moe_route(layer: Layer, logits, sel_bias, T: int, route: Route, ws=None
     _check("coli_moe_route", _load().coli_moe_route(
         ctypes.byref(layer.c), _ptr(logits), _ptr(sel_bias), T, ctypes.byref(route.c),
         _ptr(ws), nb, _stream(stream)))
+
+
+def coli_moe_route_hidden(layer: Layer, w_router, x, sel_bias, T: int, logits, route: Route,
+                          ws=None, stream=None):
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("coli_moe_route_hidden", _load().coli_moe_route_hidden(
+        ctypes.byref(layer.c), _ptr(w_router), _ptr(x), _ptr(sel_bias), T, _ptr(logits),
+        ctypes.byref(route.c), _ptr(ws), nb, _stream(stream)))
 
 
 def coli_moe_forward_decode(layer: Layer, route: Route, x, T: int, y, y_dtype: int, ws,

@@ -129,6 +129,26 @@ int coli_moe_route(const coli_moe_layer_t *layer, const float *logits, const flo
   return launch_route(L, logits, sel_bias, T, *route, reinterpret_cast<hipStream_t>(stream));
 }
 
+int coli_moe_route_hidden(const coli_moe_layer_t *layer, const uint16_t *w_router,
+                          const uint16_t *x, const float *sel_bias, int32_t T, float *logits,
+                          const coli_moe_route_t *route, void *ws, size_t ws_bytes,
+                          void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if ((rc = check_route(route))) return rc;
+  if ((rc = check_tokens(L, T, kMaxT))) return rc;
+  if (!w_router || !x || !logits) return COLI_E_INVALID;
+  if (!aligned(w_router, 16) || !aligned(x, 16) || !aligned(logits, 4) ||
+      (sel_bias && !aligned(sel_bias, 4)))
+    return COLI_E_ALIGN;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((rc = launch_router_logits(L, w_router, x, T, logits, s))) return rc;
+  return launch_route(L, logits, sel_bias, T, *route, s);
+}
+
 int coli_moe_forward_decode(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
                             const uint16_t *x, int32_t T, void *y, int32_t y_dtype, void *ws,
                             size_t ws_bytes, void *stream) {

@@ -43,6 +43,9 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
                   void *y, int y_dtype, void *ws, hipStream_t s);
 int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                    void *y, int y_dtype, void *ws, hipStream_t s);
+// Router logits x . W_r^T (router.hip).
+int launch_router_logits(const Layer &L, const uint16_t *w, const uint16_t *x, int T,
+                         float *logits, hipStream_t s);
 // Streaming gate/up + down GEMVs for decode batches of up to kMaxStreamT
 // tokens (decode_stream.hip); false if the shape has no streaming path.
 constexpr int kMaxStreamT = 16;

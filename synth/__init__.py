@@ -34,7 +34,7 @@ ZIPF_S = 1.1
 # seed 0 it gives per-expert token counts of roughly 20 to 400.
 ZIPF_ALPHA = 0.21
 
-_KIND = {"q4": 1, "scales": 2, "logits": 3, "x": 4, "rank": 5, "bias": 6}
+_KIND = {"q4": 1, "scales": 2, "logits": 3, "x": 4, "rank": 5, "bias": 6, "router": 7}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -153,6 +153,16 @@ def make_x(spec: LayerSpec, T: int, seed: int = 0, layer: int = 0, device="cpu",
     g = _gen(device, seed, layer, "x", extra=step * 7919 + T)
     return torch.randn(T, spec.hidden, generator=g, device=device,
                        dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_router_weights(spec: LayerSpec, seed: int = 0, layer: int = 0, device="cpu"
+                        ) -> torch.Tensor:
+    """Router weights bf16 [E, H], N(0, 1/H): with N(0, 1) activations the
+    logits come out about N(0, 1)."""
+    g = _gen(device, seed, layer, "router")
+    w = torch.randn(spec.n_experts, spec.hidden, generator=g, device=device,
+                    dtype=torch.float32)
+    return (w * spec.hidden ** -0.5).to(torch.bfloat16)
 
 
 def make_sel_bias(spec: LayerSpec, seed: int = 0, layer: int = 0) -> torch.Tensor:

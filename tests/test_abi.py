@@ -24,9 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("coli_moe_route", "coli_moe_forward_decode", "coli_moe_forward_prefill",
-              "coli_moe_workspace_bytes", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
-              "coli_moe_strerror", "coli_moe_version"):
+    for n in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
+              "coli_moe_forward_prefill", "coli_moe_workspace_bytes", "coli_moe_quantize_q8_0",
+              "coli_moe_block_dots", "coli_moe_strerror", "coli_moe_version"):
         assert n in names
 
 
@@ -117,6 +117,25 @@ def test_route_quantize_dots_reject_bad_calls():
     assert bd(ctypes.byref(L.c), 257, 0, FAKE, 4, FAKE, None) == -1   # expert out of range
     assert bd(ctypes.byref(L.c), 0, 3, FAKE, 4, FAKE, None) == -1     # matrix out of range
     assert bd(ctypes.byref(L.c), 0, 0, FAKE, 0, FAKE, None) == -1     # T = 0
+
+
+def test_route_hidden_rejects_bad_calls():
+    L = _layer()
+    lib = binding.raw_library()
+    r = ctypes.byref(_FakeRoute().c)
+    rh = lib.coli_moe_route_hidden
+    Lc = ctypes.byref(L.c)
+    assert rh(None, FAKE, FAKE, None, 4, FAKE, r, None, 0, None) == -1
+    assert rh(Lc, 0, FAKE, None, 4, FAKE, r, None, 0, None) == -1          # weights NULL
+    assert rh(Lc, FAKE, 0, None, 4, FAKE, r, None, 0, None) == -1          # x NULL
+    assert rh(Lc, FAKE, FAKE, None, 4, 0, r, None, 0, None) == -1          # logits NULL
+    assert rh(Lc, FAKE, FAKE, None, 0, FAKE, r, None, 0, None) == -1       # T = 0
+    assert rh(Lc, FAKE, FAKE, None, 65537, FAKE, r, None, 0, None) == -1   # T too big
+    assert rh(Lc, FAKE + 8, FAKE, None, 4, FAKE, r, None, 0, None) == -4   # weights align
+    assert rh(Lc, FAKE, FAKE + 2, None, 4, FAKE, r, None, 0, None) == -4   # x align
+    assert rh(Lc, FAKE, FAKE, FAKE + 1, 4, FAKE, r, None, 0, None) == -4   # bias align
+    assert rh(Lc, FAKE, FAKE, None, 4, FAKE,
+              ctypes.byref(_FakeRoute(null=True).c), None, 0, None) == -1  # route buffers
 
 
 def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
