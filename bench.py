@@ -39,6 +39,9 @@ if _ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak (POP/s -> TOPS)
+# fp32 vector peak; a bf16 dot2 (two products and two adds per lane) issues
+# at the same rate as a packed fp32 FMA, so it is the dot2 router's ALU peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "MoE-layer tokens/s + int4 weight GB/s (decode) / int8 TOPS (prefill)"
 
 
@@ -319,6 +322,50 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
     return out
 
 
+def secondary_router(name, spec, T, steps, warmup):
+    """Router logits + routing from the layer input (coli_moe_route_hidden)."""
+    import torch
+
+    import int4_routed_expert_router_amd as coli
+    import synth
+
+    small = synth.LayerSpec(spec.hidden, 64, spec.n_experts, spec.n_shared, spec.top_k,
+                            spec.sigmoid, spec.renorm, spec.routed_scale)
+    q4, sc = synth.make_weights(small, seed=0, device="cuda", experts=1)
+    L = coli.Layer(spec.hidden, 64, spec.n_experts, spec.n_shared, spec.top_k, spec.flags, q4,
+                   sc, spec.routed_scale)
+    copies = 8  # rotate router weights so repeated calls do not hit in cache
+    ws = [synth.make_router_weights(spec, seed=0, layer=c, device="cuda") for c in range(copies)]
+    x = synth.make_x(spec, T, seed=0).cuda()
+    r = coli.Route(L, T)
+    logits = torch.empty(T, spec.n_experts, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        coli.coli_moe_route_hidden(L, ws[i % copies], x, None, T, logits, r)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kern = traced_kernels(lambda: step(1), reps=max(4, steps // 4))
+    us = kern["router_logits"]["avg_us"]
+    wbytes = spec.n_experts * spec.hidden * 2
+    flops = 2.0 * T * spec.n_experts * spec.hidden
+    return {"workload": name, "path": "router", "tokens": T, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "router_logits_us": round(us, 3),
+            "router_weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+            "router_TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+            "alu_frac": round(flops / (us * 1e-6) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +450,8 @@ def main():
                                            10, 2, layer=stack.layers[0]))
         del stack
         torch.cuda.empty_cache()
+        secondary.append(secondary_router("glm_router_T1", w.spec, 1, 200, 10))
+        secondary.append(secondary_router("glm_router_T2048", w.spec, 2048, 20, 3))
         ow = synth.WORKLOADS["olmoe"]
         secondary.append(secondary_decode("olmoe_decode_T1", ow.spec, 1, 0.0, 4, 200, 10))
         secondary.append(secondary_prefill("olmoe_prefill_T512", ow.spec, 512, 0.0, 20, 3, copies=4))

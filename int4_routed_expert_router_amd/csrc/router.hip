@@ -6,16 +6,17 @@
 // layer without bias, bf16 weights [E][H] and bf16 activations [T][H], with
 // fp32 accumulation and fp32 logits.
 //
-// One kernel serves every batch size with the same arithmetic per (token,
-// expert), so a token's logits -- and hence its expert choice -- do not
-// depend on the rest of the batch:
+// Every batch size gets the same arithmetic per (token, expert), so a
+// token's logits -- and hence its expert choice -- do not depend on the rest
+// of the batch:
 //  - K is cut into tiles of 512 values; lane L of a wavefront owns the
 //    8-value chunk L of every tile (chunk index 64 * tile + L), and adds it
 //    to its running sum as four bf16 dot2 steps, tile after tile;
 //  - the 64 lane sums are then added by one fixed butterfly (xor 32 .. 1).
-// Only the grouping of the work changes with T: a wavefront computes EPW
-// experts x TT tokens (TT tokens per workgroup, staged per tile in LDS,
-// double-buffered), with the next tile's weights already in flight.
+// Only the grouping of the work changes with T: in router_kernel a
+// wavefront computes EPW experts x TT tokens (TT tokens per workgroup, staged
+// per tile in LDS, double-buffered), with the next tile's weights already in
+// flight; router_one_kernel (up to 16 tokens) loads everything at once.
 #include "device_common.h"
 #include "internal.h"
 
@@ -108,6 +109,40 @@ __global__ void __launch_bounds__(kThreads) router_kernel(const uint16_t *__rest
     }
 }
 
+// Small batches: no staging.  Each wavefront (one expert, one token: token
+// blockIdx.y) requests all of its lane's weight and activation chunks at
+// once -- NT tiles, one 16-byte chunk of each per lane -- then adds them in
+// the same order as router_kernel.  The router weights are read once per
+// token, mostly from L2.
+template <int NT>
+__global__ void __launch_bounds__(kThreads) router_one_kernel(const uint16_t *__restrict__ w,
+                                                              const uint16_t *__restrict__ x,
+                                                              int E, int H,
+                                                              float *__restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int e = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (e >= E) return;
+  const int nch = H >> 3;
+  x += (int64_t)blockIdx.y * H;
+  logits += (int64_t)blockIdx.y * E;
+  uint4 wq[NT], xq[NT];
+#pragma unroll
+  for (int tile = 0; tile < NT; ++tile) {
+    const int c = 64 * tile + lane;
+    const bool ok = c < nch;
+    wq[tile] = ok ? *reinterpret_cast<const uint4 *>(w + (int64_t)e * H + 8 * c)
+                  : make_uint4(0, 0, 0, 0);
+    xq[tile] = ok ? *reinterpret_cast<const uint4 *>(x + 8 * c) : make_uint4(0, 0, 0, 0);
+  }
+  float v = 0.0f;
+#pragma unroll
+  for (int tile = 0; tile < NT; ++tile)
+    if (64 * tile + lane < nch) v = chunk8_dot(wq[tile], xq[tile], v);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) logits[e] = v;
+}
+
 template <int EPW, int TT>
 void launch_cfg(const uint16_t *w, const uint16_t *x, int T, int E, int H, float *logits,
                 hipStream_t s) {
@@ -120,9 +155,26 @@ void launch_cfg(const uint16_t *w, const uint16_t *x, int T, int E, int H, float
 
 int launch_router_logits(const Layer &L, const uint16_t *w, const uint16_t *x, int T,
                          float *logits, hipStream_t s) {
-  // decode / verify batches: one expert per wavefront, the whole batch per
-  // workgroup; larger batches: 4 experts x 16 tokens per wavefront
-  if (T <= 1) launch_cfg<1, 1>(w, x, T, L.E, L.H, logits, s);
+  // up to 16 tokens (H <= 8192): one wavefront per (expert, token), all
+  // loads at once; otherwise staged tiles -- one expert per wavefront and the
+  // whole batch per workgroup up to 16 tokens, else 4 experts x 16 tokens
+  // per wavefront
+  const int ntiles = (L.H / 8 + 63) / 64;
+  if (T <= 16 && ntiles <= 16) {
+    const dim3 grid((L.E + 3) / 4, T);
+    if (ntiles <= 4)
+      launch_k(COLI_K_ROUTER_LOGITS, router_one_kernel<4>, grid, dim3(kThreads), 0, s, w, x,
+               L.E, L.H, logits);
+    else if (ntiles <= 8)
+      launch_k(COLI_K_ROUTER_LOGITS, router_one_kernel<8>, grid, dim3(kThreads), 0, s, w, x,
+               L.E, L.H, logits);
+    else if (ntiles <= 12)
+      launch_k(COLI_K_ROUTER_LOGITS, router_one_kernel<12>, grid, dim3(kThreads), 0, s, w, x,
+               L.E, L.H, logits);
+    else
+      launch_k(COLI_K_ROUTER_LOGITS, router_one_kernel<16>, grid, dim3(kThreads), 0, s, w, x,
+               L.E, L.H, logits);
+  } else if (T <= 1) launch_cfg<1, 1>(w, x, T, L.E, L.H, logits, s);
   else if (T <= 2) launch_cfg<1, 2>(w, x, T, L.E, L.H, logits, s);
   else if (T <= 4) launch_cfg<1, 4>(w, x, T, L.E, L.H, logits, s);
   else if (T <= 8) launch_cfg<1, 8>(w, x, T, L.E, L.H, logits, s);
