@@ -42,10 +42,12 @@ def _bind(path):
     lib.oracle_quantize_q8_0.argtypes = [p, i64, p, p]
     lib.oracle_block_dots.argtypes = [i64, i64, i64, i64, p, p, i64, ctypes.c_int, p, i64, p]
     lib.oracle_router_logits.argtypes = [i64, i64, i64, p, p, p]
+    lib.oracle_quantize_int4_gs64.argtypes = [p, i64, i64, p, p]
     lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_f16.restype = ctypes.c_uint16
     for f in ("oracle_route", "oracle_forward_decode", "oracle_forward_prefill",
-              "oracle_quantize_q8_0", "oracle_block_dots", "oracle_router_logits"):
+              "oracle_quantize_q8_0", "oracle_block_dots", "oracle_router_logits",
+              "oracle_quantize_int4_gs64"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -121,6 +123,19 @@ def route(logits, top_k: int, flags: int, routed_scale: float = 1.0, sel_bias=No
     out["topk_idx"] = out["topk_idx"].reshape(T, top_k)
     out["topk_w"] = out["topk_w"].reshape(T, top_k)
     return out
+
+
+def quantize_int4_gs64(w):
+    """int4 gs64 container of fp32 weights [rows, K] -> (uint8 [rows, K/2],
+    uint16 fp16-bits [rows, K/64])."""
+    lib = _load()
+    w = _c(w, np.float32)
+    rows, K = w.shape
+    q4 = np.zeros((rows, K // 2), np.uint8)
+    sc = np.zeros((rows, K // 64), np.uint16)
+    if lib.oracle_quantize_int4_gs64(_ptr(w), rows, K, _ptr(q4), _ptr(sc)) != 0:
+        raise ValueError("oracle_quantize_int4_gs64: invalid arguments")
+    return q4, sc
 
 
 def router_logits(w_bf16, x_bf16):

@@ -326,6 +326,47 @@ int oracle_quantize_q8_0(const float *v, int64_t n, int8_t *q, uint16_t *d16) {
   return OR_OK;
 }
 
+/* int4 gs64 container from float weights: rows x K values (K % 64 == 0),
+ * row-major.  Per group of 64 consecutive weights of a row: a = max |w|;
+ * s = a / 7 (IEEE fp32 division), stored as fp16 (nearest, ties to even);
+ * each weight becomes q = round-half-away-from-zero(w / s16) with the
+ * stored scale s16 (fp32 division), clamped to [-8, 7]; a group whose
+ * stored scale is 0 gives q = 0.  Nibbles are packed two's complement, the
+ * even k in the low nibble.  The pages fix the container -- int4, one fp16
+ * scale per 64 weights, symmetric (tantan.ink post, section "我看到的几个坑")
+ * -- but not the quantiser; this rule (the largest magnitude maps to 7,
+ * quantised against the scale the decoder will use) is the reading taken.
+ * Inputs must be finite with max |w| <= 7 * 65504. */
+int oracle_quantize_int4_gs64(const float *w, int64_t rows, int64_t K, uint8_t *q4,
+                              uint16_t *scales) {
+  if (rows < 0 || K <= 0 || K % 64) return OR_EINVAL;
+  for (int64_t n = 0; n < rows; ++n)
+    for (int64_t g = 0; g < K / 64; ++g) {
+      const float *wg = w + n * K + 64 * g;
+      float a = 0.0f;
+      for (int i = 0; i < 64; ++i)
+        if (fabsf(wg[i]) > a) a = fabsf(wg[i]);
+      volatile float s = a / 7.0f;
+      const uint16_t s16 = oracle_f32_to_f16(s);
+      scales[n * (K / 64) + g] = s16;
+      const float sf = (float)or_f16(s16);
+      for (int i = 0; i < 64; ++i) {
+        int r = 0;
+        if (sf != 0.0f) {
+          volatile float u = wg[i] / sf;
+          r = (int)roundf(u); /* halfway cases away from zero */
+          if (r > 7) r = 7;
+          if (r < -8) r = -8;
+        }
+        const int64_t k = 64 * g + i;
+        uint8_t *byte = q4 + n * (K / 2) + k / 2;
+        const uint8_t nib = (uint8_t)(r & 15);
+        *byte = (k & 1) ? (uint8_t)((*byte & 0x0f) | (nib << 4)) : (uint8_t)((*byte & 0xf0) | nib);
+      }
+    }
+  return OR_OK;
+}
+
 /* Exact int32 dot of one 32-block: weights of row n (nibble matrix with
  * K/2 bytes per row) against int8 activations a[K], over k in [32b, 32b+32). */
 static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n,

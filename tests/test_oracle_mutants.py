@@ -18,7 +18,8 @@ CHECKS = [
     pins.check_decode_zero_scales, pins.check_decode_swiglu_mlp, pins.check_decode_closed_form,
     pins.check_block_dots_vs_bruteforce, pins.check_prefill_vs_bruteforce,
     pins.check_prefill_zero_scales, pins.check_router_logits_closed_form,
-    pins.check_router_logits_vs_bruteforce,
+    pins.check_router_logits_vs_bruteforce, pins.check_int4_quant_vs_bruteforce,
+    pins.check_int4_quant_closed_form, pins.check_int4_quant_properties,
 ]
 
 # (name, text in the oracle, replacement)
@@ -59,6 +60,15 @@ MUTANTS = [
     ("prefill h not requantised", "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *",
      "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[0]) *"),
     ("f16 rounding truncates", "double m = nearbyint(ldexp(a, 10 - E));", "double m = floor(ldexp(a, 10 - E));"),
+    ("int4 scale from max / 8", "volatile float s = a / 7.0f;", "volatile float s = a / 8.0f;"),
+    ("int4 quantised with the fp32 scale", "const float sf = (float)or_f16(s16);",
+     "const float sf = s;"),
+    ("int4 rounds half to even",
+     "r = (int)roundf(u);", "r = (int)nearbyintf(u);"),
+    ("int4 clamps at -7", "if (r < -8) r = -8;", "if (r < -7) r = -7;"),
+    ("int4 nibbles packed high first",
+     "*byte = (k & 1) ? (uint8_t)((*byte & 0x0f) | (nib << 4)) : (uint8_t)((*byte & 0xf0) | nib);",
+     "*byte = (k & 1) ? (uint8_t)((*byte & 0xf0) | nib) : (uint8_t)((*byte & 0x0f) | (nib << 4));"),
     ("router weight transposed", "acc += or_bf16(x[t * H + k]) * or_bf16(w[e * H + k]);",
      "acc += or_bf16(x[t * H + k]) * or_bf16(w[k * E + e]);"),
     ("router drops the last column", "for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])",

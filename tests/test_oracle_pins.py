@@ -406,6 +406,97 @@ def test_router_logits_vs_bruteforce():
     check_router_logits_vs_bruteforce()
 
 
+# ------------------------------------------------------- int4 quantiser
+
+def _int4_bruteforce(w):
+    """Independent numpy statement of the container quantiser."""
+    w = np.asarray(w, np.float32)
+    rows, K = w.shape
+    g = w.reshape(rows, K // 64, 64)
+    a = np.max(np.abs(g), axis=2)
+    s16 = (a / np.float32(7.0)).astype(np.float16)          # fp32 division, RNE to fp16
+    sf = s16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (g / sf[:, :, None]).astype(np.float64)      # fp32 division, exact widen
+    r = np.sign(ratio) * np.floor(np.abs(ratio) + 0.5)        # half away from zero
+    r = np.where(sf[:, :, None] == 0, 0, np.clip(r, -8, 7)).astype(np.int64).reshape(rows, K)
+    nib = (r & 15).astype(np.uint8)
+    q4 = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return q4, s16.view(np.uint16)
+
+
+def _int4_cases():
+    rng = np.random.default_rng(31)
+    w = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.0                                    # all-zero group
+    w[1, 64:128] = -np.abs(w[1, 64:128])               # negative-only group
+    w[2, :64] = np.round(rng.standard_normal(64) * 4) / 8  # exact halves after scaling
+    w[3, :64] = rng.uniform(-5e-7, 5e-7, 64)           # subnormal fp16 scales
+    w[3, 0] = -5e-7                                    # negative max: the scale rounds down,
+    w[3, 64:128] = rng.uniform(-3e-7, 3e-7, 64)        # so this group reaches -8
+    w[4] = rng.uniform(-400000, 400000, 256)           # near the largest valid scale
+    return w
+
+
+def check_int4_quant_vs_bruteforce():
+    w = _int4_cases()
+    q4, sc = oracle.quantize_int4_gs64(w)
+    bq, bs = _int4_bruteforce(w)
+    assert np.any(q4[3] & 15 == 8) or np.any(q4[3] >> 4 == 8)   # the case reaches -8
+    assert np.array_equal(sc, bs)
+    assert np.array_equal(q4, bq)
+
+
+def check_int4_quant_closed_form():
+    """w = q * 2^-6 with max |q| = 7 in every group gives back q and 2^-6."""
+    rng = np.random.default_rng(32)
+    q = rng.integers(-7, 8, size=(4, 128))
+    q[:, 0] = 7
+    q[:, 64] = -7
+    w = (q * 2.0 ** -6).astype(np.float32)
+    q4, sc = oracle.quantize_int4_gs64(w)
+    assert np.all(sc == 0x2400)                      # fp16 bits of 2^-6
+    nib = (q & 15).astype(np.uint8)
+    assert np.array_equal(q4, nib[:, 0::2] | (nib[:, 1::2] << 4))
+    # exact halves (scale 2^-6 again) round away from zero
+    h = np.concatenate([[7.0], np.arange(-6.5, 7.0, 1.0), np.full(49, 0.5)])
+    q4, sc = oracle.quantize_int4_gs64((h * 2.0 ** -6).astype(np.float32)[None, :])
+    qh = np.sign(h) * np.floor(np.abs(h) + 0.5)
+    nib = (qh.astype(np.int64) & 15).astype(np.uint8)
+    assert sc[0, 0] == 0x2400
+    assert np.array_equal(q4[0], nib[0::2] | (nib[1::2] << 4))
+    z4, zs = oracle.quantize_int4_gs64(np.zeros((2, 64), np.float32))
+    assert np.all(z4 == 0) and np.all(zs == 0)
+
+
+def check_int4_quant_properties():
+    rng = np.random.default_rng(33)
+    w = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    q4, sc = oracle.quantize_int4_gs64(w)
+    lo = (q4 & 15).astype(np.int64)
+    hi = (q4 >> 4).astype(np.int64)
+    q = np.empty((16, 512), np.int64)
+    q[:, 0::2], q[:, 1::2] = lo, hi
+    q = np.where(q >= 8, q - 16, q)
+    sf = sc.view(np.float16).astype(np.float64).repeat(64, axis=1)
+    assert np.all(np.abs(w - q * sf) <= sf / 2 * (1 + 1e-6))
+    g = np.abs(w).reshape(16, 8, 64).argmax(axis=2)
+    qg = q.reshape(16, 8, 64)
+    assert np.all(np.abs(np.take_along_axis(qg, g[:, :, None], 2)) == 7)
+
+
+def test_int4_quant_vs_bruteforce():
+    check_int4_quant_vs_bruteforce()
+
+
+def test_int4_quant_closed_form():
+    check_int4_quant_closed_form()
+
+
+def test_int4_quant_properties():
+    check_int4_quant_properties()
+
+
 # ------------------------------------------------------- container identity
 
 def test_container_sizes_match_the_pages():
