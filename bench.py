@@ -366,6 +366,47 @@ def secondary_router(name, spec, T, steps, warmup):
             "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
 
 
+def secondary_convert(name, spec, experts, src, steps, warmup):
+    """Float weights -> int4 gs64 container (coli_moe_quantize_int4_gs64) for
+    `experts` experts of the spec's shape stored back to back, in one call."""
+    import torch
+
+    import int4_routed_expert_router_amd as coli
+    import synth
+
+    dtype, code = {"bf16": (torch.bfloat16, coli.COLI_SRC_BF16),
+                   "f32": (torch.float32, coli.COLI_SRC_F32)}[src]
+    n = experts * 3 * spec.inter * spec.hidden
+    w = synth.make_float_weights(n, seed=0, device="cuda", dtype=dtype)
+    q4 = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(n // 64, dtype=torch.int16, device="cuda")
+    rows = n // spec.hidden
+
+    def step(i):
+        coli.coli_moe_quantize_int4_gs64(w, code, rows, spec.hidden, q4, sc)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kern = traced_kernels(lambda: step(0), reps=max(4, steps // 2))
+    us = kern["quantize_int4"]["avg_us"]
+    nbytes = n * w.element_size() + n // 2 + 2 * (n // 64)  # read once, write once
+    del w, q4, sc
+    return {"workload": name, "path": "convert", "experts": experts, "values": n,
+            "src": src, "ms_per_call": round(ms, 4),
+            "weights_per_s": round(n / (ms * 1e-3), 1),
+            "quantize_int4_us": round(us, 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +416,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="main workload only")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the 2048-token GLM prefill workload (for profiling it)")
+    ap.add_argument("--convert-only", action="store_true",
+                    help="only the float -> int4 quantiser on 32 GLM-shaped experts")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
@@ -401,6 +444,10 @@ def main():
         pw = synth.WORKLOADS["glm_prefill"]
         print(json.dumps(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
                                            args.steps, args.warmup, copies=1)), flush=True)
+        return
+    if args.convert_only:
+        print(json.dumps(secondary_convert("glm_convert_32experts_bf16", synth.WORKLOADS["glm"].spec,
+                                           32, "bf16", args.steps, args.warmup)), flush=True)
         return
     w = synth.WORKLOADS["glm"]
     spec, T, layers = w.spec, 1, w.layers
@@ -452,6 +499,10 @@ def main():
         torch.cuda.empty_cache()
         secondary.append(secondary_router("glm_router_T1", w.spec, 1, 200, 10))
         secondary.append(secondary_router("glm_router_T2048", w.spec, 2048, 20, 3))
+        secondary.append(secondary_convert("glm_convert_32experts_bf16", w.spec, 32, "bf16",
+                                           20, 3))
+        secondary.append(secondary_convert("glm_convert_8experts_f32", w.spec, 8, "f32",
+                                           20, 3))
         ow = synth.WORKLOADS["olmoe"]
         secondary.append(secondary_decode("olmoe_decode_T1", ow.spec, 1, 0.0, 4, 200, 10))
         secondary.append(secondary_prefill("olmoe_prefill_T512", ow.spec, 512, 0.0, 20, 3, copies=4))

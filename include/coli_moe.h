@@ -72,7 +72,7 @@ enum {
 /* output element type of the forward calls */
 enum { COLI_OUT_BF16 = 0, COLI_OUT_F32 = 1 };
 
-/* quantize_q8_0 source element type */
+/* source element type of the quantisers */
 enum { COLI_SRC_BF16 = 0, COLI_SRC_F32 = 1 };
 
 /* workspace selector for coli_moe_workspace_bytes */
@@ -216,6 +216,31 @@ int coli_moe_forward_prefill(const coli_moe_layer_t *layer,
 int coli_moe_quantize_q8_0(const void *src, int32_t src_dtype, int64_t n,
                            int8_t *q, uint16_t *d, void *stream);
 
+/* The int4 gs64 container from float weights: quantises rows x K values
+ * (K a multiple of 64, row-major, K contiguous) into the container's nibble
+ * and scale layout.  The container's format is fixed by the pages (tantan.ink
+ * post, section "我看到的几个坑": symmetric int4 with one fp16 scale per 64
+ * weights); the offline conversion of a float checkpoint into it, shard by
+ * shard, by the tantan.ink post (section "几个关键工程动作") and the siami.tw
+ * article (section "技術核心").  The quantiser is not given there; per group
+ * of 64 consecutive weights w:
+ *   a = max |w|;  s = a / 7 (IEEE fp32 division);  s16 = s rounded to fp16
+ *   (nearest-even);  q = round-half-away-from-zero(w / float(s16)) (IEEE fp32
+ *   division), clamped to [-8, 7];  q = 0 for every weight of a group whose
+ *   s16 is 0.
+ *  src    [rows*K] bf16 or fp32 (src_dtype), device, 16-byte aligned; the
+ *         values must be finite with max |w| <= 7 * 65504.
+ *  q4     [rows*K/2] bytes, device, 4-byte aligned: weight k of a row in the
+ *         low nibble of byte k/2 when k is even, else the high nibble.
+ *  scales [rows*K/64] fp16 bits, device, 2-byte aligned.
+ * Groups are independent and flat, so matrices stored back to back (gate,
+ * up and down of an expert, or a whole container in container order) can be
+ * quantised in one call with rows*K their total size; rows*K <= 2^36.
+ * Returns COLI_E_INVALID for a bad size, dtype or null pointer and
+ * COLI_E_ALIGN for misaligned buffers; the outputs are then untouched. */
+int coli_moe_quantize_int4_gs64(const void *src, int32_t src_dtype, int64_t rows,
+                                int64_t K, uint8_t *q4, uint16_t *scales, void *stream);
+
 /* The exact int32 block dot products of one weight matrix of one expert
  * with T rows of int8 activations:
  *   dots[t][n][b] = sum_{k in [32b, 32b+32)} qw[n][k] * q_act[t][k]
@@ -242,7 +267,7 @@ enum {
   COLI_K_ROUTE_FUSED = 0, COLI_K_TOPK = 1, COLI_K_GROUP = 2, COLI_K_DECODE_GATEUP = 3,
   COLI_K_DECODE_DOWN = 4, COLI_K_COMBINE = 5, COLI_K_QUANTIZE = 6, COLI_K_PLAN = 7,
   COLI_K_GEMM_GATEUP = 8, COLI_K_GEMM_DOWN = 9, COLI_K_BLOCK_DOTS = 10,
-  COLI_K_ROUTER_LOGITS = 11, COLI_K_COUNT = 12
+  COLI_K_ROUTER_LOGITS = 11, COLI_K_QUANTIZE_INT4 = 12, COLI_K_COUNT = 13
 };
 typedef struct coli_moe_trace {
   void **start;     /* hipEvent_t[capacity] */

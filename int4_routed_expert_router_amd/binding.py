@@ -41,7 +41,7 @@ class _TraceC(ctypes.Structure):
 
 KERNEL_NAMES = ["route_fused", "route_topk", "route_group", "decode_gateup", "decode_down",
                 "combine", "quantize_q8_0", "plan", "gemm_gateup", "gemm_down", "block_dots",
-                "router_logits"]
+                "router_logits", "quantize_int4"]
 
 
 class _RouteC(ctypes.Structure):
@@ -74,6 +74,7 @@ def _load():
         lib.coli_moe_forward_decode.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
         lib.coli_moe_forward_prefill.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
         lib.coli_moe_quantize_q8_0.argtypes = [vp, i32, i64, vp, vp, vp]
+        lib.coli_moe_quantize_int4_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
         lib.coli_moe_block_dots.argtypes = [P(_LayerC), i32, i32, vp, i32, vp, vp]
         lib.coli_moe_strerror.argtypes = [ctypes.c_int]
         lib.coli_moe_strerror.restype = ctypes.c_char_p
@@ -82,7 +83,8 @@ def _load():
         lib.coli_moe_version.argtypes = []
         lib.coli_moe_version.restype = ctypes.c_char_p
         for f in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
-                  "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots"):
+                  "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
+                  "coli_moe_quantize_int4_gs64"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -200,6 +202,12 @@ def coli_moe_forward_prefill(layer: Layer, route: Route, x, T: int, y, y_dtype: 
 def coli_moe_quantize_q8_0(src, src_dtype: int, n: int, q, d, stream=None):
     _check("coli_moe_quantize_q8_0", _load().coli_moe_quantize_q8_0(
         _ptr(src), src_dtype, n, _ptr(q), _ptr(d), _stream(stream)))
+
+
+def coli_moe_quantize_int4_gs64(src, src_dtype: int, rows: int, K: int, q4, scales,
+                                stream=None):
+    _check("coli_moe_quantize_int4_gs64", _load().coli_moe_quantize_int4_gs64(
+        _ptr(src), src_dtype, rows, K, _ptr(q4), _ptr(scales), _stream(stream)))
 
 
 def coli_moe_block_dots(layer: Layer, expert: int, matrix: int, q_act, T: int, dots,

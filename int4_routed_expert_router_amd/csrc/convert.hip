@@ -1,0 +1,143 @@
+// convert.hip -- float weights -> the int4 gs64 expert container.
+//
+// The container (tantan.ink post, section "我看到的几个坑": int4, symmetric,
+// one fp16 scale per 64 weights) is made offline from the float checkpoint,
+// one shard at a time (tantan.ink post, section "几个关键工程动作"; siami.tw
+// article, section "技術核心").  The pages do not give the quantiser.  The
+// rule implemented, per group of 64 consecutive weights of a row:
+//   a = max |w|;  s = a / 7 in fp32 (IEEE division);  s16 = s rounded to
+//   fp16 (nearest-even);  q = round half away from zero of fp32(w / s16),
+//   clamped to [-8, 7];  a group with s16 == 0 gives q = 0.
+// Weights are quantised against the scale the decoders multiply by, so the
+// rounding error of each weight is at most half of s16.
+//
+// Layout: K % 64 == 0, so a row-major [rows][K] matrix is a flat sequence of
+// groups -- group g is source values [64g, 64g+64), nibble bytes
+// [32g, 32g+32) and scale g -- and one launch covers any number of
+// matrices stored back to back (a whole expert, gate | up | down).
+//
+// One group is handled by 8 lanes, 8 values each: a 16-byte load per lane
+// (two for fp32), max across the 8 lanes by three DPP moves, and one 4-byte
+// store of 8 nibbles per lane, so loads and stores of a wavefront are
+// contiguous.  Both divisions give the IEEE fp32 quotient.
+#include "device_common.h"
+#include "internal.h"
+
+namespace coli {
+namespace {
+
+constexpr int kThreads = 256;  // 32 groups per workgroup
+
+// DPP lane patterns (all lanes of each row and bank take part)
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kHalfRowMirror = 0x141;  // reverse within each group of 8 lanes
+template <int CTRL>
+COLI_DEV uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+// One lane's share of a group: its 8 values in, its 8 nibbles and the
+// group's scale out.  The 8 lanes of a group are consecutive and aligned.
+COLI_DEV void quantize_chunk(const float v[8], uint32_t &packed, uint16_t &s16_out) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  // a >= 0, and non-negative floats order as their bit patterns do
+  uint32_t ab = __float_as_uint(a);
+  ab = max(ab, dpp_u32<kQuadXor1>(ab));
+  ab = max(ab, dpp_u32<kQuadXor2>(ab));
+  ab = max(ab, dpp_u32<kHalfRowMirror>(ab));  // lane i <-> 7 - i: the other quad
+  a = __uint_as_float(ab);
+  const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(a, 7.0f));
+  const float sf = f16_to_f32(s16);
+  packed = 0;
+  if (sf != 0.0f) {
+    // q2 = fl(w / h) with h = sf / 2 (exact) is 2 fl(w / sf), exactly:
+    // scaling by 2 commutes with rounding away from the subnormal range, and
+    // a quotient that small is code 0 either way.
+    // The division is IEEE division by the group's one divisor with the
+    // divisor-only part done once: the hardware reciprocal refined by one
+    // Newton step, then per value a product and two exact-residual
+    // corrections, each fma rounding to nearest.  These are the steps of
+    // gfx9's correctly rounded fp32 division (v_div_scale / v_div_fmas /
+    // v_div_fixup) with its range scaling and special-case fix-up left out.
+    // Neither can change a code here: h is a normal fp32 number in
+    // [2^-25, 32752], the inputs are finite, and scaling only occurs for a
+    // numerator below about 2^-100, whose quotient rounds to code 0 anyway.
+    const float h = 0.5f * sf;
+    const float y0 = __builtin_amdgcn_rcpf(h);
+    const float y = fmaf(fmaf(-h, y0, 1.0f), y0, y0);
+    //
+    // Rounding half away from zero, in integers: with t = trunc(2q),
+    // q >= 0 gives r = floor(q + 1/2) = floor((t + 1) / 2) and q < 0 gives
+    // r = -floor(|q| + 1/2) = floor(t / 2), i.e. r = (t + 1 + [t < 0]*-1)
+    // >> 1 with an arithmetic shift.  r is nondecreasing in t, so clamping t
+    // to [-16, 14] clamps r to [-8, 7].  u = r + 8 in [0, 15] is the offset
+    // code; u ^ 8 is r's two's-complement nibble, applied to all eight
+    // nibbles at once.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q2 = v[i] * y;
+      q2 = fmaf(fmaf(-h, q2, v[i]), y, q2);
+      q2 = fmaf(fmaf(-h, q2, v[i]), y, q2);
+      int t = (int)q2;
+      t = max(-16, min(14, t));
+      const uint32_t u = (uint32_t)(t + 17 + (t >> 31)) >> 1;
+      packed |= u << (4 * i);  // even k in the low nibble
+    }
+    packed ^= 0x88888888u;
+  }
+  s16_out = s16;
+}
+
+COLI_DEV void load_chunk(const void *src, int src_dtype, int64_t t, float v[8]) {
+  if (src_dtype == COLI_SRC_BF16) {
+    const uint4 u = reinterpret_cast<const uint4 *>(src)[t];
+    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_to_f32(d[j] & 0xffffu);
+      v[2 * j + 1] = bf16_to_f32(d[j] >> 16);
+    }
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(src) + 2 * t;
+    const float4 f0 = p[0], f1 = p[1];
+    v[0] = f0.x, v[1] = f0.y, v[2] = f0.z, v[3] = f0.w;
+    v[4] = f1.x, v[5] = f1.y, v[6] = f1.z, v[7] = f1.w;
+  }
+}
+
+template <int SRC>
+__global__ void __launch_bounds__(kThreads) quantize_int4_kernel(const void *__restrict__ src,
+                                                                 int64_t ngroups,
+                                                                 uint32_t *__restrict__ q4,
+                                                                 uint16_t *__restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 8-value chunk
+  if ((t >> 3) >= ngroups) return;  // whole 8-lane groups leave together
+  float v[8];
+  load_chunk(src, SRC, t, v);
+  uint32_t packed;
+  uint16_t s16;
+  quantize_chunk(v, packed, s16);
+  q4[t] = packed;
+  if ((t & 7) == 0) scales[t >> 3] = s16;
+}
+
+}  // namespace
+
+int launch_quantize_int4(const void *src, int src_dtype, int64_t n, uint8_t *q4,
+                         uint16_t *scales, hipStream_t s) {
+  const int64_t chunks = n / 8;
+  const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
+  uint32_t *q = reinterpret_cast<uint32_t *>(q4);
+  if (src_dtype == COLI_SRC_BF16)
+    launch_k(COLI_K_QUANTIZE_INT4, quantize_int4_kernel<COLI_SRC_BF16>, grid, dim3(kThreads),
+             0, s, src, n / 64, q, scales);
+  else
+    launch_k(COLI_K_QUANTIZE_INT4, quantize_int4_kernel<COLI_SRC_F32>, grid, dim3(kThreads),
+             0, s, src, n / 64, q, scales);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace coli

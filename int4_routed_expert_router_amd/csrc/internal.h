@@ -55,6 +55,8 @@ void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int
                     void *y, int y_dtype, hipStream_t s);
 int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *d,
                          hipStream_t s);
+int launch_quantize_int4(const void *src, int src_dtype, int64_t n, uint8_t *q4,
+                         uint16_t *scales, hipStream_t s);
 int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_act, int T,
                       int32_t *dots, hipStream_t s);
 

@@ -34,7 +34,7 @@ ZIPF_S = 1.1
 # seed 0 it gives per-expert token counts of roughly 20 to 400.
 ZIPF_ALPHA = 0.21
 
-_KIND = {"q4": 1, "scales": 2, "logits": 3, "x": 4, "rank": 5, "bias": 6, "router": 7}
+_KIND = {"q4": 1, "scales": 2, "logits": 3, "x": 4, "rank": 5, "bias": 6, "router": 7, "float_w": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -163,6 +163,18 @@ def make_router_weights(spec: LayerSpec, seed: int = 0, layer: int = 0, device="
     w = torch.randn(spec.n_experts, spec.hidden, generator=g, device=device,
                     dtype=torch.float32)
     return (w * spec.hidden ** -0.5).to(torch.bfloat16)
+
+
+def make_float_weights(n: int, seed: int = 0, layer: int = 0, device="cpu",
+                       dtype=torch.bfloat16) -> torch.Tensor:
+    """n float weights before quantisation, flat (container order): N(0, 0.02^2)
+    with one value in 1000 made 8x larger, so group maxima vary as in trained
+    checkpoints."""
+    g = _gen(device, seed, layer, "float_w")
+    w = torch.randn(n, generator=g, device=device, dtype=torch.float32) * 0.02
+    big = torch.rand(n, generator=g, device=device) < 1e-3
+    w = torch.where(big, w * 8.0, w)
+    return w.to(dtype)
 
 
 def make_sel_bias(spec: LayerSpec, seed: int = 0, layer: int = 0) -> torch.Tensor:

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
               "coli_moe_forward_prefill", "coli_moe_workspace_bytes", "coli_moe_quantize_q8_0",
-              "coli_moe_block_dots", "coli_moe_strerror", "coli_moe_version"):
+              "coli_moe_quantize_int4_gs64", "coli_moe_block_dots", "coli_moe_strerror", "coli_moe_version"):
         assert n in names
 
 
@@ -113,6 +113,15 @@ def test_route_quantize_dots_reject_bad_calls():
     assert q(FAKE, 0, 33, FAKE, FAKE, None) == -1
     assert q(FAKE, 2, 64, FAKE, FAKE, None) == -1
     assert q(FAKE + 2, 0, 64, FAKE, FAKE, None) == -4
+    q4 = lib.coli_moe_quantize_int4_gs64
+    assert q4(None, 0, 1, 64, FAKE, FAKE, None) == -1         # src NULL
+    assert q4(FAKE, 2, 1, 64, FAKE, FAKE, None) == -1         # dtype
+    assert q4(FAKE, 0, 0, 64, FAKE, FAKE, None) == -1         # rows = 0
+    assert q4(FAKE, 0, 1, 96, FAKE, FAKE, None) == -1         # K % 64
+    assert q4(FAKE, 0, 1 << 30, 128, FAKE, FAKE, None) == -1  # rows * K > 2^36
+    assert q4(FAKE + 8, 0, 1, 64, FAKE, FAKE, None) == -4     # src align
+    assert q4(FAKE, 1, 1, 64, FAKE + 2, FAKE, None) == -4     # q4 align
+    assert q4(FAKE, 1, 1, 64, FAKE, FAKE + 1, None) == -4     # scales align
     bd = lib.coli_moe_block_dots
     assert bd(ctypes.byref(L.c), 257, 0, FAKE, 4, FAKE, None) == -1   # expert out of range
     assert bd(ctypes.byref(L.c), 0, 3, FAKE, 4, FAKE, None) == -1     # matrix out of range
