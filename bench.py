@@ -476,7 +476,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "traffic_over_algorithmic": round(traffic / gu_bytes, 4) if traffic else None,
-                "kernel": "decode_gateup (gateup_single_kernel)", "bytes_per_launch": int(gu_bytes),
+                "kernel": "decode_gateup (gateup_stream_kernel)", "bytes_per_launch": int(gu_bytes),
                 "avg_us": round(gu["avg_us"], 3), "launches_timed": gu["n"],
                 "kernel_source_digest": kernel_digest(),
                 "kernels_us": {k: round(v["avg_us"], 3) for k, v in kern.items()}}

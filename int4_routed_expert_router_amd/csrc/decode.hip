@@ -350,21 +350,43 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const float *__restri
   const int t = blockIdx.y;
   const int m = (blockIdx.x * kThreads + threadIdx.x) * 4;
   if (m >= H) return;
+  // The row positions and weights are uniform over the workgroup.  They are
+  // read in batches of kBatch, then all o rows of a batch are requested
+  // before the first is used, so a token costs about two memory round trips
+  // per batch instead of two per routed expert.  The sum order stays
+  // j = 0 .. k-1, then the shared expert.
+  constexpr int kBatch = 8;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(int64_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4 *>(o + (int64_t)pair_pos[(int64_t)t * k + j] * H + m);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  // the shared expert's row (row 0 when there is none: read, not used)
+  const float4 sh = *reinterpret_cast<const float4 *>(o + (S ? (int64_t)T * k + t : 0) * H + m);
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    int64_t pos[kBatch];
+    float wj[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int j = min(j0 + jj, k - 1);  // past k: a valid row, not used
+      pos[jj] = pair_pos[(int64_t)t * k + j];
+      wj[jj] = w[(int64_t)t * k + j];
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj)
+      v[jj] = *reinterpret_cast<const float4 *>(o + pos[jj] * H + m);
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      if (j0 + jj < k) {
+        acc.x = fmaf(wj[jj], v[jj].x, acc.x);
+        acc.y = fmaf(wj[jj], v[jj].y, acc.y);
+        acc.z = fmaf(wj[jj], v[jj].z, acc.z);
+        acc.w = fmaf(wj[jj], v[jj].w, acc.w);
+      }
+    }
   }
   if (S) {
-    const float4 v = *reinterpret_cast<const float4 *>(o + ((int64_t)T * k + t) * H + m);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    acc.x += sh.x;
+    acc.y += sh.y;
+    acc.z += sh.z;
+    acc.w += sh.w;
   }
   if (y_dtype == COLI_OUT_F32) {
     *reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + (int64_t)t * H + m) = acc;

@@ -73,13 +73,22 @@ template <int NPL>
 COLI_DEV float topk_wave(const float *__restrict__ lg_row, const float *__restrict__ bias, int E,
                          int k, uint32_t flags, float routed_scale, int *my_e) {
   const int lane = threadIdx.x & 63;
-  float lg[NPL];
+  float lg[NPL], bs[NPL];
   uint64_t key[NPL];
+  // every load issued before any is used: lanes past E read entry E-1, and
+  // with no bias the logits are read a second time in its place
+  const float *bsrc = bias ? bias : lg_row;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    lg[i] = lg_row[e];
+    bs[i] = bsrc[e];
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    lg[i] = e < E ? lg_row[e] : 0.0f;
-    key[i] = e < E ? select_key(bias ? lg[i] + bias[e] : lg[i], e) : 0ull;
+    if (e >= E) lg[i] = 0.0f;
+    key[i] = e < E ? select_key(bias ? lg[i] + bs[i] : lg[i], e) : 0ull;
   }
   float m = -FLT_MAX, z = 0.0f;
   if ((flags & COLI_ROUTE_SIGMOID) == 0) {
