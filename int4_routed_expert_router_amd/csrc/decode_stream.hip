@@ -266,13 +266,21 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
 // chunks each); RPI = 64/LPR rows share a wave instruction; a wavefront
 // computes RG such row groups (RPI * RG rows m) of one slot, for each of the
 // slot's tokens with the same weights in registers.  Each lane reads its
-// chunks of the token's h (hi + lo pairs, written by gate/up).
+// chunks of the token's h (hi + lo pairs, written by gate/up).  The four
+// wavefronts of a workgroup share the slot (H / RPW is a multiple of 4).
+// One token: the workgroup requests the token's h row before the weights,
+// stages it in LDS quad-major (quad q of chunk c at q * I/32 + c, so a
+// wavefront's reads are consecutive), and its wavefronts read it from there.
 template <int LPR, int CPL, int RG, bool ONE>
 __global__ void __launch_bounds__(kThreads) down_stream_kernel(
     Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
     float *__restrict__ o_out) {
   constexpr int RPI = 64 / LPR;
   constexpr int RPW = RPI * RG;
+  constexpr int NCHK = LPR * CPL;               // 32-value chunks of an h row (I / 32)
+  constexpr int NQ = 8 * NCHK;                  // 16-byte quads of an h row
+  constexpr int HPT = (NQ + kThreads - 1) / kThreads;
+  __shared__ uint4 hsm[ONE ? NQ : 1];
   const int lane = threadIdx.x & 63;
   const int lr = lane / LPR, lc = lane % LPR;
   const int H = L.H, I = L.I;
@@ -282,6 +290,15 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
   if (!ONE && slot >= L.S + r.n_union[0]) return;
   const Slot sl = slot_of<ONE>(r, L, T, slot);
   const int m0 = (wave % waves_per_slot) * RPW;
+  uint4 hpre[HPT];
+  if (ONE) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(h_in + (int64_t)sl.pos0 * I);
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int qi = threadIdx.x + kThreads * j;
+      if (NQ % kThreads == 0 || qi < NQ) hpre[j] = src[qi];
+    }
+  }
   const uint8_t *qd = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)I * H +
                       (int64_t)(m0 + lr) * (I / 2) + 16 * lc;
   const uint16_t *sdp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64 +
@@ -296,7 +313,15 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
       w[j][i] = *reinterpret_cast<const uint4 *>(qd + row * (I / 2) + 16 * LPR * i);
       sc[j][i] = sdp[row * (I / 64) + LPR / 2 * i];
     }
-    const int cnt = ONE ? 1 : sl.cnt;
+  if (ONE) {
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int qi = threadIdx.x + kThreads * j;
+      if (NQ % kThreads == 0 || qi < NQ) hsm[(qi & 7) * NCHK + (qi >> 3)] = hpre[j];
+    }
+    __syncthreads();
+  }
+  const int cnt = ONE ? 1 : sl.cnt;
 #pragma unroll 1
   for (int ti = 0; ti < cnt; ++ti) {
     if (!ONE) {
@@ -311,11 +336,13 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
     for (int j = 0; j < RG; ++j) v[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(h_in + pos * I + 32 * (lc + LPR * i));
+      const int c = lc + LPR * i;
+      const uint4 *src = reinterpret_cast<const uint4 *>(h_in + pos * I + 32 * c);
       XChunk hi, lo;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 a = src[q], b = src[4 + q];
+        const uint4 a = ONE ? hsm[q * NCHK + c] : src[q];
+        const uint4 b = ONE ? hsm[(4 + q) * NCHK + c] : src[4 + q];
         hi.p[4 * q] = a.x, hi.p[4 * q + 1] = a.y, hi.p[4 * q + 2] = a.z, hi.p[4 * q + 3] = a.w;
         lo.p[4 * q] = b.x, lo.p[4 * q + 1] = b.y, lo.p[4 * q + 2] = b.z, lo.p[4 * q + 3] = b.w;
       }
