@@ -37,10 +37,12 @@ def _bind(path):
     p = ctypes.c_void_p
     i32, i64, u32, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
     lib.oracle_route.argtypes = [i32, i32, i32, u32, f32, p, p, p, p, p, p, p]
-    lib.oracle_forward_decode.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p]
-    lib.oracle_forward_prefill.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p, p]
+    lib.oracle_forward_decode.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p, i32]
+    lib.oracle_forward_prefill.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p, p,
+                                           i32]
     lib.oracle_quantize_q8_0.argtypes = [p, i64, p, p]
-    lib.oracle_block_dots.argtypes = [i64, i64, i64, i64, p, p, i64, ctypes.c_int, p, i64, p]
+    lib.oracle_block_dots.argtypes = [i64, i64, i64, i64, p, p, i64, ctypes.c_int, p, i64, p,
+                                      i32]
     lib.oracle_router_logits.argtypes = [i64, i64, i64, p, p, p]
     lib.oracle_quantize_int4_gs64.argtypes = [p, i64, i64, p, p]
     lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
@@ -153,8 +155,9 @@ def router_logits(w_bf16, x_bf16):
     return out
 
 
-def forward_decode(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16):
-    """Decode-mode layer output, fp64 [T, H].  x_bf16: uint16 bits [T, H]."""
+def forward_decode(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, int8_weights=False):
+    """Decode-mode layer output, fp64 [T, H].  x_bf16: uint16 bits [T, H].
+    int8_weights: the container holds one int8 byte per weight (else nibbles)."""
     lib = _load()
     q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
     topk_idx, topk_w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
@@ -162,13 +165,14 @@ def forward_decode(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16):
     T = x.shape[0]
     y = np.zeros((T, H), np.float64)
     rc = lib.oracle_forward_decode(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
-                                   _ptr(topk_w), _ptr(x), T, _ptr(y))
+                                   _ptr(topk_w), _ptr(x), T, _ptr(y), int(bool(int8_weights)))
     if rc != 0:
         raise ValueError("oracle_forward_decode failed")
     return y
 
 
-def forward_prefill(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, want_h=False):
+def forward_prefill(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, want_h=False,
+                    int8_weights=False):
     """Integer-path (Q8_0) layer output, fp64 [T, H] (and fp32 h [T, k+S, I])."""
     lib = _load()
     q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
@@ -178,7 +182,8 @@ def forward_prefill(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, want_h=
     y = np.zeros((T, H), np.float64)
     h = np.zeros((T, k + S, I), np.float32) if want_h else None
     rc = lib.oracle_forward_prefill(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
-                                    _ptr(topk_w), _ptr(x), T, _ptr(y), _ptr(h))
+                                    _ptr(topk_w), _ptr(x), T, _ptr(y), _ptr(h),
+                                    int(bool(int8_weights)))
     if rc != 0:
         raise ValueError("oracle_forward_prefill failed")
     return (y, h) if want_h else y
@@ -195,7 +200,7 @@ def quantize_q8_0(v):
     return q, d
 
 
-def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act):
+def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act, int8_weights=False):
     """Exact int32 block dots [T, rows, K/32] of one matrix of one expert."""
     lib = _load()
     q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
@@ -205,7 +210,7 @@ def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act):
     T = q_act.reshape(-1, K).shape[0]
     dots = np.zeros((T, rows, K // 32), np.int32)
     rc = lib.oracle_block_dots(H, I, E, S, _ptr(q4), _ptr(scales), expert, matrix,
-                               _ptr(q_act), T, _ptr(dots))
+                               _ptr(q_act), T, _ptr(dots), int(bool(int8_weights)))
     if rc != 0:
         raise ValueError("oracle_block_dots: invalid arguments")
     return dots

@@ -14,6 +14,10 @@
  * Definitions followed (web pages about the colibri engine):
  *  - int4, one fp16 scale per 64 weights ("gs64"): tantan.ink post
  *    "colibri: 把 744B 模型当数据流...", section "我看到的几个坑".
+ *  - int8-weight experts (the MTP layer's experts must be int8, same post
+ *    and section; the OLMoE container is int8, ai-tools-nav review, model
+ *    family table): read as the same container with one two's-complement
+ *    byte per weight in place of a nibble, the same fp16 scale per 64.
  *  - three matrices gate/up/down per expert, each distinct expert read once
  *    per batch: same post, section "几个关键工程动作".
  *  - Q8_0-style int8 activations on the integer path: alphamatch.ai blog
@@ -94,9 +98,11 @@ static int or_nib(uint8_t byte, int high) {
   return v >= 8 ? v - 16 : v;
 }
 
-/* weight q[n][k] of a row-major nibble matrix whose rows hold K/2 bytes:
- * byte k/2, low nibble for even k, high nibble for odd k. */
-static int or_q(const uint8_t *mat, int64_t K, int64_t n, int64_t k) {
+/* weight q[n][k] of a row-major code matrix.  int4 (w8 == 0): rows hold
+ * K/2 bytes, byte k/2, low nibble for even k, high nibble for odd k.
+ * int8 (w8 == 1): rows hold K bytes, byte k, two's complement. */
+static int or_q(const uint8_t *mat, int64_t K, int64_t n, int64_t k, int w8) {
+  if (w8) return (int)(int8_t)mat[n * K + k];
   return or_nib(mat[n * (K / 2) + k / 2], (int)(k & 1));
 }
 
@@ -111,12 +117,17 @@ typedef struct {
   int64_t H, I, E, S;
   const uint8_t *q4;      /* host copy of the container */
   const uint16_t *scales; /* host copy, fp16 bits */
+  int w8;                 /* 0: int4 nibbles, 1: int8 bytes */
 } or_layer;
 
-/* matrix m (0 gate, 1 up, 2 down) of expert e: nibble base and scale base.
- * Expert e occupies 3*I*H/2 bytes and 3*I*H/64 scales, matrices in order. */
+/* matrix m (0 gate, 1 up, 2 down) of expert e: code base and scale base.
+ * A matrix holds I*H codes: I*H/2 bytes (int4) or I*H bytes (int8).  Expert
+ * e occupies three matrices and 3*I*H/64 scales, matrices in order. */
+static int64_t or_mat_bytes(const or_layer *L) {
+  return L->w8 ? L->I * L->H : L->I * L->H / 2;
+}
 static const uint8_t *or_mat(const or_layer *L, int64_t e, int m) {
-  return L->q4 + e * (3 * L->I * L->H / 2) + (int64_t)m * (L->I * L->H / 2);
+  return L->q4 + e * 3 * or_mat_bytes(L) + (int64_t)m * or_mat_bytes(L);
 }
 static const uint16_t *or_sc(const or_layer *L, int64_t e, int m) {
   return L->scales + e * (3 * L->I * L->H / 64) + (int64_t)m * (L->I * L->H / 64);
@@ -241,15 +252,15 @@ static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t k = 0; k < H; ++k) {
-      g += (double)or_q(qg, H, n, k) * or_s(sg, H, n, k) * x[k];
-      u += (double)or_q(qu, H, n, k) * or_s(su, H, n, k) * x[k];
+      g += (double)or_q(qg, H, n, k, L->w8) * or_s(sg, H, n, k) * x[k];
+      u += (double)or_q(qu, H, n, k, L->w8) * or_s(su, H, n, k) * x[k];
     }
     h[n] = or_silu(g) * u;
   }
   for (int64_t m = 0; m < H; ++m) {
     double acc = 0.0;
     for (int64_t n = 0; n < I; ++n)
-      acc += (double)or_q(qd, I, m, n) * or_s(sd, I, m, n) * h[n];
+      acc += (double)or_q(qd, I, m, n, L->w8) * or_s(sd, I, m, n) * h[n];
     o[m] = acc;
   }
 }
@@ -261,10 +272,11 @@ static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
 int oracle_forward_decode(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
                           const uint8_t *q4, const uint16_t *scales,
                           const int32_t *topk_idx, const float *topk_w,
-                          const uint16_t *x_bf16, int64_t T, double *y) {
-  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1)
+                          const uint16_t *x_bf16, int64_t T, double *y, int32_t w8) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1 ||
+      (w8 != 0 && w8 != 1))
     return OR_EINVAL;
-  or_layer L = {H, I, E, S, q4, scales};
+  or_layer L = {H, I, E, S, q4, scales, w8};
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t t = 0; t < T; ++t) {
@@ -367,29 +379,31 @@ int oracle_quantize_int4_gs64(const float *w, int64_t rows, int64_t K, uint8_t *
   return OR_OK;
 }
 
-/* Exact int32 dot of one 32-block: weights of row n (nibble matrix with
- * K/2 bytes per row) against int8 activations a[K], over k in [32b, 32b+32). */
-static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n,
+/* Exact int32 dot of one 32-block: weights of row n of a code matrix
+ * against int8 activations a[K], over k in [32b, 32b+32). */
+static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n, int w8,
                             const int8_t *a, int64_t b) {
   int32_t acc = 0;
-  for (int64_t k = 32 * b; k < 32 * b + 32; ++k) acc += or_q(mat, K, n, k) * (int32_t)a[k];
+  for (int64_t k = 32 * b; k < 32 * b + 32; ++k)
+    acc += or_q(mat, K, n, k, w8) * (int32_t)a[k];
   return acc;
 }
 
 /* dots[t][n][b] for matrix m (0 gate, 1 up, 2 down) of expert e. */
 int oracle_block_dots(int64_t H, int64_t I, int64_t E, int64_t S,
                       const uint8_t *q4, const uint16_t *scales, int64_t e,
-                      int m, const int8_t *q_act, int64_t T, int32_t *dots) {
-  if (H <= 0 || I <= 0 || H % 64 || I % 64 || m < 0 || m > 2 || e < 0 || e >= E + S)
+                      int m, const int8_t *q_act, int64_t T, int32_t *dots, int32_t w8) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || m < 0 || m > 2 || e < 0 || e >= E + S ||
+      (w8 != 0 && w8 != 1))
     return OR_EINVAL;
-  or_layer L = {H, I, E, S, q4, scales};
+  or_layer L = {H, I, E, S, q4, scales, w8};
   const int64_t K = (m == 2) ? I : H, rows = (m == 2) ? H : I, nb = K / 32;
   const uint8_t *mat = or_mat(&L, e, m);
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t)
     for (int64_t n = 0; n < rows; ++n)
       for (int64_t b = 0; b < nb; ++b)
-        dots[(t * rows + n) * nb + b] = or_block_dot(mat, K, n, q_act + t * K, b);
+        dots[(t * rows + n) * nb + b] = or_block_dot(mat, K, n, L.w8, q_act + t * K, b);
   return OR_OK;
 }
 
@@ -408,8 +422,8 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
     double g = 0.0, u = 0.0;
     for (int64_t b = 0; b < H / 32; ++b) {
       double d = or_f16(dx[b]);
-      g += or_f16(sg[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qg, H, n, qx, b);
-      u += or_f16(su[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qu, H, n, qx, b);
+      g += or_f16(sg[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qg, H, n, L->w8, qx, b);
+      u += or_f16(su[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qu, H, n, L->w8, qx, b);
     }
     hf[n] = (float)(or_silu(g) * u);
   }
@@ -418,7 +432,7 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
     double acc = 0.0;
     for (int64_t b = 0; b < I / 32; ++b)
       acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *
-             (double)or_block_dot(qd, I, m, qh, b);
+             (double)or_block_dot(qd, I, m, L->w8, qh, b);
     o[m] = acc;
   }
   return OR_OK;
@@ -432,10 +446,11 @@ int oracle_forward_prefill(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k
                            const uint8_t *q4, const uint16_t *scales,
                            const int32_t *topk_idx, const float *topk_w,
                            const uint16_t *x_bf16, int64_t T, double *y,
-                           float *h_out) {
-  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1)
+                           float *h_out, int32_t w8) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1 ||
+      (w8 != 0 && w8 != 1))
     return OR_EINVAL;
-  or_layer L = {H, I, E, S, q4, scales};
+  or_layer L = {H, I, E, S, q4, scales, w8};
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t t = 0; t < T; ++t) {

@@ -49,6 +49,7 @@ class LayerSpec:
     sigmoid: bool
     renorm: bool
     routed_scale: float = 1.0
+    int8: bool = False  # one int8 byte per weight instead of a nibble
 
     @property
     def flags(self) -> int:
@@ -60,8 +61,9 @@ class LayerSpec:
 
     @property
     def expert_bytes(self) -> int:
-        """Nibble bytes of one expert: gate, up and down (3*I*H weights)."""
-        return 3 * self.inter * self.hidden // 2
+        """Code bytes of one expert: gate, up and down (3*I*H weights), a
+        nibble or a byte each."""
+        return 3 * self.inter * self.hidden // (1 if self.int8 else 2)
 
     @property
     def expert_scales(self) -> int:
@@ -116,7 +118,9 @@ def make_weights(spec: LayerSpec, seed: int = 0, layer: int = 0, device="cpu",
                  experts: int | None = None):
     """Container of one layer: (q4 uint8 [n*expert_bytes], scales fp16 [n*expert_scales]).
 
-    `experts` defaults to E + S.  Uniform random bytes are uniform nibbles.
+    `experts` defaults to E + S.  Uniform random bytes are uniform nibbles
+    (or uniform int8 codes).  Scales are |N(0, 0.02)| for int4 codes and 16x
+    smaller for int8 codes, so both give weights of the same size.
     """
     n = spec.n_total if experts is None else experts
     g = _gen(device, seed, layer, "q4")
@@ -125,7 +129,7 @@ def make_weights(spec: LayerSpec, seed: int = 0, layer: int = 0, device="cpu",
     g = _gen(device, seed, layer, "scales")
     sc = torch.randn(n * spec.expert_scales, generator=g, device=device,
                      dtype=torch.float32)
-    scales = (sc * 0.02).abs_().to(torch.float16)
+    scales = (sc * (0.02 / 16 if spec.int8 else 0.02)).abs_().to(torch.float16)
     return q4, scales
 
 

@@ -24,19 +24,27 @@ def unpack_nibbles(rows_bytes: np.ndarray) -> np.ndarray:
     return out
 
 
-def dense_experts(H, I, n, q4, scales):
+def codes(qb: np.ndarray, rows: int, K: int, int8: bool) -> np.ndarray:
+    """[rows, K] integer codes of one matrix's bytes."""
+    if int8:
+        return np.asarray(qb, np.uint8).view(np.int8).reshape(rows, K)
+    return unpack_nibbles(np.asarray(qb, np.uint8).reshape(rows, K // 2))
+
+
+def dense_experts(H, I, n, q4, scales, int8=False):
     """Dequantised fp64 (Wg [I,H], Wu [I,H], Wd [H,I]) for experts 0..n-1."""
     q4 = np.asarray(q4, np.uint8)
     sc = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
-    eb, es = 3 * I * H // 2, 3 * I * H // 64
+    mb = I * H if int8 else I * H // 2
+    eb, es = 3 * mb, 3 * I * H // 64
     out = []
     for e in range(n):
         qe, se = q4[e * eb:(e + 1) * eb], sc[e * es:(e + 1) * es]
         mats = []
         for m, (rows, K) in enumerate(((I, H), (I, H), (H, I))):
-            qb = qe[m * (I * H // 2):(m + 1) * (I * H // 2)].reshape(rows, K // 2)
+            qm = codes(qe[m * mb:(m + 1) * mb], rows, K, int8)
             sb = se[m * (I * H // 64):(m + 1) * (I * H // 64)].reshape(rows, K // 64)
-            mats.append(unpack_nibbles(qb).astype(np.float64) * np.repeat(sb, 64, axis=1))
+            mats.append(qm.astype(np.float64) * np.repeat(sb, 64, axis=1))
         out.append(tuple(mats))
     return out
 
@@ -82,10 +90,10 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def decode_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits):
+def decode_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, int8=False):
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
-    experts = dense_experts(H, I, E + S, q4, scales)
+    experts = dense_experts(H, I, E + S, q4, scales, int8)
     wmat = np.zeros((T, E + S))
     for t in range(T):
         for j in range(topk_idx.shape[1]):
@@ -112,13 +120,13 @@ def q8_0(v):
     return q.astype(np.int8).reshape(-1), d.astype(np.float16)
 
 
-def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits):
+def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, int8=False):
     x32 = bf16_to_f64(x_bits).astype(np.float32)
     T = x32.shape[0]
     qx, dx = q8_0(x32)
     xh = qx.reshape(T, H // 32, 32).astype(np.float64) * dx.astype(np.float64).reshape(T, H // 32, 1)
     xh = xh.reshape(T, H)
-    experts = dense_experts(H, I, E + S, q4, scales)
+    experts = dense_experts(H, I, E + S, q4, scales, int8)
     wmat = np.zeros((T, E + S))
     for t in range(T):
         for j in range(topk_idx.shape[1]):
@@ -135,12 +143,12 @@ def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits):
     return y
 
 
-def block_dots(H, I, q4, expert, matrix, q_act):
-    eb = 3 * I * H // 2
+def block_dots(H, I, q4, expert, matrix, q_act, int8=False):
+    mb = I * H if int8 else I * H // 2
+    eb = 3 * mb
     rows, K = ((I, H), (I, H), (H, I))[matrix]
-    qb = np.asarray(q4, np.uint8)[expert * eb + matrix * (I * H // 2):
-                                  expert * eb + (matrix + 1) * (I * H // 2)]
-    w = unpack_nibbles(qb.reshape(rows, K // 2)).astype(np.int64)
+    qb = np.asarray(q4, np.uint8)[expert * eb + matrix * mb:expert * eb + (matrix + 1) * mb]
+    w = codes(qb, rows, K, int8).astype(np.int64)
     a = np.asarray(q_act, np.int8).reshape(-1, K).astype(np.int64)
     T = a.shape[0]
     prod = w[None, :, :] * a[:, None, :]

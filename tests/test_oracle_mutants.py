@@ -20,6 +20,7 @@ CHECKS = [
     pins.check_prefill_zero_scales, pins.check_router_logits_closed_form,
     pins.check_router_logits_vs_bruteforce, pins.check_int4_quant_vs_bruteforce,
     pins.check_int4_quant_closed_form, pins.check_int4_quant_properties,
+    pins.check_int8_decode_prefill_vs_bruteforce, pins.check_int8_block_dots,
 ]
 
 # (name, text in the oracle, replacement)
@@ -31,14 +32,20 @@ MUTANTS = [
     ("scale group of 32", "return or_f16(sc[n * (K / 64) + k / 64]);",
      "return or_f16(sc[n * (K / 64) + (k / 32) % (K / 64)]);"),
     ("matrix stride wrong",
-     "return L->q4 + e * (3 * L->I * L->H / 2) + (int64_t)m * (L->I * L->H / 2);",
-     "return L->q4 + e * (3 * L->I * L->H / 2) + (int64_t)m * (L->I * L->H / 4);"),
+     "return L->q4 + e * 3 * or_mat_bytes(L) + (int64_t)m * or_mat_bytes(L);",
+     "return L->q4 + e * 3 * or_mat_bytes(L) + (int64_t)m * or_mat_bytes(L) / 2;"),
+    ("int8 code read unsigned", "if (w8) return (int)(int8_t)mat[n * K + k];",
+     "if (w8) return (int)mat[n * K + k];"),
+    ("int8 rows read as nibble rows", "if (w8) return (int)(int8_t)mat[n * K + k];",
+     "if (w8) return (int)(int8_t)mat[n * (K / 2) + k];"),
+    ("int8 matrix sized as nibbles", "return L->w8 ? L->I * L->H : L->I * L->H / 2;",
+     "return L->I * L->H / 2;"),
     ("up uses gate scales", "*su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {",
      "*su = or_sc(L, e, 0), *sd = or_sc(L, e, 2);\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {"),
     ("silu sign flipped", "return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
     ("gate and up swapped in swiglu", "h[n] = or_silu(g) * u;", "h[n] = or_silu(u) * g;"),
-    ("down transposed", "acc += (double)or_q(qd, I, m, n) * or_s(sd, I, m, n) * h[n];",
-     "acc += (double)or_q(qd, I, n % I, m % I) * or_s(sd, I, m, n) * h[n];"),
+    ("down transposed", "acc += (double)or_q(qd, I, m, n, L->w8) * or_s(sd, I, m, n) * h[n];",
+     "acc += (double)or_q(qd, I, n % I, m % I, L->w8) * or_s(sd, I, m, n) * h[n];"),
     ("shared expert dropped", "      if (S) {\n        or_ffn_f64(&L, E, x, h, o);", "      if (0) {\n        or_ffn_f64(&L, E, x, h, o);"),
     ("routing weight ignored", "for (int64_t i = 0; i < H; ++i) yt[i] += w * o[i];\n      }\n      if (S)",
      "for (int64_t i = 0; i < H; ++i) yt[i] += o[i];\n      }\n      if (S)"),

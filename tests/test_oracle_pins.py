@@ -351,8 +351,71 @@ def check_prefill_zero_scales():
     assert np.all(y == 0.0)
 
 
+SIGMOID_SMALL_I8 = synth.LayerSpec(192, 128, 5, 1, 3, sigmoid=True, renorm=True, int8=True)
+SOFTMAX_SMALL_I8 = synth.LayerSpec(128, 64, 6, 0, 2, sigmoid=False, renorm=False, int8=True)
+
+
+def check_int8_decode_prefill_vs_bruteforce():
+    for spec, T in ((SOFTMAX_SMALL_I8, 4), (SIGMOID_SMALL_I8, 5)):
+        q4, sc, r, x = _decode_case(spec, T, seed=12, zipf=0.3)
+        s = spec
+        assert q4.size == s.n_total * 3 * s.hidden * s.inter  # one byte per weight
+        args = (s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k, q4, sc, r["topk_idx"],
+                r["topk_w"], x)
+        y = oracle.forward_decode(*args, int8_weights=True)
+        yb = bf.decode_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
+                             r["topk_idx"], r["topk_w"], x, int8=True)
+        assert _rel(y, yb) < 1e-10
+        yp = oracle.forward_prefill(*args, int8_weights=True)
+        ypb = bf.prefill_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
+                               r["topk_idx"], r["topk_w"], x, int8=True)
+        assert _rel(yp, ypb) < 1e-10
+        assert 1e-6 < _rel(yp, y) < 5e-2
+
+
+def check_int8_block_dots():
+    spec = SIGMOID_SMALL_I8
+    q4, sc = _host_layer(spec, 13)
+    rng = np.random.default_rng(13)
+    for m in (0, 2):
+        K = spec.inter if m == 2 else spec.hidden
+        a = rng.integers(-127, 128, (3, K)).astype(np.int8)
+        for e in (0, spec.n_total - 1):
+            d = oracle.block_dots(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, q4, sc,
+                                  e, m, a, int8_weights=True)
+            assert np.array_equal(d, bf.block_dots(spec.hidden, spec.inter, q4, e, m, a,
+                                                   int8=True))
+    # every int8 code: row 0 of a gate matrix holds byte values 0..255 at
+    # k = 0..255; activation row j is 127 (or -1) at k = j only
+    H, I = 256, 64
+    q8 = np.zeros(3 * H * I, np.uint8)
+    q8[:256] = np.arange(256)
+    a = np.zeros((512, H), np.int8)
+    a[np.arange(256), np.arange(256)] = 127
+    a[256 + np.arange(256), np.arange(256)] = -1
+    z = np.zeros(3 * H * I // 64, np.uint16)
+    d = oracle.block_dots(H, I, 1, 0, q8, z, 0, 0, a, int8_weights=True)
+    code = np.arange(256).astype(np.uint8).view(np.int8).astype(np.int32)
+    j = np.arange(256)
+    assert np.array_equal(d[j, 0, j // 32], 127 * code)
+    assert np.array_equal(d[256 + j, 0, j // 32], -code)
+    assert not d[:, 1:, :].any()
+    worst = np.full(3 * H * I, 0x80, np.uint8)  # every code -128
+    d = oracle.block_dots(H, I, 1, 0, worst, z, 0, 0, np.full((1, H), -127, np.int8),
+                          int8_weights=True)
+    assert np.all(d == 32 * 128 * 127)
+
+
 def test_block_dots_vs_bruteforce():
     check_block_dots_vs_bruteforce()
+
+
+def test_int8_decode_prefill_vs_bruteforce():
+    check_int8_decode_prefill_vs_bruteforce()
+
+
+def test_int8_block_dots():
+    check_int8_block_dots()
 
 
 def test_prefill_vs_bruteforce():
