@@ -75,10 +75,13 @@ enum { COLI_OUT_BF16 = 0, COLI_OUT_F32 = 1 };
 /* source element type of the quantisers */
 enum { COLI_SRC_BF16 = 0, COLI_SRC_F32 = 1 };
 
+/* weight code width of the expert container (coli_moe_layer_t.weight_format) */
+enum { COLI_WEIGHTS_INT4 = 0, COLI_WEIGHTS_INT8 = 1 };
+
 /* workspace selector for coli_moe_workspace_bytes */
 enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
 
-/* ---- the int4 gs64 expert container --------------------------------------
+/* ---- the gs64 expert container --------------------------------------------
  * Experts e = 0 .. E-1 are routed; when n_shared == 1, expert E is the shared
  * expert.  Every expert owns three matrices, stored adjacently in this order:
  *     gate [I rows x H]   up [I rows x H]   down [H rows x I]
@@ -99,6 +102,19 @@ enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
  * post, section "它的核心判断").
  * Requirements: H, I multiples of 64 in [64, 16384]; 1 <= E <= 1024;
  * n_shared in {0, 1}; 1 <= k <= min(E, 32); q4 and scales 16-byte aligned.
+ *
+ * int8 codes (weight_format = COLI_WEIGHTS_INT8): the same container with one
+ * byte per weight, a two's-complement integer q in [-128, 127], in place of
+ * a nibble: row n holds K bytes (byte k is weight k); a matrix is I*H bytes
+ * and expert e starts at byte e * 3*I*H (gate at 0, up at I*H, down at
+ * 2*I*H).  Scales are unchanged: one fp16 per 64 weights, w = q * s.  The
+ * pages require int8 experts for the MTP layer (int4 there collapses the
+ * draft acceptance; tantan.ink post, section "我看到的几个坑") and list the
+ * OLMoE container as int8 (ai-tools-nav review, model family table); they do
+ * not give its scale granularity, read here as the same gs64.  int8 layers
+ * run in coli_moe_forward_decode when the shape has the streaming path
+ * (H a multiple of 2048 up to 8192; I in {512, 1024} or a multiple of 2048
+ * up to 8192) and T <= 16; other calls return COLI_E_UNSUPPORTED.
  */
 typedef struct coli_moe_layer {
   int32_t hidden;        /* H */
@@ -110,6 +126,7 @@ typedef struct coli_moe_layer {
   float routed_scale;    /* multiplies every routing weight (1.0f usually) */
   const uint8_t *q4;     /* device, see above */
   const uint16_t *scales;/* device, fp16 bit patterns, see above */
+  int32_t weight_format; /* COLI_WEIGHTS_INT4 (0) or COLI_WEIGHTS_INT8 */
 } coli_moe_layer_t;
 
 /* ---- route buffers (caller-allocated device memory) ---------------------

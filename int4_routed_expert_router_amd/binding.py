@@ -15,6 +15,7 @@ COLI_ROUTE_SOFTMAX, COLI_ROUTE_SIGMOID, COLI_ROUTE_RENORM = 0, 1, 256
 COLI_OUT_BF16, COLI_OUT_F32 = 0, 1
 COLI_SRC_BF16, COLI_SRC_F32 = 0, 1
 COLI_ENTRY_ROUTE, COLI_ENTRY_DECODE, COLI_ENTRY_PREFILL = 0, 1, 2
+COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8 = 0, 1
 
 
 class ColiError(RuntimeError):
@@ -30,6 +31,7 @@ class _LayerC(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("routed_scale", ctypes.c_float),
         ("q4", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("weight_format", ctypes.c_int32),
     ]
 
 
@@ -105,22 +107,24 @@ def _stream(stream):
 
 
 class Layer:
-    """One MoE layer: shape, routing kind and the device int4 gs64 container.
+    """One MoE layer: shape, routing kind and the device gs64 container.
 
-    q4: uint8 tensor of (E+S)*3*I*H/2 bytes; scales: fp16 tensor of
-    (E+S)*3*I*H/64 values (see include/coli_moe.h for the byte layout).
+    q4: uint8 tensor of (E+S)*3*I*H/2 bytes (int4 codes) or (E+S)*3*I*H bytes
+    (int8 codes, int8=True); scales: fp16 tensor of (E+S)*3*I*H/64 values
+    (see include/coli_moe.h for the byte layout).
     """
 
     def __init__(self, hidden, inter, n_experts, n_shared, top_k, flags, q4, scales,
-                 routed_scale=1.0):
+                 routed_scale=1.0, int8=False):
         self.q4, self.scales = q4, scales  # keep the tensors alive
         self.c = _LayerC(hidden, inter, n_experts, n_shared, top_k, flags, routed_scale,
-                         _ptr(q4), _ptr(scales))
+                         _ptr(q4), _ptr(scales),
+                         COLI_WEIGHTS_INT8 if int8 else COLI_WEIGHTS_INT4)
 
     @classmethod
     def from_spec(cls, spec, q4, scales):
         return cls(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, spec.top_k,
-                   spec.flags, q4, scales, spec.routed_scale)
+                   spec.flags, q4, scales, spec.routed_scale, getattr(spec, "int8", False))
 
     hidden = property(lambda s: s.c.hidden)
     inter = property(lambda s: s.c.inter)

@@ -29,6 +29,8 @@ int check_layer(const coli_moe_layer_t *l, Layer *out) {
   if (l->top_k < 1 || l->top_k > l->n_experts || l->top_k > kMaxTopK) return COLI_E_INVALID;
   if (l->flags & ~(uint32_t)(COLI_ROUTE_SIGMOID | COLI_ROUTE_RENORM)) return COLI_E_INVALID;
   if (!isfinite(l->routed_scale)) return COLI_E_INVALID;
+  if (l->weight_format != COLI_WEIGHTS_INT4 && l->weight_format != COLI_WEIGHTS_INT8)
+    return COLI_E_INVALID;
   if (out) {
     out->H = H;
     out->I = I;
@@ -39,7 +41,8 @@ int check_layer(const coli_moe_layer_t *l, Layer *out) {
     out->routed_scale = l->routed_scale;
     out->q4 = l->q4;
     out->scales = l->scales;
-    out->expert_bytes = (int64_t)3 * I * H / 2;
+    out->w8 = l->weight_format == COLI_WEIGHTS_INT8;
+    out->expert_bytes = out->w8 ? (int64_t)3 * I * H : (int64_t)3 * I * H / 2;
     out->expert_scales = (int64_t)3 * I * H / 64;
   }
   return COLI_OK;
@@ -80,6 +83,9 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
   if ((rc = check_route(route))) return rc;
   if ((rc = check_tokens(*L, T, entry == COLI_ENTRY_DECODE ? kMaxDecodeT : kMaxT))) return rc;
   if (entry == COLI_ENTRY_DECODE && L->I > kMaxDecodeInter) return COLI_E_UNSUPPORTED;
+  // int8 codes: decode on the streaming path only; prefill not yet
+  if (L->w8 && (entry != COLI_ENTRY_DECODE || !decode_stream_supported(*L, T)))
+    return COLI_E_UNSUPPORTED;
   if (!x || !y) return COLI_E_INVALID;
   if (y_dtype != COLI_OUT_BF16 && y_dtype != COLI_OUT_F32) return COLI_E_INVALID;
   if (!aligned(x, 16) || !aligned(y, 16)) return COLI_E_ALIGN;

@@ -10,9 +10,11 @@
 // independent wavefronts keep the most bytes in flight.  Gate/up stages the
 // slot's activations per workgroup in LDS, up to four tokens at a time; down
 // reads its chunks of each token's h directly, as gate/up wrote them.
-// Nibbles become exact bf16 values 136 + q (one v_bitop3 per pair after a
-// shift) and meet the activations in v_dot2_f32_bf16; each 32-chunk's bias
-// 136 * sum(x) is removed before its fp16 group scale.  Lane partials of
+// int4 codes become exact bf16 values 136 + q (one v_bitop3 per pair after
+// a shift) and meet the activations in v_dot2_f32_bf16; each 32-chunk's bias
+// 136 * sum(x) is removed before its fp16 group scale.  int8 codes (same
+// container, one byte per weight) become exact bf16 values q through an
+// fp32 conversion of each sign-extended byte (see the codecs below).  Lane partials of
 // several rows are combined with a reduce-scatter (each shuffle step halves
 // the values a lane carries).  A token's arithmetic does not depend on the
 // other tokens of the batch.
@@ -118,31 +120,107 @@ COLI_DEV void opaque(uint4 &w) {
   asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
 }
 
-// 32 weights of one chunk (a 16-byte load) dotted with paired activations;
-// the accumulator starts at -bias.
-COLI_DEV float chunk_dot(const uint4 w, const uint32_t *xp, float neg_bias) {
-  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-  float a = neg_bias;
+// Weight codecs.  A chunk is 32 consecutive weights of a row (half of a
+// 64-weight scale group): Q 16-byte quads of codes.  Activations are staged
+// as 16 bf16 pairs per chunk in the pair order the codec's unpacking
+// produces; every pair value is an exact bf16 integer (bias + q), and a
+// codec with a bias removes the chunk's bias * sum(x) before its fp16 scale.
+//
+// int4 (one nibble per weight): one quad per chunk; pairs (k, k+4) within
+// each 8 weights; bf16 136 + q from one v_bitop3 per pair.
+struct CodecI4 {
+  static constexpr int Q = 1;
+  static constexpr float kBias = (float)kNibBias;
+  static constexpr int64_t bytes(int64_t codes) { return codes / 2; }
+  COLI_DEV static void pairs(const uint32_t d[4], uint32_t out[4]) { x8_to_pairs(d, out); }
+  // chunk dotted with pairs xp (and, when lp is given, with a second set of
+  // pairs lp: the low half of a split activation), from accumulator a
+  template <bool TWO>
+  COLI_DEV static float dot(const uint4 *w, const uint32_t *xp, const uint32_t *lp, float a) {
+    const uint32_t wv[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
 #pragma unroll
-  for (int dw = 0; dw < 4; ++dw) {
-    uint32_t p[4];
-    nib8_to_bf16x4(wv[dw], p[0], p[1], p[2], p[3]);
+    for (int dw = 0; dw < 4; ++dw) {
+      uint32_t p[4];
+      nib8_to_bf16x4(wv[dw], p[0], p[1], p[2], p[3]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a = dot2_bf16(p[q], xp[4 * dw + q], a);
+      for (int q = 0; q < 4; ++q) {
+        a = dot2_bf16(p[q], xp[4 * dw + q], a);
+        if (TWO) a = dot2_bf16(p[q], lp[4 * dw + q], a);
+      }
+    }
+    return a;
   }
-  return a;
+  // bf16 slot of value w (0..31) in a chunk half: dword 4o + q pairs values
+  // 8o + q (low 16 bits) and 8o + q + 4 (high 16 bits)
+  COLI_DEV static int half_index(int w) {
+    const int o = w >> 3, k = w & 7;
+    return 2 * (4 * o + (k & 3)) + (k >> 2);
+  }
+};
+
+// int8 (one byte per weight): two quads per chunk; natural pairs (k, k+1).
+// Each signed byte converts to fp32 exactly (one sign-extending byte select
+// per value) and two of them pack into a bf16 pair (their low halves are
+// zero), so the pairs hold q itself: no bias, no cancellation.
+struct CodecI8 {
+  static constexpr int Q = 2;
+  static constexpr float kBias = 0.0f;
+  static constexpr int64_t bytes(int64_t codes) { return codes; }
+  COLI_DEV static void pairs(const uint32_t d[4], uint32_t out[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = d[i];
+  }
+  COLI_DEV static uint32_t bf16_pair(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
+  template <bool TWO>
+  COLI_DEV static float dot(const uint4 *w, const uint32_t *xp, const uint32_t *lp, float a) {
+    const uint32_t wv[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+    for (int dw = 0; dw < 8; ++dw) {
+      const uint32_t v = wv[dw];
+      const uint32_t p01 = bf16_pair((float)(int8_t)v, (float)(int8_t)(v >> 8));
+      const uint32_t p23 = bf16_pair((float)(int8_t)(v >> 16), (float)(int8_t)(v >> 24));
+      a = dot2_bf16(p01, xp[2 * dw], a);
+      if (TWO) a = dot2_bf16(p01, lp[2 * dw], a);
+      a = dot2_bf16(p23, xp[2 * dw + 1], a);
+      if (TWO) a = dot2_bf16(p23, lp[2 * dw + 1], a);
+    }
+    return a;
+  }
+  COLI_DEV static int half_index(int w) { return w; }
+};
+
+template <class C>
+COLI_DEV float codec_bias(const uint32_t p[16]) {
+  if (C::kBias == 0.0f) return 0.0f;
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) s = dot2_bf16(p[q], kBf16Ones, s);
+  return -C::kBias * s;
+}
+template <class C>
+COLI_DEV float codec_bias2(const uint32_t hp[16], const uint32_t lp[16]) {
+  if (C::kBias == 0.0f) return 0.0f;
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    s = dot2_bf16(hp[q], kBf16Ones, s);
+    s = dot2_bf16(lp[q], kBf16Ones, s);
+  }
+  return -C::kBias * s;
 }
 
 // The down GEMV consumes h as bf16 hi + lo halves (16 significant bits),
-// already paired to the nibble order.  Row layout (I values, 4 bytes each):
-// chunk c of 32 values holds 16 hi dwords then 16 lo dwords; dword 4*o + q
-// of a half pairs values 8o + q (low 16 bits) and 8o + q + 4 (high 16 bits).
+// already paired in the codec's order.  Row layout (I values, 4 bytes each):
+// chunk c of 32 values holds 16 hi dwords then 16 lo dwords.
+template <class C>
 COLI_DEV void store_h_pair(float *row, int n, float h) {
   const uint32_t hi = f32_to_bf16_bits(h);
   const uint32_t lo = f32_to_bf16_bits(h - bf16_to_f32(hi));
-  const int c = n >> 5, w = n & 31, o = w >> 3, k = w & 7;
+  const int c = n >> 5;
   uint16_t *base = reinterpret_cast<uint16_t *>(row + 32 * c);
-  const int half = 2 * (4 * o + (k & 3)) + (k >> 2);
+  const int half = C::half_index(n & 31);
   base[half] = (uint16_t)hi;
   base[32 + half] = (uint16_t)lo;
 }
@@ -157,7 +235,7 @@ COLI_DEV void store_h_pair(float *row, int n, float h) {
 // the staging loop and its barriers are uniform over the workgroup.  Dynamic
 // LDS holds tg tokens: tg x 4 x NCH quads of paired bf16, then tg x NCH
 // chunk biases.
-template <int CPL, int RPW, bool ONE>
+template <int CPL, int RPW, bool ONE, class C>
 __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
     Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
     float *__restrict__ h_out) {
@@ -174,8 +252,10 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
   if (!ONE && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
   const Slot sl = slot_of<ONE>(r, L, T, slot);
   const int n0 = (wave % waves_per_slot) * RPW;
-  const uint8_t *qg = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)n0 * (H / 2) + 16 * lane;
-  const uint8_t *qu = qg + (int64_t)I * H / 2;
+  const int64_t row_bytes = C::bytes(H);
+  const uint8_t *qg = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)n0 * row_bytes +
+                      16 * C::Q * lane;
+  const uint8_t *qu = qg + (int64_t)I * row_bytes;
   const uint16_t *sgp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)n0 * (H / 64) + lane / 2;
   const uint16_t *sup = sgp + (int64_t)I * H / 64;
   // One token: this thread's activation chunk (c = threadIdx.x < NCH) is
@@ -187,16 +267,19 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) xpre[dw] = src[dw];
   }
-  uint4 wg[RPW][CPL], wu[RPW][CPL];
+  uint4 wg[RPW][CPL][C::Q], wu[RPW][CPL][C::Q];
   uint16_t sg[RPW][CPL], su[RPW][CPL];
 #pragma unroll
   for (int j = 0; j < RPW; ++j)
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int64_t ob = (int64_t)j * (H / 2) + 1024 * i;
+      const int64_t ob = (int64_t)j * row_bytes + 1024 * C::Q * i;
       const int64_t os = (int64_t)j * (H / 64) + 32 * i;
-      wg[j][i] = *reinterpret_cast<const uint4 *>(qg + ob);
-      wu[j][i] = *reinterpret_cast<const uint4 *>(qu + ob);
+#pragma unroll
+      for (int q = 0; q < C::Q; ++q) {
+        wg[j][i][q] = *reinterpret_cast<const uint4 *>(qg + ob + 16 * q);
+        wu[j][i][q] = *reinterpret_cast<const uint4 *>(qu + ob + 16 * q);
+      }
       sg[j][i] = sgp[os];
       su[j][i] = sup[os];
     }
@@ -219,10 +302,10 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
       for (int dw = 0; dw < 4; ++dw) {
         const uint4 v = ONE ? xpre[dw] : src[dw];
         const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-        x8_to_pairs(d, &p[4 * dw]);
+        C::pairs(d, &p[4 * dw]);
         xs[dw * NCH + c] = make_uint4(p[4 * dw], p[4 * dw + 1], p[4 * dw + 2], p[4 * dw + 3]);
       }
-      xbias[ti * NCH + c] = chunk_bias(p);
+      xbias[ti * NCH + c] = codec_bias<C>(p);
     }
     __syncthreads();
     #pragma unroll 1
@@ -230,10 +313,12 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
 #pragma unroll
       for (int j = 0; j < RPW; ++j)
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          opaque(wg[j][i]);
-          opaque(wu[j][i]);
-        }
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+          for (int q = 0; q < C::Q; ++q) {
+            opaque(wg[j][i][q]);
+            opaque(wu[j][i][q]);
+          }
       const uint4 *xs = smem + ti * 4 * NCH;
       float v[2 * RPW];
 #pragma unroll
@@ -245,8 +330,10 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
         const float nb = xbias[ti * NCH + lane + 64 * i];
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-          v[2 * j] = fmaf(f16_to_f32(sg[j][i]), chunk_dot(wg[j][i], xc.p, nb), v[2 * j]);
-          v[2 * j + 1] = fmaf(f16_to_f32(su[j][i]), chunk_dot(wu[j][i], xc.p, nb), v[2 * j + 1]);
+          v[2 * j] = fmaf(f16_to_f32(sg[j][i]), C::template dot<false>(wg[j][i], xc.p, xc.p, nb),
+                          v[2 * j]);
+          v[2 * j + 1] = fmaf(f16_to_f32(su[j][i]),
+                              C::template dot<false>(wu[j][i], xc.p, xc.p, nb), v[2 * j + 1]);
         }
       }
       // value 2j is the gate of row j, 2j+1 its up; bring them to one lane
@@ -255,7 +342,7 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
       constexpr int kSpan = 64 / (2 * RPW);  // lanes holding one value
       const float up = __shfl_down(tot, kSpan, 64);
       if ((lane % kSpan) == 0 && (vi & 1) == 0)
-        store_h_pair(h_out + (int64_t)(sl.pos0 + g0 + ti) * I, n0 + vi / 2, silu_mul(tot, up));
+        store_h_pair<C>(h_out + (int64_t)(sl.pos0 + g0 + ti) * I, n0 + vi / 2, silu_mul(tot, up));
     }
   }
 }
@@ -271,7 +358,7 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
 // One token: the workgroup requests the token's h row before the weights,
 // stages it in LDS quad-major (quad q of chunk c at q * I/32 + c, so a
 // wavefront's reads are consecutive), and its wavefronts read it from there.
-template <int LPR, int CPL, int RG, bool ONE>
+template <int LPR, int CPL, int RG, bool ONE, class C>
 __global__ void __launch_bounds__(kThreads) down_stream_kernel(
     Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
     float *__restrict__ o_out) {
@@ -299,18 +386,22 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
       if (NQ % kThreads == 0 || qi < NQ) hpre[j] = src[qi];
     }
   }
-  const uint8_t *qd = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)I * H +
-                      (int64_t)(m0 + lr) * (I / 2) + 16 * lc;
+  const int64_t row_bytes = C::bytes(I);
+  const uint8_t *qd = L.q4 + (int64_t)sl.e * L.expert_bytes + C::bytes((int64_t)2 * I * H) +
+                      (int64_t)(m0 + lr) * row_bytes + 16 * C::Q * lc;
   const uint16_t *sdp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64 +
                         (int64_t)(m0 + lr) * (I / 64) + lc / 2;
-  uint4 w[RG][CPL];
+  uint4 w[RG][CPL][C::Q];
   uint16_t sc[RG][CPL];
 #pragma unroll
   for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int64_t row = RPI * j;
-      w[j][i] = *reinterpret_cast<const uint4 *>(qd + row * (I / 2) + 16 * LPR * i);
+#pragma unroll
+      for (int q = 0; q < C::Q; ++q)
+        w[j][i][q] = *reinterpret_cast<const uint4 *>(qd + row * row_bytes + 16 * C::Q * LPR * i +
+                                                      16 * q);
       sc[j][i] = sdp[row * (I / 64) + LPR / 2 * i];
     }
   if (ONE) {
@@ -328,7 +419,9 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
 #pragma unroll
       for (int j = 0; j < RG; ++j)
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) opaque(w[j][i]);
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+          for (int q = 0; q < C::Q; ++q) opaque(w[j][i][q]);
     }
     const int64_t pos = sl.pos0 + ti;
     float v[RG];
@@ -346,23 +439,10 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
         hi.p[4 * q] = a.x, hi.p[4 * q + 1] = a.y, hi.p[4 * q + 2] = a.z, hi.p[4 * q + 3] = a.w;
         lo.p[4 * q] = b.x, lo.p[4 * q + 1] = b.y, lo.p[4 * q + 2] = b.z, lo.p[4 * q + 3] = b.w;
       }
-      const float nb = chunk_bias2(hi.p, lo.p);
+      const float nb = codec_bias2<C>(hi.p, lo.p);
 #pragma unroll
-      for (int j = 0; j < RG; ++j) {
-        const uint32_t wv[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
-        float a = nb;
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          uint32_t p[4];
-          nib8_to_bf16x4(wv[dw], p[0], p[1], p[2], p[3]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            a = dot2_bf16(p[q], hi.p[4 * dw + q], a);
-            a = dot2_bf16(p[q], lo.p[4 * dw + q], a);
-          }
-        }
-        v[j] = fmaf(f16_to_f32(sc[j][i]), a, v[j]);
-      }
+      for (int j = 0; j < RG; ++j)
+        v[j] = fmaf(f16_to_f32(sc[j][i]), C::template dot<true>(w[j][i], hi.p, lo.p, nb), v[j]);
     }
     const float tot = reduce_scatter<RG, LPR>(v, lc);
     constexpr int kSpan = LPR / RG;
@@ -373,10 +453,15 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
 
 constexpr int kMaxStage = 4;  // tokens of one slot staged in LDS at once
 
-template <int CPL>
+// gate/up rows per wavefront: two with int4 codes, one with int8 codes
+// (the same weight registers either way)
+template <class C>
+constexpr int gateup_rpw() { return C::Q == 1 ? 2 : 1; }
+
+template <int CPL, class C>
 hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                       float *h, int nslots, hipStream_t s) {
-  constexpr int RPW = 2;
+  constexpr int RPW = gateup_rpw<C>();
   const int waves = nslots * (L.I / RPW);
   // up to kMaxStage tokens per LDS stage, within 64 KB
   const size_t per_token = (size_t)64 * CPL * (4 * sizeof(uint4) + sizeof(float));
@@ -385,34 +470,81 @@ hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t 
   const size_t lds = tg * per_token;
   const dim3 grid((waves + kWaves - 1) / kWaves);
   if (T == 1)
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, true>, grid, dim3(kThreads),
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, true, C>, grid, dim3(kThreads),
              lds, s, L, r, x, T, tg, h);
   else
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, false>, grid, dim3(kThreads),
-             lds, s, L, r, x, T, tg, h);
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, false, C>, grid,
+             dim3(kThreads), lds, s, L, r, x, T, tg, h);
   return hipGetLastError();
 }
 
 // row groups per wavefront of the down GEMV: about eight 16-byte loads per
-// lane (8 rows of 1 KB when I = 2048)
-template <int LPR, int CPL>
-constexpr int down_rg() { return CPL == 1 ? 8 : (CPL == 2 ? 4 : 2); }
-template <int LPR, int CPL>
-constexpr int down_rows_wave() { return (64 / LPR) * down_rg<LPR, CPL>(); }
+// lane (8 rows of 1 KB of int4 codes when I = 2048; half the rows for int8)
+template <int LPR, int CPL, class C>
+constexpr int down_rg() {
+  return (CPL == 1 ? 8 : (CPL == 2 ? 4 : 2)) / C::Q;
+}
+template <int LPR, int CPL, class C>
+constexpr int down_rows_wave() { return (64 / LPR) * down_rg<LPR, CPL, C>(); }
 
-template <int LPR, int CPL>
+template <int LPR, int CPL, class C>
 hipError_t down_shape(const Layer &L, const coli_moe_route_t &r, int T, const float *h,
                       float *o, int nslots, hipStream_t s) {
-  const int waves = nslots * (L.H / down_rows_wave<LPR, CPL>());
+  const int waves = nslots * (L.H / down_rows_wave<LPR, CPL, C>());
   const dim3 grid((waves + kWaves - 1) / kWaves);
-  constexpr int RG = down_rg<LPR, CPL>();
+  constexpr int RG = down_rg<LPR, CPL, C>();
   if (T == 1)
-    launch_k(COLI_K_DECODE_DOWN, down_stream_kernel<LPR, CPL, RG, true>, grid, dim3(kThreads), 0,
-             s, L, r, T, h, o);
-  else
-    launch_k(COLI_K_DECODE_DOWN, down_stream_kernel<LPR, CPL, RG, false>, grid, dim3(kThreads),
+    launch_k(COLI_K_DECODE_DOWN, down_stream_kernel<LPR, CPL, RG, true, C>, grid, dim3(kThreads),
              0, s, L, r, T, h, o);
+  else
+    launch_k(COLI_K_DECODE_DOWN, down_stream_kernel<LPR, CPL, RG, false, C>, grid,
+             dim3(kThreads), 0, s, L, r, T, h, o);
   return hipGetLastError();
+}
+
+// Shape of the streaming path for this layer, or false if it has none.
+template <class C>
+bool stream_shape(const Layer &L, int &lpr, int &cpl) {
+  const int hc = L.H / 2048;
+  if (L.H % 2048 || hc < 1 || hc > 4) return false;
+  int rows_wave;
+  if (L.I == 512) {
+    lpr = 16, cpl = 1, rows_wave = down_rows_wave<16, 1, C>();
+  } else if (L.I == 1024) {
+    lpr = 32, cpl = 1, rows_wave = down_rows_wave<32, 1, C>();
+  } else if (L.I % 2048 == 0 && L.I / 2048 <= 4) {
+    lpr = 64, cpl = L.I / 2048;
+    rows_wave = cpl == 1 ? down_rows_wave<64, 1, C>() : cpl == 2 ? down_rows_wave<64, 2, C>()
+                : cpl == 3 ? down_rows_wave<64, 3, C>() : down_rows_wave<64, 4, C>();
+  } else {
+    return false;
+  }
+  return L.I % 8 == 0 && L.H % rows_wave == 0;
+}
+
+template <class C>
+bool launch_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                   float *h, float *o, hipStream_t s, hipError_t *err) {
+  int lpr, cpl;
+  if (T > kMaxStreamT || !stream_shape<C>(L, lpr, cpl)) return false;
+  const int nslots = max_union(L, T) + L.S;
+  hipError_t e = hipSuccess;
+  switch (L.H / 2048) {
+    case 1: e = gateup_cpl<1, C>(L, r, x, T, h, nslots, s); break;
+    case 2: e = gateup_cpl<2, C>(L, r, x, T, h, nslots, s); break;
+    case 3: e = gateup_cpl<3, C>(L, r, x, T, h, nslots, s); break;
+    default: e = gateup_cpl<4, C>(L, r, x, T, h, nslots, s); break;
+  }
+  if (e == hipSuccess) {
+    if (lpr == 16) e = down_shape<16, 1, C>(L, r, T, h, o, nslots, s);
+    else if (lpr == 32) e = down_shape<32, 1, C>(L, r, T, h, o, nslots, s);
+    else if (cpl == 1) e = down_shape<64, 1, C>(L, r, T, h, o, nslots, s);
+    else if (cpl == 2) e = down_shape<64, 2, C>(L, r, T, h, o, nslots, s);
+    else if (cpl == 3) e = down_shape<64, 3, C>(L, r, T, h, o, nslots, s);
+    else e = down_shape<64, 4, C>(L, r, T, h, o, nslots, s);
+  }
+  *err = e;
+  return true;
 }
 
 }  // namespace
@@ -423,40 +555,14 @@ hipError_t down_shape(const Layer &L, const coli_moe_route_t &r, int T, const fl
 // Returns false, launching nothing, otherwise.
 bool launch_decode_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                           float *h, float *o, hipStream_t s, hipError_t *err) {
+  return L.w8 ? launch_stream<CodecI8>(L, r, x, T, h, o, s, err)
+              : launch_stream<CodecI4>(L, r, x, T, h, o, s, err);
+}
+
+bool decode_stream_supported(const Layer &L, int T) {
+  int lpr, cpl;
   if (T > kMaxStreamT) return false;
-  const int nslots = max_union(L, T) + L.S;
-  const int hc = L.H / 2048;
-  if (L.H % 2048 || hc < 1 || hc > 4) return false;
-  int lpr, cpl, rows_wave;
-  if (L.I == 512) {
-    lpr = 16, cpl = 1, rows_wave = down_rows_wave<16, 1>();
-  } else if (L.I == 1024) {
-    lpr = 32, cpl = 1, rows_wave = down_rows_wave<32, 1>();
-  } else if (L.I % 2048 == 0 && L.I / 2048 <= 4) {
-    lpr = 64, cpl = L.I / 2048;
-    rows_wave = cpl == 1 ? down_rows_wave<64, 1>() : cpl == 2 ? down_rows_wave<64, 2>()
-                : cpl == 3 ? down_rows_wave<64, 3>() : down_rows_wave<64, 4>();
-  } else {
-    return false;
-  }
-  if (L.I % 8 || L.H % rows_wave) return false;
-  hipError_t e = hipSuccess;
-  switch (hc) {
-    case 1: e = gateup_cpl<1>(L, r, x, T, h, nslots, s); break;
-    case 2: e = gateup_cpl<2>(L, r, x, T, h, nslots, s); break;
-    case 3: e = gateup_cpl<3>(L, r, x, T, h, nslots, s); break;
-    default: e = gateup_cpl<4>(L, r, x, T, h, nslots, s); break;
-  }
-  if (e == hipSuccess) {
-    if (lpr == 16) e = down_shape<16, 1>(L, r, T, h, o, nslots, s);
-    else if (lpr == 32) e = down_shape<32, 1>(L, r, T, h, o, nslots, s);
-    else if (cpl == 1) e = down_shape<64, 1>(L, r, T, h, o, nslots, s);
-    else if (cpl == 2) e = down_shape<64, 2>(L, r, T, h, o, nslots, s);
-    else if (cpl == 3) e = down_shape<64, 3>(L, r, T, h, o, nslots, s);
-    else e = down_shape<64, 4>(L, r, T, h, o, nslots, s);
-  }
-  *err = e;
-  return true;
+  return L.w8 ? stream_shape<CodecI8>(L, lpr, cpl) : stream_shape<CodecI4>(L, lpr, cpl);
 }
 
 }  // namespace coli

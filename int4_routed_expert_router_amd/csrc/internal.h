@@ -17,7 +17,8 @@ struct Layer {
   float routed_scale;
   const uint8_t *q4;
   const uint16_t *scales;
-  int64_t expert_bytes;   // 3*I*H/2
+  int w8;                 // 0: int4 nibble codes, 1: int8 byte codes
+  int64_t expert_bytes;   // 3*I*H/2 (int4) or 3*I*H (int8)
   int64_t expert_scales;  // 3*I*H/64
 };
 
@@ -51,6 +52,8 @@ int launch_router_logits(const Layer &L, const uint16_t *w, const uint16_t *x, i
 constexpr int kMaxStreamT = 16;
 bool launch_decode_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                           float *h, float *o, hipStream_t s, hipError_t *err);
+// Whether launch_decode_stream has a path for this layer and batch.
+bool decode_stream_supported(const Layer &L, int T);
 void launch_combine(const float *o, const coli_moe_route_t &r, int T, int H, int k, int S,
                     void *y, int y_dtype, hipStream_t s);
 int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *d,

@@ -62,7 +62,7 @@ def oracle_layer(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarray, top
     xb = synth.bf16_bits(x)[tokens]
     fn = oracle.forward_decode if entry == "decode" else oracle.forward_prefill
     return fn(spec.hidden, spec.inter, len(used), spec.n_shared, spec.top_k, q4h, sch,
-              remap[idx], w, xb)
+              remap[idx], w, xb, int8_weights=spec.int8)
 
 
 def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
