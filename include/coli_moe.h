@@ -114,7 +114,9 @@ enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
  * not give its scale granularity, read here as the same gs64.  int8 layers
  * run in coli_moe_forward_decode when the shape has the streaming path
  * (H a multiple of 2048 up to 8192; I in {512, 1024} or a multiple of 2048
- * up to 8192) and T <= 16; other calls return COLI_E_UNSUPPORTED.
+ * up to 8192) and T <= 16, and in coli_moe_forward_prefill and
+ * coli_moe_block_dots when H and I (the reduction length) are multiples of
+ * 256; other calls return COLI_E_UNSUPPORTED.
  */
 typedef struct coli_moe_layer {
   int32_t hidden;        /* H */

@@ -176,7 +176,8 @@ struct Stage {
 };
 
 struct GemmArgs {
-  const uint8_t *wq;       // nibble matrix base (rows x K/2)
+  const uint8_t *wq;       // code matrix base (rows x K >> rs bytes)
+  int rs;                  // row bytes = K >> rs: 1 for int4 codes, 0 for int8
   const uint16_t *ws;      // its scales (rows x K/64)
   int rows;                // rows of this matrix (I or H)
   int K;                   // reduction length
@@ -203,7 +204,7 @@ COLI_DEV void weight_row(const GemmArgs &g, int n0, int r, const uint8_t *&q,
     n = n0 + r;
   }
   const int nn = n < g.rows ? n : 0;
-  q = g.wq + oq + (int64_t)nn * (g.K / 2);
+  q = g.wq + oq + (int64_t)nn * (g.K >> g.rs);
   s = g.ws + os + (int64_t)nn * (g.K / 64);
 }
 
@@ -595,15 +596,23 @@ struct Src4 {
   const uint16_t *s;
   int s_group;  // scale elements per group: 4 (a weight row) or 8 (a token)
 };
+// W8: int8 codes, 256 bytes of a row per stage instead of 128, so each of
+// the four weight loads is a pair of 16-byte loads (both halves of one
+// 32-block); the stage holds the codes as they are.
+template <bool W8>
 struct Group4 {
-  uint4 w[4], a[4];
+  uint4 w[4][W8 ? 2 : 1], a[4];
   uint2 s;
 };
 
-COLI_DEV void load_group(const Src4 &src, int gi, Group4 &G) {
+template <bool W8>
+COLI_DEV void load_group(const Src4 &src, int gi, Group4<W8> &G) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    G.w[j] = *reinterpret_cast<const uint4 *>(src.wbase + (src.w[j] + gi * 128));
+#pragma unroll
+    for (int h = 0; h < (W8 ? 2 : 1); ++h)
+      G.w[j][h] = *reinterpret_cast<const uint4 *>(src.wbase +
+                                                   (src.w[j] + gi * (W8 ? 256 : 128) + 16 * h));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     G.a[j] = *reinterpret_cast<const uint4 *>(src.abase + (src.a[j] + gi * 256));
@@ -613,15 +622,24 @@ COLI_DEV void load_group(const Src4 &src, int gi, Group4 &G) {
 // Registers -> LDS.  Within each half-wavefront the 8-byte writes land on
 // distinct banks: lane bits 0-1 pick consecutive entries and the (step,
 // block) pair moves the address by a multiple of 4 entries (mod 32).
-template <int MODE>
-COLI_DEV void store_group(const Group4 &G, Stage4 &st, int wid) {
+template <int MODE, bool W8>
+COLI_DEV void store_group(const Group4<W8> &G, Stage4 &st, int wid) {
   const int l = threadIdx.x & 63;
   {
     const int c = (l >> 2) & 7, s = c >> 1, b = c & 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rt = 2 * wid + (j >> 1), rr = 8 * (j & 1) + 4 * (l >> 5) + (l & 3);
-      const uint32_t w[4] = {G.w[j].x, G.w[j].y, G.w[j].z, G.w[j].w};
+      if (W8) {  // k-quarters 2h and 2h + 1 of the 32-block
+#pragma unroll
+        for (int h = 0; h < (W8 ? 2 : 1); ++h) {
+          const uint4 v = G.w[j][h];
+          st.w[rt][s][b][(rr + 16 * (2 * h)) ^ swz(s, b)] = make_uint2(v.x, v.y);
+          st.w[rt][s][b][(rr + 16 * (2 * h + 1)) ^ swz(s, b)] = make_uint2(v.z, v.w);
+        }
+        continue;
+      }
+      const uint32_t w[4] = {G.w[j][0].x, G.w[j][0].y, G.w[j][0].z, G.w[j][0].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t even = (w[i] << 4) & 0xf0f0f0f0u;  // k 0,2,4,6 (x16)
@@ -649,15 +667,16 @@ COLI_DEV void store_group(const Group4 &G, Stage4 &st, int wid) {
 #pragma unroll
     for (int s = 0; s < kGroup; ++s) st.sw[s][t] = f16_to_f32(h[s]);
   } else {  // token (t-128)/2: steps 2*(t&1) and 2*(t&1)+1, two blocks each
+    // int4 codes sit in the stage x16: their activation scales carry 1/16
+    constexpr float f = W8 ? 1.0f : 0.0625f;
     const int m = (t - BR) >> 1, s0 = 2 * (t & 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      st.sa[s0 + u][m] =
-          make_float2(f16_to_f32(h[2 * u]) * 0.0625f, f16_to_f32(h[2 * u + 1]) * 0.0625f);
+      st.sa[s0 + u][m] = make_float2(f16_to_f32(h[2 * u]) * f, f16_to_f32(h[2 * u + 1]) * f);
   }
 }
 
-template <int MODE>
+template <int MODE, bool W8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
              const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
@@ -696,7 +715,7 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
       for (int j = 0; j < 4; ++j) {
         const uint8_t *q;
         weight_row<MODE>(ge, it.n0, 32 * wid + 8 * j + 4 * (lane >> 5) + (lane & 3), q, unused);
-        src.w[j] = (uint32_t)(q - ge.wq) + 16 * ((lane >> 2) & 7);
+        src.w[j] = (uint32_t)(q - ge.wq) + (W8 ? 32 : 16) * ((lane >> 2) & 7);
         const int m = 16 * wid + 4 * j + (lane & 3);
         const int c = 4 * ((lane >> 2) & 3) + 2 * ((lane >> 4) & 1) + (lane >> 5);
         src.a[j] = (uint32_t)rowid[m] * (uint32_t)ge.K + 16 * c;
@@ -774,7 +793,7 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
               const int n = it.n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
               if (n >= g.rows) continue;
               dots_out[((int64_t)(it.row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks + blk] =
-                  (d[a * 2 + ms][i] - (int)kMagic) >> 4;
+                  (d[a * 2 + ms][i] - (int)kMagic) >> (W8 ? 0 : 4);
             }
           }
       } else {
@@ -813,16 +832,16 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
       }
     };
 
-    Group4 grp;
+    Group4<W8> grp;
     load_group(src, 0, grp);
-    store_group<MODE>(grp, st, wid);
+    store_group<MODE, W8>(grp, st, wid);
     __syncthreads();
     if (ngroups > 1) load_group(src, 1, grp);
     for (int gi = 0; gi < ngroups; ++gi) {
       compute_stage(gi);
       if (gi + 1 < ngroups) {
         __syncthreads();  // every wavefront is done with the stage
-        store_group<MODE>(grp, st, wid);
+        store_group<MODE, W8>(grp, st, wid);
         __syncthreads();
         if (gi + 2 < ngroups) load_group(src, gi + 2, grp);
       }
@@ -906,26 +925,32 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.ws = L.scales;
     g.rows = L.I;
     g.K = L.H;
+    g.rs = L.w8 ? 0 : 1;
     g.act = w.qx;
     g.act_d = w.dx;
-    g.up_offset_q = (int64_t)L.I * L.H / 2;
+    g.up_offset_q = ((int64_t)L.I * L.H) >> g.rs;
     g.up_offset_s = (int64_t)L.I * L.H / 64;
     const int nn = (L.I + 63) / 64;
-    launch_k(COLI_K_GEMM_GATEUP, L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp>,
+    launch_k(COLI_K_GEMM_GATEUP,
+             L.w8 ? gemm4_kernel<kGateUp, true>
+                  : (L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp, false>),
              dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh, nullptr, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
   }
   {  // down
     GemmArgs g{};
-    g.wq = L.q4 + (int64_t)L.I * L.H;
+    g.rs = L.w8 ? 0 : 1;
+    g.wq = L.q4 + (((int64_t)2 * L.I * L.H) >> g.rs);
     g.ws = L.scales + (int64_t)2 * L.I * L.H / 64;
     g.rows = L.H;
     g.K = L.I;
     g.act = w.qh;
     g.act_d = w.dh;
     const int nn = (L.H + BR - 1) / BR;
-    launch_k(COLI_K_GEMM_DOWN, L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown>,
+    launch_k(COLI_K_GEMM_DOWN,
+             L.w8 ? gemm4_kernel<kDown, true>
+                  : (L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown, false>),
              dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr, nullptr, w.o, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
@@ -937,7 +962,8 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
 int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_act, int T,
                       int32_t *dots, hipStream_t s) {
   GemmArgs g{};
-  const int64_t moff = (int64_t)matrix * L.I * L.H / 2;
+  g.rs = L.w8 ? 0 : 1;
+  const int64_t moff = ((int64_t)matrix * L.I * L.H) >> g.rs;
   g.wq = L.q4 + moff;
   g.ws = L.scales + (int64_t)matrix * L.I * L.H / 64;
   g.rows = matrix == 2 ? L.H : L.I;
@@ -947,7 +973,9 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
   const int nn = (g.rows + BR - 1) / BR;
   const int ntile = (T + BM - 1) / BM;
   coli_moe_route_t none{};
-  launch_k(COLI_K_BLOCK_DOTS, g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots>,
+  launch_k(COLI_K_BLOCK_DOTS,
+           L.w8 ? gemm4_kernel<kDots, true>
+                : (g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots, false>),
            dim3(grid_for(band_items_host(ntile, nn))),
            dim3(kThreads), 0, s, g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes,
            L.expert_scales, nullptr, nullptr, nullptr, dots);

@@ -83,3 +83,85 @@ def bf16_ulp_distance(y_bf16: torch.Tensor, ref: np.ndarray) -> int:
     a = torch.where(a < 0, -(a & 0x7FFF), a)
     b = torch.where(b < 0, -(b & 0x7FFF), b)
     return int((a - b).abs().max())
+
+
+def prefill_flip_budget(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarray,
+                        topk_w: np.ndarray, x: torch.Tensor, tokens, band=1e-5):
+    """Oracle prefill output of `tokens` and, per output element, the most that
+    Q8_0 decisions of h sitting on a rounding boundary can move it.
+
+    The integer path quantises h (fp32) to Q8_0 on both sides; the GPU's h
+    differs from the oracle's by fp32 rounding-order ulps, so a code whose
+    h / d lies within `band` (absolute, in code units, plus 2^-19 relative,
+    about 16 ulps) of a .5 boundary may round the other way, and a block
+    whose fp32 scale lies within 2^-19 of an fp16 tie may store the
+    neighbouring fp16 scale.  A
+    code change of 1 moves down output m by at most d * |W_down[m, n]|; a
+    scale change by one fp16 step moves it by at most 2^-10 * |q d W[m, n]|
+    summed over the block.  Returns (ref [len(tokens), H], budget [same]).
+    """
+    tokens = list(tokens)
+    H, I, k, S = spec.hidden, spec.inter, spec.top_k, spec.n_shared
+    idx = topk_idx.reshape(-1, k)[tokens]
+    w = topk_w.reshape(-1, k)[tokens]
+    used = sorted(set(int(e) for e in idx.ravel()))
+    experts = used + ([spec.n_experts] if S else [])
+    q4h, sch = synth.expert_slice(spec, L.q4, L.scales, experts)
+    remap = np.zeros(spec.n_experts, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    xb = synth.bf16_bits(x)[tokens]
+    ref, h = oracle.forward_prefill(H, I, len(used), S, k, q4h, sch, remap[idx], w, xb,
+                                    want_h=True, int8_weights=spec.int8)
+    mb = I * H if spec.int8 else I * H // 2
+    eb, es = 3 * mb, 3 * I * H // 64
+    scf = sch.view(np.float16).astype(np.float64)
+    budget = np.zeros((len(tokens), H))
+    for ti in range(len(tokens)):
+        for j in range(k + S):
+            le = int(remap[idx[ti, j]]) if j < k else len(used)
+            wj = float(np.float32(w[ti, j])) if j < k else 1.0
+            hv = h[ti, j].astype(np.float32).reshape(I // 32, 32)
+            amax = np.abs(hv).max(axis=1)
+            d32 = (amax / np.float32(127.0)).astype(np.float32)
+            safe = np.where(d32 == 0, np.float32(1.0), d32)
+            ratio = np.abs((hv / safe[:, None]).astype(np.float32)).astype(np.float64)
+            frac = ratio - np.floor(ratio)
+            code_risk = np.abs(frac - 0.5) < band + 2.0 ** -19 * ratio
+            d16 = d32.astype(np.float16).astype(np.float64)
+            up = np.nextafter(d32.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+            dn = np.nextafter(d32.astype(np.float16), np.float16(0)).astype(np.float64)
+            nb = np.where(d32 >= d16, up, dn)
+            scale_risk = np.abs(d32 - (d16 + nb) / 2) < 2.0 ** -19 * d32
+            # per column n: the most a decision there moves o[m] / |W_down[m, n]|
+            q = np.floor(ratio + 0.5)
+            col = (code_risk * d16[:, None]
+                   + scale_risk[:, None] * 2.0 ** -10 * q * d16[:, None]).reshape(I)
+            cols = np.flatnonzero(col)
+            if cols.size == 0:
+                continue
+            base = le * eb + 2 * mb
+            if spec.int8:
+                rows = np.asarray(q4h[base:base + mb], np.uint8).view(np.int8).reshape(H, I)
+                wq = rows[:, cols].astype(np.float64)
+            else:
+                b = np.asarray(q4h[base:base + mb], np.uint8).reshape(H, I // 2)[:, cols // 2]
+                nib = np.where(cols % 2 == 1, b >> 4, b & 15).astype(np.int64)
+                wq = np.where(nib >= 8, nib - 16, nib).astype(np.float64)
+            s = scf[le * es + 2 * (I * H // 64):le * es + 3 * (I * H // 64)].reshape(H, I // 64)
+            wabs = np.abs(wq) * s[:, cols // 64]
+            budget[ti] += wj * (wabs @ col[cols])
+    return ref, budget
+
+
+def check_prefill_output(spec, L, g, x, y, tokens, tol=REL_TOL):
+    """|y - ref| <= tol * max(|ref|, rms of ref's row) + the Q8_0 boundary
+    budget of prefill_flip_budget, element by element.  Returns the plain
+    metric and the number of elements that needed budget."""
+    tokens = list(tokens)
+    ref, budget = prefill_flip_budget(spec, L, g["topk_idx"], g["topk_w"], x, tokens)
+    yv = y.float().cpu().numpy()[tokens].astype(np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    denom = np.maximum(np.abs(ref), rms)
+    err = np.abs(yv - ref)
+    assert np.all(err <= tol * denom + budget), float(np.max((err - budget) / denom))
+    return rel_err(yv, ref), int(np.count_nonzero(err > tol * denom))
