@@ -27,6 +27,7 @@ Prints ONE JSON line.  Inputs are synthetic (seeded generator module
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -272,7 +273,8 @@ def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=N
     nbytes = statistics.mean(union_bytes(spec, stack.logits[r], spec.top_k)
                              for r in range(len(stack.logits)))
     gbps = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": name, "path": "decode", "tokens": T, "layers": layers,
+    return {"workload": name, "path": "decode", "weights": "int8" if spec.int8 else "int4",
+            "tokens": T, "layers": layers,
             "ms_per_step": round(ms, 4), "tokens_per_s": round(T * layers / (ms * 1e-3), 1),
             "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
@@ -311,7 +313,8 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
     nbytes = union_bytes(spec, [lg], spec.top_k)
     ops = 2.0 * 3 * spec.hidden * spec.inter * T * (spec.top_k + spec.n_shared)
     gemm_us = sum(kern.get(k, {"avg_us": 0})["avg_us"] for k in ("gemm_gateup", "gemm_down"))
-    out = {"workload": name, "path": "prefill", "tokens": T, "ms_per_step": round(ms, 4),
+    out = {"workload": name, "path": "prefill",
+           "weights": "int8" if spec.int8 else "int4", "tokens": T, "ms_per_step": round(ms, 4),
            "tokens_per_s": round(T / (ms * 1e-3), 1),
            "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
            "int8_frac": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -506,6 +509,15 @@ def main():
         ow = synth.WORKLOADS["olmoe"]
         secondary.append(secondary_decode("olmoe_decode_T1", ow.spec, 1, 0.0, 4, 200, 10))
         secondary.append(secondary_prefill("olmoe_prefill_T512", ow.spec, 512, 0.0, 20, 3, copies=4))
+        # int8-weight experts: the OLMoE-style int8 container, and a GLM-shaped
+        # MTP layer (int8 experts) verifying a 4-token draft
+        o8 = dataclasses.replace(ow.spec, int8=True)
+        secondary.append(secondary_decode("olmoe_int8_decode_T1", o8, 1, 0.0, 4, 200, 10))
+        secondary.append(secondary_prefill("olmoe_int8_prefill_T512", o8, 512, 0.0, 20, 3,
+                                           copies=4))
+        g8 = dataclasses.replace(w.spec, int8=True)
+        secondary.append(secondary_decode("glm_mtp_int8_decode_T4", g8, 4, w.zipf_alpha, 2,
+                                          50, 5))
         aw = synth.WORKLOADS["a3b"]
         for t in aw.tokens:
             secondary.append(secondary_decode("a3b_decode_T%d" % t, aw.spec, t, aw.zipf_alpha, 4,
