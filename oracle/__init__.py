@@ -155,35 +155,44 @@ def router_logits(w_bf16, x_bf16):
     return out
 
 
-def forward_decode(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, int8_weights=False):
+WEIGHT_FORMATS = {"int4": 0, "int8": 1, "mxfp4": 2}
+
+
+def _weights(q4, scales, weights):
+    """Codes as bytes and scales as fp16 bits (int4, int8) or E8M0 bytes (mxfp4)."""
+    fmt = WEIGHT_FORMATS[weights]
+    return _c(q4, np.uint8), _c(scales, np.uint8 if weights == "mxfp4" else np.uint16), fmt
+
+
+def forward_decode(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, weights="int4"):
     """Decode-mode layer output, fp64 [T, H].  x_bf16: uint16 bits [T, H].
-    int8_weights: the container holds one int8 byte per weight (else nibbles)."""
+    weights: "int4" (nibbles + fp16 per 64), "int8" (bytes + fp16 per 64) or
+    "mxfp4" (E2M1 nibbles + E8M0 byte per 32)."""
     lib = _load()
-    q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
+    q4, scales, fmt = _weights(q4, scales, weights)
     topk_idx, topk_w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
     x = _c(x_bf16, np.uint16)
     T = x.shape[0]
     y = np.zeros((T, H), np.float64)
     rc = lib.oracle_forward_decode(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
-                                   _ptr(topk_w), _ptr(x), T, _ptr(y), int(bool(int8_weights)))
+                                   _ptr(topk_w), _ptr(x), T, _ptr(y), fmt)
     if rc != 0:
         raise ValueError("oracle_forward_decode failed")
     return y
 
 
 def forward_prefill(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, want_h=False,
-                    int8_weights=False):
+                    weights="int4"):
     """Integer-path (Q8_0) layer output, fp64 [T, H] (and fp32 h [T, k+S, I])."""
     lib = _load()
-    q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
+    q4, scales, fmt = _weights(q4, scales, weights)
     topk_idx, topk_w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
     x = _c(x_bf16, np.uint16)
     T = x.shape[0]
     y = np.zeros((T, H), np.float64)
     h = np.zeros((T, k + S, I), np.float32) if want_h else None
     rc = lib.oracle_forward_prefill(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
-                                    _ptr(topk_w), _ptr(x), T, _ptr(y), _ptr(h),
-                                    int(bool(int8_weights)))
+                                    _ptr(topk_w), _ptr(x), T, _ptr(y), _ptr(h), fmt)
     if rc != 0:
         raise ValueError("oracle_forward_prefill failed")
     return (y, h) if want_h else y
@@ -200,17 +209,18 @@ def quantize_q8_0(v):
     return q, d
 
 
-def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act, int8_weights=False):
-    """Exact int32 block dots [T, rows, K/32] of one matrix of one expert."""
+def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act, weights="int4"):
+    """Exact int32 block dots [T, rows, K/32] of one matrix of one expert
+    (mxfp4: of the doubled E2M1 values, integers in [-12, 12])."""
     lib = _load()
-    q4, scales = _c(q4, np.uint8), _c(scales, np.uint16)
+    q4, scales, fmt = _weights(q4, scales, weights)
     q_act = _c(q_act, np.int8)
     K = I if matrix == 2 else H
     rows = H if matrix == 2 else I
     T = q_act.reshape(-1, K).shape[0]
     dots = np.zeros((T, rows, K // 32), np.int32)
     rc = lib.oracle_block_dots(H, I, E, S, _ptr(q4), _ptr(scales), expert, matrix,
-                               _ptr(q_act), T, _ptr(dots), int(bool(int8_weights)))
+                               _ptr(q_act), T, _ptr(dots), fmt)
     if rc != 0:
         raise ValueError("oracle_block_dots: invalid arguments")
     return dots

@@ -18,6 +18,9 @@
  *    and section; the OLMoE container is int8, ai-tools-nav review, model
  *    family table): read as the same container with one two's-complement
  *    byte per weight in place of a nibble, the same fp16 scale per 64.
+ *  - fp4 experts (the Kimi K3 and DeepSeek V4 rows of the ai-tools-nav
+ *    model family table): read as OCP MXFP4 -- FP4 E2M1 codes packed two
+ *    per byte like the int4 nibbles, one E8M0 scale byte per 32 weights.
  *  - three matrices gate/up/down per expert, each distinct expert read once
  *    per batch: same post, section "几个关键工程动作".
  *  - Q8_0-style int8 activations on the integer path: alphamatch.ai blog
@@ -98,39 +101,64 @@ static int or_nib(uint8_t byte, int high) {
   return v >= 8 ? v - 16 : v;
 }
 
-/* weight q[n][k] of a row-major code matrix.  int4 (w8 == 0): rows hold
- * K/2 bytes, byte k/2, low nibble for even k, high nibble for odd k.
- * int8 (w8 == 1): rows hold K bytes, byte k, two's complement. */
-static int or_q(const uint8_t *mat, int64_t K, int64_t n, int64_t k, int w8) {
-  if (w8) return (int)(int8_t)mat[n * K + k];
-  return or_nib(mat[n * (K / 2) + k / 2], (int)(k & 1));
+/* weight formats of the container */
+#define OR_INT4 0  /* nibble codes, fp16 scale per 64 */
+#define OR_INT8 1  /* byte codes, fp16 scale per 64 */
+#define OR_FP4 2   /* MXFP4: E2M1 nibbles, E8M0 scale byte per 32 */
+
+/* FP4 E2M1 value of a nibble (OCP microscaling formats): bit 3 sign, bits
+ * 2-1 exponent e with bias 1, bit 0 mantissa m; e = 0 is subnormal:
+ * m / 2; otherwise 2^(e-1) * (1 + m/2).  Values 0, .5, 1, 1.5, 2, 3, 4, 6. */
+static double or_e2m1(int nib) {
+  const int e = (nib >> 1) & 3, m = nib & 1;
+  const double v = e ? ldexp(1.0 + 0.5 * m, e - 1) : 0.5 * m;
+  return (nib & 8) ? -v : v;
 }
 
-/* scale s[n][k/64] of a matrix whose rows hold K/64 fp16 scales. */
-static double or_s(const uint16_t *sc, int64_t K, int64_t n, int64_t k) {
-  return or_f16(sc[n * (K / 64) + k / 64]);
+/* integer code of weight [n][k] of a row-major code matrix.
+ *  int4: rows hold K/2 bytes, byte k/2, low nibble for even k, high nibble
+ *        for odd k, two's complement.
+ *  int8: rows hold K bytes, byte k, two's complement.
+ *  fp4:  nibbles placed as for int4; the code is twice the E2M1 value, an
+ *        integer in [-12, 12] (its scale below carries the 1/2). */
+static int or_q(const uint8_t *mat, int64_t K, int64_t n, int64_t k, int fmt) {
+  if (fmt == OR_INT8) return (int)(int8_t)mat[n * K + k];
+  const uint8_t byte = mat[n * (K / 2) + k / 2];
+  if (fmt == OR_FP4) return (int)(2.0 * or_e2m1((k & 1) ? byte >> 4 : byte & 15));
+  return or_nib(byte, (int)(k & 1));
+}
+
+/* scale of weight [n][k] of a matrix: fp16 s[n][k/64] (int4, int8), or for
+ * fp4 the E8M0 byte E[n][k/32] as 2^(E-127), halved. */
+static double or_s(const uint8_t *sc, int64_t K, int64_t n, int64_t k, int fmt) {
+  if (fmt == OR_FP4) return ldexp(1.0, (int)sc[n * (K / 32) + k / 32] - 128);
+  return or_f16(((const uint16_t *)sc)[n * (K / 64) + k / 64]);
 }
 
 /* --------------------------------------------------------------- container */
 
 typedef struct {
   int64_t H, I, E, S;
-  const uint8_t *q4;      /* host copy of the container */
-  const uint16_t *scales; /* host copy, fp16 bits */
-  int w8;                 /* 0: int4 nibbles, 1: int8 bytes */
+  const uint8_t *q4;     /* host copy of the container's codes */
+  const uint8_t *scales; /* host copy of its scales (fp16 bits or E8M0) */
+  int fmt;               /* OR_INT4, OR_INT8 or OR_FP4 */
 } or_layer;
 
 /* matrix m (0 gate, 1 up, 2 down) of expert e: code base and scale base.
- * A matrix holds I*H codes: I*H/2 bytes (int4) or I*H bytes (int8).  Expert
- * e occupies three matrices and 3*I*H/64 scales, matrices in order. */
+ * A matrix holds I*H codes: I*H/2 bytes (int4, fp4) or I*H bytes (int8),
+ * and I*H/64 fp16 scales (int4, int8) or I*H/32 E8M0 bytes (fp4).  Expert e
+ * occupies three matrices of codes and three of scales, in order. */
 static int64_t or_mat_bytes(const or_layer *L) {
-  return L->w8 ? L->I * L->H : L->I * L->H / 2;
+  return L->fmt == OR_INT8 ? L->I * L->H : L->I * L->H / 2;
+}
+static int64_t or_sc_bytes(const or_layer *L) {  /* the same for every format */
+  return L->fmt == OR_FP4 ? L->I * L->H / 32 : 2 * (L->I * L->H / 64);
 }
 static const uint8_t *or_mat(const or_layer *L, int64_t e, int m) {
   return L->q4 + e * 3 * or_mat_bytes(L) + (int64_t)m * or_mat_bytes(L);
 }
-static const uint16_t *or_sc(const or_layer *L, int64_t e, int m) {
-  return L->scales + e * (3 * L->I * L->H / 64) + (int64_t)m * (L->I * L->H / 64);
+static const uint8_t *or_sc(const or_layer *L, int64_t e, int m) {
+  return L->scales + e * 3 * or_sc_bytes(L) + (int64_t)m * or_sc_bytes(L);
 }
 
 /* --------------------------------------------------------- router logits */
@@ -248,19 +276,20 @@ static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
                        double *o) {
   const int64_t H = L->H, I = L->I;
   const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
-  const uint16_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  const uint8_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  const int f = L->fmt;
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t k = 0; k < H; ++k) {
-      g += (double)or_q(qg, H, n, k, L->w8) * or_s(sg, H, n, k) * x[k];
-      u += (double)or_q(qu, H, n, k, L->w8) * or_s(su, H, n, k) * x[k];
+      g += (double)or_q(qg, H, n, k, f) * or_s(sg, H, n, k, f) * x[k];
+      u += (double)or_q(qu, H, n, k, f) * or_s(su, H, n, k, f) * x[k];
     }
     h[n] = or_silu(g) * u;
   }
   for (int64_t m = 0; m < H; ++m) {
     double acc = 0.0;
     for (int64_t n = 0; n < I; ++n)
-      acc += (double)or_q(qd, I, m, n, L->w8) * or_s(sd, I, m, n) * h[n];
+      acc += (double)or_q(qd, I, m, n, f) * or_s(sd, I, m, n, f) * h[n];
     o[m] = acc;
   }
 }
@@ -270,13 +299,13 @@ static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
  * Each token is computed on its own, so the batch union (which only changes
  * how often weights are read) does not appear here. */
 int oracle_forward_decode(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
-                          const uint8_t *q4, const uint16_t *scales,
+                          const uint8_t *q4, const void *scales,
                           const int32_t *topk_idx, const float *topk_w,
-                          const uint16_t *x_bf16, int64_t T, double *y, int32_t w8) {
+                          const uint16_t *x_bf16, int64_t T, double *y, int32_t fmt) {
   if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1 ||
-      (w8 != 0 && w8 != 1))
+      fmt < OR_INT4 || fmt > OR_FP4)
     return OR_EINVAL;
-  or_layer L = {H, I, E, S, q4, scales, w8};
+  or_layer L = {H, I, E, S, q4, (const uint8_t *)scales, fmt};
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t t = 0; t < T; ++t) {
@@ -381,29 +410,29 @@ int oracle_quantize_int4_gs64(const float *w, int64_t rows, int64_t K, uint8_t *
 
 /* Exact int32 dot of one 32-block: weights of row n of a code matrix
  * against int8 activations a[K], over k in [32b, 32b+32). */
-static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n, int w8,
+static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n, int fmt,
                             const int8_t *a, int64_t b) {
   int32_t acc = 0;
   for (int64_t k = 32 * b; k < 32 * b + 32; ++k)
-    acc += or_q(mat, K, n, k, w8) * (int32_t)a[k];
+    acc += or_q(mat, K, n, k, fmt) * (int32_t)a[k];
   return acc;
 }
 
 /* dots[t][n][b] for matrix m (0 gate, 1 up, 2 down) of expert e. */
 int oracle_block_dots(int64_t H, int64_t I, int64_t E, int64_t S,
-                      const uint8_t *q4, const uint16_t *scales, int64_t e,
-                      int m, const int8_t *q_act, int64_t T, int32_t *dots, int32_t w8) {
+                      const uint8_t *q4, const void *scales, int64_t e,
+                      int m, const int8_t *q_act, int64_t T, int32_t *dots, int32_t fmt) {
   if (H <= 0 || I <= 0 || H % 64 || I % 64 || m < 0 || m > 2 || e < 0 || e >= E + S ||
-      (w8 != 0 && w8 != 1))
+      fmt < OR_INT4 || fmt > OR_FP4)
     return OR_EINVAL;
-  or_layer L = {H, I, E, S, q4, scales, w8};
+  or_layer L = {H, I, E, S, q4, (const uint8_t *)scales, fmt};
   const int64_t K = (m == 2) ? I : H, rows = (m == 2) ? H : I, nb = K / 32;
   const uint8_t *mat = or_mat(&L, e, m);
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t)
     for (int64_t n = 0; n < rows; ++n)
       for (int64_t b = 0; b < nb; ++b)
-        dots[(t * rows + n) * nb + b] = or_block_dot(mat, K, n, L.w8, q_act + t * K, b);
+        dots[(t * rows + n) * nb + b] = or_block_dot(mat, K, n, L.fmt, q_act + t * K, b);
   return OR_OK;
 }
 
@@ -417,13 +446,14 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
                      double *o) {
   const int64_t H = L->H, I = L->I;
   const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
-  const uint16_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  const uint8_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  const int f = L->fmt;
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t b = 0; b < H / 32; ++b) {
       double d = or_f16(dx[b]);
-      g += or_f16(sg[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qg, H, n, L->w8, qx, b);
-      u += or_f16(su[n * (H / 64) + b / 2]) * d * (double)or_block_dot(qu, H, n, L->w8, qx, b);
+      g += or_s(sg, H, n, 32 * b, f) * d * (double)or_block_dot(qg, H, n, f, qx, b);
+      u += or_s(su, H, n, 32 * b, f) * d * (double)or_block_dot(qu, H, n, f, qx, b);
     }
     hf[n] = (float)(or_silu(g) * u);
   }
@@ -431,8 +461,8 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
   for (int64_t m = 0; m < H; ++m) {
     double acc = 0.0;
     for (int64_t b = 0; b < I / 32; ++b)
-      acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *
-             (double)or_block_dot(qd, I, m, L->w8, qh, b);
+      acc += or_s(sd, I, m, 32 * b, f) * or_f16(dh[b]) *
+             (double)or_block_dot(qd, I, m, f, qh, b);
     o[m] = acc;
   }
   return OR_OK;
@@ -443,14 +473,14 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
  * If h_out is not NULL it receives the fp32 h of every (token, slot) in
  * [T][k+S][I] order (slot k = shared expert), for diagnosis in tests. */
 int oracle_forward_prefill(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
-                           const uint8_t *q4, const uint16_t *scales,
+                           const uint8_t *q4, const void *scales,
                            const int32_t *topk_idx, const float *topk_w,
                            const uint16_t *x_bf16, int64_t T, double *y,
-                           float *h_out, int32_t w8) {
+                           float *h_out, int32_t fmt) {
   if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1 ||
-      (w8 != 0 && w8 != 1))
+      fmt < OR_INT4 || fmt > OR_FP4)
     return OR_EINVAL;
-  or_layer L = {H, I, E, S, q4, scales, w8};
+  or_layer L = {H, I, E, S, q4, (const uint8_t *)scales, fmt};
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t t = 0; t < T; ++t) {

@@ -49,11 +49,16 @@ class LayerSpec:
     sigmoid: bool
     renorm: bool
     routed_scale: float = 1.0
-    int8: bool = False  # one int8 byte per weight instead of a nibble
+    int8: bool = False   # one int8 byte per weight instead of a nibble
+    mxfp4: bool = False  # E2M1 nibbles with one E8M0 scale byte per 32 weights
 
     @property
     def flags(self) -> int:
         return (1 if self.sigmoid else 0) | (256 if self.renorm else 0)
+
+    @property
+    def weights(self) -> str:
+        return "mxfp4" if self.mxfp4 else ("int8" if self.int8 else "int4")
 
     @property
     def n_total(self) -> int:
@@ -67,12 +72,17 @@ class LayerSpec:
 
     @property
     def expert_scales(self) -> int:
-        """fp16 scales of one expert: one per 64 weights."""
-        return 3 * self.inter * self.hidden // 64
+        """Scales of one expert: one fp16 per 64 weights, or one E8M0 byte per
+        32 weights (mxfp4)."""
+        return 3 * self.inter * self.hidden // (32 if self.mxfp4 else 64)
+
+    @property
+    def scale_bytes(self) -> int:
+        return 1 if self.mxfp4 else 2
 
     @property
     def expert_total_bytes(self) -> int:
-        return self.expert_bytes + 2 * self.expert_scales
+        return self.expert_bytes + self.scale_bytes * self.expert_scales
 
 
 @dataclasses.dataclass(frozen=True)
@@ -127,6 +137,10 @@ def make_weights(spec: LayerSpec, seed: int = 0, layer: int = 0, device="cpu",
     q4 = torch.randint(0, 256, (n * spec.expert_bytes,), dtype=torch.uint8,
                        generator=g, device=device)
     g = _gen(device, seed, layer, "scales")
+    if spec.mxfp4:  # E8M0 exponents 118..122: 2^-9 .. 2^-5 (E2M1 codes reach 6)
+        scales = torch.randint(118, 123, (n * spec.expert_scales,), dtype=torch.uint8,
+                               generator=g, device=device)
+        return q4, scales
     sc = torch.randn(n * spec.expert_scales, generator=g, device=device,
                      dtype=torch.float32)
     scales = (sc * (0.02 / 16 if spec.int8 else 0.02)).abs_().to(torch.float16)
@@ -202,7 +216,8 @@ def expert_slice(spec: LayerSpec, q4: torch.Tensor, scales: torch.Tensor, expert
     eb, es = spec.expert_bytes, spec.expert_scales
     qs = [q4[e * eb:(e + 1) * eb].cpu() for e in experts]
     ss = [scales[e * es:(e + 1) * es].cpu() for e in experts]
-    return (torch.cat(qs).numpy(), f16_bits(torch.cat(ss)))
+    sc = torch.cat(ss)
+    return (torch.cat(qs).numpy(), sc.numpy() if spec.mxfp4 else f16_bits(sc))
 
 
 def container_gib(spec: LayerSpec, layers: int = 1) -> float:

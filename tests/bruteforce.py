@@ -24,27 +24,49 @@ def unpack_nibbles(rows_bytes: np.ndarray) -> np.ndarray:
     return out
 
 
-def codes(qb: np.ndarray, rows: int, K: int, int8: bool) -> np.ndarray:
-    """[rows, K] integer codes of one matrix's bytes."""
-    if int8:
+# FP4 E2M1 magnitudes of codes 0..7 as tabulated in the OCP microscaling
+# formats specification; bit 3 of a code is its sign.
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def codes(qb: np.ndarray, rows: int, K: int, weights: str) -> np.ndarray:
+    """[rows, K] integer codes of one matrix's bytes (mxfp4: twice the E2M1
+    value, an integer)."""
+    if weights == "int8":
         return np.asarray(qb, np.uint8).view(np.int8).reshape(rows, K)
-    return unpack_nibbles(np.asarray(qb, np.uint8).reshape(rows, K // 2))
+    b = np.asarray(qb, np.uint8).reshape(rows, K // 2)
+    if weights == "mxfp4":
+        nib = np.empty((rows, K), np.uint8)
+        nib[:, 0::2], nib[:, 1::2] = b & 15, b >> 4
+        v = E2M1[nib & 7] * np.where(nib & 8, -2.0, 2.0)
+        return v.astype(np.int8)
+    return unpack_nibbles(b)
 
 
-def dense_experts(H, I, n, q4, scales, int8=False):
+def scale_matrix(sb: np.ndarray, rows: int, K: int, weights: str) -> np.ndarray:
+    """[rows, K] fp64 scale of every weight (mxfp4: halved, for the doubled codes)."""
+    if weights == "mxfp4":
+        e = np.asarray(sb, np.uint8).reshape(rows, K // 32).astype(np.float64)
+        return np.repeat(np.exp2(e - 128.0), 32, axis=1)
+    s = np.asarray(sb, np.uint16).view(np.float16).astype(np.float64).reshape(rows, K // 64)
+    return np.repeat(s, 64, axis=1)
+
+
+def dense_experts(H, I, n, q4, scales, weights="int4"):
     """Dequantised fp64 (Wg [I,H], Wu [I,H], Wd [H,I]) for experts 0..n-1."""
     q4 = np.asarray(q4, np.uint8)
-    sc = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
-    mb = I * H if int8 else I * H // 2
-    eb, es = 3 * mb, 3 * I * H // 64
+    sc = np.asarray(scales, np.uint8 if weights == "mxfp4" else np.uint16)
+    mb = I * H if weights == "int8" else I * H // 2
+    ms = I * H // (32 if weights == "mxfp4" else 64)
+    eb, es = 3 * mb, 3 * ms
     out = []
     for e in range(n):
         qe, se = q4[e * eb:(e + 1) * eb], sc[e * es:(e + 1) * es]
         mats = []
         for m, (rows, K) in enumerate(((I, H), (I, H), (H, I))):
-            qm = codes(qe[m * mb:(m + 1) * mb], rows, K, int8)
-            sb = se[m * (I * H // 64):(m + 1) * (I * H // 64)].reshape(rows, K // 64)
-            mats.append(qm.astype(np.float64) * np.repeat(sb, 64, axis=1))
+            qm = codes(qe[m * mb:(m + 1) * mb], rows, K, weights)
+            sm = scale_matrix(se[m * ms:(m + 1) * ms], rows, K, weights)
+            mats.append(qm.astype(np.float64) * sm)
         out.append(tuple(mats))
     return out
 
@@ -90,10 +112,10 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def decode_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, int8=False):
+def decode_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, weights="int4"):
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
-    experts = dense_experts(H, I, E + S, q4, scales, int8)
+    experts = dense_experts(H, I, E + S, q4, scales, weights)
     wmat = np.zeros((T, E + S))
     for t in range(T):
         for j in range(topk_idx.shape[1]):
@@ -120,13 +142,13 @@ def q8_0(v):
     return q.astype(np.int8).reshape(-1), d.astype(np.float16)
 
 
-def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, int8=False):
+def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, weights="int4"):
     x32 = bf16_to_f64(x_bits).astype(np.float32)
     T = x32.shape[0]
     qx, dx = q8_0(x32)
     xh = qx.reshape(T, H // 32, 32).astype(np.float64) * dx.astype(np.float64).reshape(T, H // 32, 1)
     xh = xh.reshape(T, H)
-    experts = dense_experts(H, I, E + S, q4, scales, int8)
+    experts = dense_experts(H, I, E + S, q4, scales, weights)
     wmat = np.zeros((T, E + S))
     for t in range(T):
         for j in range(topk_idx.shape[1]):
@@ -143,12 +165,12 @@ def prefill_layer(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits, int8=False):
     return y
 
 
-def block_dots(H, I, q4, expert, matrix, q_act, int8=False):
-    mb = I * H if int8 else I * H // 2
+def block_dots(H, I, q4, expert, matrix, q_act, weights="int4"):
+    mb = I * H if weights == "int8" else I * H // 2
     eb = 3 * mb
     rows, K = ((I, H), (I, H), (H, I))[matrix]
     qb = np.asarray(q4, np.uint8)[expert * eb + matrix * mb:expert * eb + (matrix + 1) * mb]
-    w = codes(qb, rows, K, int8).astype(np.int64)
+    w = codes(qb, rows, K, weights).astype(np.int64)
     a = np.asarray(q_act, np.int8).reshape(-1, K).astype(np.int64)
     T = a.shape[0]
     prod = w[None, :, :] * a[:, None, :]

@@ -62,7 +62,7 @@ def oracle_layer(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarray, top
     xb = synth.bf16_bits(x)[tokens]
     fn = oracle.forward_decode if entry == "decode" else oracle.forward_prefill
     return fn(spec.hidden, spec.inter, len(used), spec.n_shared, spec.top_k, q4h, sch,
-              remap[idx], w, xb, int8_weights=spec.int8)
+              remap[idx], w, xb, weights=spec.weights)
 
 
 def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
@@ -111,7 +111,7 @@ def prefill_flip_budget(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarr
     remap[used] = np.arange(len(used), dtype=np.int32)
     xb = synth.bf16_bits(x)[tokens]
     ref, h = oracle.forward_prefill(H, I, len(used), S, k, q4h, sch, remap[idx], w, xb,
-                                    want_h=True, int8_weights=spec.int8)
+                                    want_h=True, weights=spec.weights)
     mb = I * H if spec.int8 else I * H // 2
     eb, es = 3 * mb, 3 * I * H // 64
     scf = sch.view(np.float16).astype(np.float64)

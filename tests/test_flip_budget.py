@@ -47,7 +47,7 @@ def test_budget_covers_boundary_decisions(shape, int8):
         try:
             y = bf.prefill_layer(spec.hidden, spec.inter, spec.n_experts, spec.n_shared,
                                  q4.numpy(), synth.f16_bits(sc), r["topk_idx"], r["topk_w"],
-                                 synth.bf16_bits(x), int8=int8)
+                                 synth.bf16_bits(x), weights=spec.weights)
         finally:
             bf.q8_0 = orig
         assert np.all(np.abs(y - ref) <= 1e-5 * den + budget)

@@ -44,7 +44,7 @@ def test_int8_block_dots_bit_exact(spec, T, experts):
             torch.cuda.synchronize()
             qh, sh = synth.expert_slice(spec, q8, sc, [e])
             want = oracle.block_dots(spec.hidden, spec.inter, 1, 0, qh, sh, 0, m, a.numpy(),
-                                     int8_weights=True)
+                                     weights="int8")
             assert np.array_equal(dots.cpu().numpy(), want), (e, m)
 
 

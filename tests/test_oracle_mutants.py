@@ -21,6 +21,7 @@ CHECKS = [
     pins.check_router_logits_vs_bruteforce, pins.check_int4_quant_vs_bruteforce,
     pins.check_int4_quant_closed_form, pins.check_int4_quant_properties,
     pins.check_int8_decode_prefill_vs_bruteforce, pins.check_int8_block_dots,
+    pins.check_mxfp4_decode_prefill_vs_bruteforce, pins.check_mxfp4_block_dots,
 ]
 
 # (name, text in the oracle, replacement)
@@ -29,23 +30,33 @@ MUTANTS = [
      "int v = high ? (byte & 15) : (byte >> 4);"),
     ("nibble read unsigned", "return v >= 8 ? v - 16 : v;", "return v;"),
     ("nibble sign off by one", "return v >= 8 ? v - 16 : v;", "return v > 8 ? v - 16 : v;"),
-    ("scale group of 32", "return or_f16(sc[n * (K / 64) + k / 64]);",
-     "return or_f16(sc[n * (K / 64) + (k / 32) % (K / 64)]);"),
+    ("scale group of 32", "return or_f16(((const uint16_t *)sc)[n * (K / 64) + k / 64]);",
+     "return or_f16(((const uint16_t *)sc)[n * (K / 64) + (k / 32) % (K / 64)]);"),
     ("matrix stride wrong",
      "return L->q4 + e * 3 * or_mat_bytes(L) + (int64_t)m * or_mat_bytes(L);",
      "return L->q4 + e * 3 * or_mat_bytes(L) + (int64_t)m * or_mat_bytes(L) / 2;"),
-    ("int8 code read unsigned", "if (w8) return (int)(int8_t)mat[n * K + k];",
-     "if (w8) return (int)mat[n * K + k];"),
-    ("int8 rows read as nibble rows", "if (w8) return (int)(int8_t)mat[n * K + k];",
-     "if (w8) return (int)(int8_t)mat[n * (K / 2) + k];"),
-    ("int8 matrix sized as nibbles", "return L->w8 ? L->I * L->H : L->I * L->H / 2;",
+    ("int8 code read unsigned", "if (fmt == OR_INT8) return (int)(int8_t)mat[n * K + k];",
+     "if (fmt == OR_INT8) return (int)mat[n * K + k];"),
+    ("int8 rows read as nibble rows", "if (fmt == OR_INT8) return (int)(int8_t)mat[n * K + k];",
+     "if (fmt == OR_INT8) return (int)(int8_t)mat[n * (K / 2) + k];"),
+    ("int8 matrix sized as nibbles", "return L->fmt == OR_INT8 ? L->I * L->H : L->I * L->H / 2;",
      "return L->I * L->H / 2;"),
-    ("up uses gate scales", "*su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {",
-     "*su = or_sc(L, e, 0), *sd = or_sc(L, e, 2);\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {"),
+    ("e2m1 subnormals read as normal", "const double v = e ? ldexp(1.0 + 0.5 * m, e - 1) : 0.5 * m;",
+     "const double v = ldexp(1.0 + 0.5 * m, e - 1);"),
+    ("e2m1 exponent bias 0", "const double v = e ? ldexp(1.0 + 0.5 * m, e - 1) : 0.5 * m;",
+     "const double v = e ? ldexp(1.0 + 0.5 * m, e) : 0.5 * m;"),
+    ("e8m0 scale not halved", "return ldexp(1.0, (int)sc[n * (K / 32) + k / 32] - 128);",
+     "return ldexp(1.0, (int)sc[n * (K / 32) + k / 32] - 127);"),
+    ("fp4 scale per 64", "return ldexp(1.0, (int)sc[n * (K / 32) + k / 32] - 128);",
+     "return ldexp(1.0, (int)sc[n * (K / 32) + k / 64] - 128);"),
+    ("fp4 nibbles high first", "or_e2m1((k & 1) ? byte >> 4 : byte & 15)",
+     "or_e2m1((k & 1) ? byte & 15 : byte >> 4)"),
+    ("up uses gate scales", "*su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);\n  const int f = L->fmt;\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {",
+     "*su = or_sc(L, e, 0), *sd = or_sc(L, e, 2);\n  const int f = L->fmt;\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {"),
     ("silu sign flipped", "return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
     ("gate and up swapped in swiglu", "h[n] = or_silu(g) * u;", "h[n] = or_silu(u) * g;"),
-    ("down transposed", "acc += (double)or_q(qd, I, m, n, L->w8) * or_s(sd, I, m, n) * h[n];",
-     "acc += (double)or_q(qd, I, n % I, m % I, L->w8) * or_s(sd, I, m, n) * h[n];"),
+    ("down transposed", "acc += (double)or_q(qd, I, m, n, f) * or_s(sd, I, m, n, f) * h[n];",
+     "acc += (double)or_q(qd, I, n % I, m % I, f) * or_s(sd, I, m, n, f) * h[n];"),
     ("shared expert dropped", "      if (S) {\n        or_ffn_f64(&L, E, x, h, o);", "      if (0) {\n        or_ffn_f64(&L, E, x, h, o);"),
     ("routing weight ignored", "for (int64_t i = 0; i < H; ++i) yt[i] += w * o[i];\n      }\n      if (S)",
      "for (int64_t i = 0; i < H; ++i) yt[i] += o[i];\n      }\n      if (S)"),
@@ -62,10 +73,10 @@ MUTANTS = [
     ("q8_0 truncates", "r = (int)roundf(ratio);", "r = (int)ratio;"),
     ("block dot off by one block", "for (int64_t k = 32 * b; k < 32 * b + 32; ++k)",
      "for (int64_t k = 32 * b; k < 32 * b + 31; ++k)"),
-    ("prefill weight scale group", "g += or_f16(sg[n * (H / 64) + b / 2]) * d",
-     "g += or_f16(sg[n * (H / 64) + b % (H / 64)]) * d"),
-    ("prefill h not requantised", "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[b]) *",
-     "acc += or_f16(sd[m * (I / 64) + b / 2]) * or_f16(dh[0]) *"),
+    ("prefill weight scale group", "g += or_s(sg, H, n, 32 * b, f) * d",
+     "g += or_s(sg, H, n, b, f) * d"),
+    ("prefill h not requantised", "acc += or_s(sd, I, m, 32 * b, f) * or_f16(dh[b]) *",
+     "acc += or_s(sd, I, m, 32 * b, f) * or_f16(dh[0]) *"),
     ("f16 rounding truncates", "double m = nearbyint(ldexp(a, 10 - E));", "double m = floor(ldexp(a, 10 - E));"),
     ("int4 scale from max / 8", "volatile float s = a / 7.0f;", "volatile float s = a / 8.0f;"),
     ("int4 quantised with the fp32 scale", "const float sf = (float)or_f16(s16);",

@@ -28,7 +28,7 @@ TINY = synth.WORKLOADS["tiny"].spec
 
 def _host_layer(spec, seed=0):
     q4, sc = synth.make_weights(spec, seed=seed)
-    return q4.numpy(), synth.f16_bits(sc)
+    return q4.numpy(), (sc.numpy() if spec.mxfp4 else synth.f16_bits(sc))
 
 
 def _x_bits(spec, T, seed=0):
@@ -362,13 +362,13 @@ def check_int8_decode_prefill_vs_bruteforce():
         assert q4.size == s.n_total * 3 * s.hidden * s.inter  # one byte per weight
         args = (s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k, q4, sc, r["topk_idx"],
                 r["topk_w"], x)
-        y = oracle.forward_decode(*args, int8_weights=True)
+        y = oracle.forward_decode(*args, weights="int8")
         yb = bf.decode_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
-                             r["topk_idx"], r["topk_w"], x, int8=True)
+                             r["topk_idx"], r["topk_w"], x, weights="int8")
         assert _rel(y, yb) < 1e-10
-        yp = oracle.forward_prefill(*args, int8_weights=True)
+        yp = oracle.forward_prefill(*args, weights="int8")
         ypb = bf.prefill_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
-                               r["topk_idx"], r["topk_w"], x, int8=True)
+                               r["topk_idx"], r["topk_w"], x, weights="int8")
         assert _rel(yp, ypb) < 1e-10
         assert 1e-6 < _rel(yp, y) < 5e-2
 
@@ -382,9 +382,9 @@ def check_int8_block_dots():
         a = rng.integers(-127, 128, (3, K)).astype(np.int8)
         for e in (0, spec.n_total - 1):
             d = oracle.block_dots(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, q4, sc,
-                                  e, m, a, int8_weights=True)
+                                  e, m, a, weights="int8")
             assert np.array_equal(d, bf.block_dots(spec.hidden, spec.inter, q4, e, m, a,
-                                                   int8=True))
+                                                   weights="int8"))
     # every int8 code: row 0 of a gate matrix holds byte values 0..255 at
     # k = 0..255; activation row j is 127 (or -1) at k = j only
     H, I = 256, 64
@@ -394,7 +394,7 @@ def check_int8_block_dots():
     a[np.arange(256), np.arange(256)] = 127
     a[256 + np.arange(256), np.arange(256)] = -1
     z = np.zeros(3 * H * I // 64, np.uint16)
-    d = oracle.block_dots(H, I, 1, 0, q8, z, 0, 0, a, int8_weights=True)
+    d = oracle.block_dots(H, I, 1, 0, q8, z, 0, 0, a, weights="int8")
     code = np.arange(256).astype(np.uint8).view(np.int8).astype(np.int32)
     j = np.arange(256)
     assert np.array_equal(d[j, 0, j // 32], 127 * code)
@@ -402,8 +402,74 @@ def check_int8_block_dots():
     assert not d[:, 1:, :].any()
     worst = np.full(3 * H * I, 0x80, np.uint8)  # every code -128
     d = oracle.block_dots(H, I, 1, 0, worst, z, 0, 0, np.full((1, H), -127, np.int8),
-                          int8_weights=True)
+                          weights="int8")
     assert np.all(d == 32 * 128 * 127)
+
+
+SIGMOID_SMALL_F4 = synth.LayerSpec(192, 128, 5, 1, 3, sigmoid=True, renorm=True, mxfp4=True)
+SOFTMAX_SMALL_F4 = synth.LayerSpec(128, 64, 6, 0, 2, sigmoid=False, renorm=False, mxfp4=True)
+
+
+def check_mxfp4_decode_prefill_vs_bruteforce():
+    for spec, T in ((SOFTMAX_SMALL_F4, 4), (SIGMOID_SMALL_F4, 5)):
+        q4, sc, r, x = _decode_case(spec, T, seed=14, zipf=0.3)
+        s = spec
+        assert sc.dtype == np.uint8 and sc.size == s.n_total * 3 * s.hidden * s.inter // 32
+        # E8M0 extremes in the first expert's gate scales (fp64 decode path)
+        sx = sc.copy()
+        sx[:7] = (0, 1, 127, 128, 200, 254, 60)
+        args = (s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k, q4, sx, r["topk_idx"],
+                r["topk_w"], x)
+        y = oracle.forward_decode(*args, weights="mxfp4")
+        with np.errstate(over="ignore"):  # silu of a huge negative gate is -0
+            yb = bf.decode_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sx,
+                                 r["topk_idx"], r["topk_w"], x, weights="mxfp4")
+        assert _rel(y, yb) < 1e-10
+        # the integer path keeps h in fp32: scales that keep it finite
+        sc = sc.copy()
+        sc[:7] = (100, 110, 127, 128, 130, 135, 60)
+        args = (s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k, q4, sc, r["topk_idx"],
+                r["topk_w"], x)
+        yp = oracle.forward_prefill(*args, weights="mxfp4")
+        ypb = bf.prefill_layer(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
+                               r["topk_idx"], r["topk_w"], x, weights="mxfp4")
+        assert _rel(yp, ypb) < 1e-10
+
+
+def check_mxfp4_block_dots():
+    # the 16 E2M1 codes at k = 0..15 of row 0 (two per byte, low nibble
+    # first); activation row j is 127 (or -1) at k = j only
+    H, I = 64, 64
+    q = np.zeros(3 * H * I // 2, np.uint8)
+    nib = np.arange(16, dtype=np.uint8)
+    q[:8] = nib[0::2] | (nib[1::2] << 4)
+    a = np.zeros((32, H), np.int8)
+    a[np.arange(16), np.arange(16)] = 127
+    a[16 + np.arange(16), np.arange(16)] = -1
+    z = np.full(3 * H * I // 32, 127, np.uint8)
+    d = oracle.block_dots(H, I, 1, 0, q, z, 0, 0, a, weights="mxfp4")
+    doubled = np.array([0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12])
+    assert np.array_equal(d[np.arange(16), 0, 0], 127 * doubled)
+    assert np.array_equal(d[16 + np.arange(16), 0, 0], -doubled)
+    assert not d[:, 1:, :].any() and not d[:, 0, 1:].any()
+    spec = SIGMOID_SMALL_F4
+    q4, sc = _host_layer(spec, 15)
+    rng = np.random.default_rng(15)
+    for m in (0, 2):
+        K = spec.inter if m == 2 else spec.hidden
+        a = rng.integers(-127, 128, (3, K)).astype(np.int8)
+        dd = oracle.block_dots(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, q4, sc,
+                               spec.n_total - 1, m, a, weights="mxfp4")
+        assert np.array_equal(dd, bf.block_dots(spec.hidden, spec.inter, q4, spec.n_total - 1,
+                                                m, a, weights="mxfp4"))
+
+
+def test_mxfp4_decode_prefill_vs_bruteforce():
+    check_mxfp4_decode_prefill_vs_bruteforce()
+
+
+def test_mxfp4_block_dots():
+    check_mxfp4_block_dots()
 
 
 def test_block_dots_vs_bruteforce():
