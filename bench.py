@@ -273,7 +273,7 @@ def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=N
     nbytes = statistics.mean(union_bytes(spec, stack.logits[r], spec.top_k)
                              for r in range(len(stack.logits)))
     gbps = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": name, "path": "decode", "weights": "int8" if spec.int8 else "int4",
+    return {"workload": name, "path": "decode", "weights": spec.weights,
             "tokens": T, "layers": layers,
             "ms_per_step": round(ms, 4), "tokens_per_s": round(T * layers / (ms * 1e-3), 1),
             "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
@@ -314,7 +314,7 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
     ops = 2.0 * 3 * spec.hidden * spec.inter * T * (spec.top_k + spec.n_shared)
     gemm_us = sum(kern.get(k, {"avg_us": 0})["avg_us"] for k in ("gemm_gateup", "gemm_down"))
     out = {"workload": name, "path": "prefill",
-           "weights": "int8" if spec.int8 else "int4", "tokens": T, "ms_per_step": round(ms, 4),
+           "weights": spec.weights, "tokens": T, "ms_per_step": round(ms, 4),
            "tokens_per_s": round(T / (ms * 1e-3), 1),
            "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
            "int8_frac": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),

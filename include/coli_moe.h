@@ -76,7 +76,7 @@ enum { COLI_OUT_BF16 = 0, COLI_OUT_F32 = 1 };
 enum { COLI_SRC_BF16 = 0, COLI_SRC_F32 = 1 };
 
 /* weight code width of the expert container (coli_moe_layer_t.weight_format) */
-enum { COLI_WEIGHTS_INT4 = 0, COLI_WEIGHTS_INT8 = 1 };
+enum { COLI_WEIGHTS_INT4 = 0, COLI_WEIGHTS_INT8 = 1, COLI_WEIGHTS_MXFP4 = 2 };
 
 /* workspace selector for coli_moe_workspace_bytes */
 enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
@@ -117,6 +117,20 @@ enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
  * up to 8192) and T <= 16, and in coli_moe_forward_prefill and
  * coli_moe_block_dots when H and I (the reduction length) are multiples of
  * 256; other calls return COLI_E_UNSUPPORTED.
+ *
+ * MXFP4 codes (weight_format = COLI_WEIGHTS_MXFP4): the pages list fp4
+ * experts for Kimi K3 and DeepSeek V4 (ai-tools-nav review, model family
+ * table) without the format; read as OCP MXFP4.  Codes are FP4 E2M1 nibbles
+ * (bit 3 sign, bits 2-1 exponent with bias 1, bit 0 mantissa: 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6), packed and laid out exactly like the int4 codes.  The
+ * scales pointer holds E8M0 bytes instead of fp16: byte E[n][b] scales
+ * weights k in [32b, 32b+32) of row n by 2^(E-127); E must be below 255.
+ * One E8M0 byte per 32 weights takes the bytes of one fp16 per 64, so the
+ * scale layout per expert and matrix is the same (gate at byte 0, up at
+ * I*H/32, down at 2*I*H/32; expert e at byte e * 3*I*H/32).  Same calls and
+ * shape limits as int8 codes.  On the integer path the codes enter the
+ * int8 matrix cores as 2 * E2M1 (integers in [-12, 12], exact) with the
+ * scale halved; coli_moe_block_dots returns the dots of those doubled codes.
  */
 typedef struct coli_moe_layer {
   int32_t hidden;        /* H */
@@ -128,7 +142,7 @@ typedef struct coli_moe_layer {
   float routed_scale;    /* multiplies every routing weight (1.0f usually) */
   const uint8_t *q4;     /* device, see above */
   const uint16_t *scales;/* device, fp16 bit patterns, see above */
-  int32_t weight_format; /* COLI_WEIGHTS_INT4 (0) or COLI_WEIGHTS_INT8 */
+  int32_t weight_format; /* COLI_WEIGHTS_INT4 (0), _INT8 or _MXFP4 */
 } coli_moe_layer_t;
 
 /* ---- route buffers (caller-allocated device memory) ---------------------

@@ -18,7 +18,7 @@ plus two small holders that own the device buffers the C calls take:
 from .binding import (  # noqa: F401
     COLI_ENTRY_DECODE, COLI_ENTRY_PREFILL, COLI_ENTRY_ROUTE, COLI_OUT_BF16, COLI_OUT_F32,
     COLI_ROUTE_RENORM, COLI_ROUTE_SIGMOID, COLI_ROUTE_SOFTMAX, COLI_SRC_BF16, COLI_SRC_F32,
-    COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8,
+    COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8, COLI_WEIGHTS_MXFP4,
     ColiError, KernelTimer, Layer, Route, coli_moe_block_dots, coli_moe_forward_decode,
     coli_moe_forward_prefill, coli_moe_quantize_int4_gs64, coli_moe_quantize_q8_0, coli_moe_route,
     coli_moe_route_hidden,

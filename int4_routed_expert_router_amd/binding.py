@@ -15,7 +15,7 @@ COLI_ROUTE_SOFTMAX, COLI_ROUTE_SIGMOID, COLI_ROUTE_RENORM = 0, 1, 256
 COLI_OUT_BF16, COLI_OUT_F32 = 0, 1
 COLI_SRC_BF16, COLI_SRC_F32 = 0, 1
 COLI_ENTRY_ROUTE, COLI_ENTRY_DECODE, COLI_ENTRY_PREFILL = 0, 1, 2
-COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8 = 0, 1
+COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8, COLI_WEIGHTS_MXFP4 = 0, 1, 2
 
 
 class ColiError(RuntimeError):
@@ -109,22 +109,24 @@ def _stream(stream):
 class Layer:
     """One MoE layer: shape, routing kind and the device gs64 container.
 
-    q4: uint8 tensor of (E+S)*3*I*H/2 bytes (int4 codes) or (E+S)*3*I*H bytes
-    (int8 codes, int8=True); scales: fp16 tensor of (E+S)*3*I*H/64 values
-    (see include/coli_moe.h for the byte layout).
+    q4: uint8 tensor of (E+S)*3*I*H/2 bytes (int4 or MXFP4 codes) or
+    (E+S)*3*I*H bytes (int8 codes, int8=True); scales: fp16 tensor of
+    (E+S)*3*I*H/64 values, or for MXFP4 (mxfp4=True) a uint8 tensor of
+    (E+S)*3*I*H/32 E8M0 bytes (see include/coli_moe.h for the byte layout).
     """
 
     def __init__(self, hidden, inter, n_experts, n_shared, top_k, flags, q4, scales,
-                 routed_scale=1.0, int8=False):
+                 routed_scale=1.0, int8=False, mxfp4=False):
         self.q4, self.scales = q4, scales  # keep the tensors alive
+        fmt = COLI_WEIGHTS_MXFP4 if mxfp4 else (COLI_WEIGHTS_INT8 if int8 else COLI_WEIGHTS_INT4)
         self.c = _LayerC(hidden, inter, n_experts, n_shared, top_k, flags, routed_scale,
-                         _ptr(q4), _ptr(scales),
-                         COLI_WEIGHTS_INT8 if int8 else COLI_WEIGHTS_INT4)
+                         _ptr(q4), _ptr(scales), fmt)
 
     @classmethod
     def from_spec(cls, spec, q4, scales):
         return cls(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, spec.top_k,
-                   spec.flags, q4, scales, spec.routed_scale, getattr(spec, "int8", False))
+                   spec.flags, q4, scales, spec.routed_scale, getattr(spec, "int8", False),
+                   getattr(spec, "mxfp4", False))
 
     hidden = property(lambda s: s.c.hidden)
     inter = property(lambda s: s.c.inter)

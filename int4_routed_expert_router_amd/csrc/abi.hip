@@ -29,7 +29,8 @@ int check_layer(const coli_moe_layer_t *l, Layer *out) {
   if (l->top_k < 1 || l->top_k > l->n_experts || l->top_k > kMaxTopK) return COLI_E_INVALID;
   if (l->flags & ~(uint32_t)(COLI_ROUTE_SIGMOID | COLI_ROUTE_RENORM)) return COLI_E_INVALID;
   if (!isfinite(l->routed_scale)) return COLI_E_INVALID;
-  if (l->weight_format != COLI_WEIGHTS_INT4 && l->weight_format != COLI_WEIGHTS_INT8)
+  if (l->weight_format != COLI_WEIGHTS_INT4 && l->weight_format != COLI_WEIGHTS_INT8 &&
+      l->weight_format != COLI_WEIGHTS_MXFP4)
     return COLI_E_INVALID;
   if (out) {
     out->H = H;
@@ -42,6 +43,7 @@ int check_layer(const coli_moe_layer_t *l, Layer *out) {
     out->q4 = l->q4;
     out->scales = l->scales;
     out->w8 = l->weight_format == COLI_WEIGHTS_INT8;
+    out->f4 = l->weight_format == COLI_WEIGHTS_MXFP4;
     out->expert_bytes = out->w8 ? (int64_t)3 * I * H : (int64_t)3 * I * H / 2;
     out->expert_scales = (int64_t)3 * I * H / 64;
   }
@@ -83,10 +85,10 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
   if ((rc = check_route(route))) return rc;
   if ((rc = check_tokens(*L, T, entry == COLI_ENTRY_DECODE ? kMaxDecodeT : kMaxT))) return rc;
   if (entry == COLI_ENTRY_DECODE && L->I > kMaxDecodeInter) return COLI_E_UNSUPPORTED;
-  // int8 codes: decode on the streaming path; prefill with H, I multiples
-  // of 256 (the four-step matrix-core kernel)
-  if (L->w8 && (entry == COLI_ENTRY_DECODE ? !decode_stream_supported(*L, T)
-                                           : (L->H % 256 || L->I % 256)))
+  // int8 and MXFP4 codes: decode on the streaming path; prefill with H, I
+  // multiples of 256 (the four-step matrix-core kernel)
+  if ((L->w8 || L->f4) && (entry == COLI_ENTRY_DECODE ? !decode_stream_supported(*L, T)
+                                                      : (L->H % 256 || L->I % 256)))
     return COLI_E_UNSUPPORTED;
   if (!x || !y) return COLI_E_INVALID;
   if (y_dtype != COLI_OUT_BF16 && y_dtype != COLI_OUT_F32) return COLI_E_INVALID;
@@ -203,7 +205,7 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t m
   if (expert < 0 || expert >= L.E + L.S || matrix < 0 || matrix > 2) return COLI_E_INVALID;
   if (T < 1 || T > 4096 || !q_act || !dots) return COLI_E_INVALID;
   if (!aligned(q_act, 16) || !aligned(dots, 16)) return COLI_E_ALIGN;
-  if (L.w8 && (matrix == 2 ? L.I : L.H) % 256) return COLI_E_UNSUPPORTED;
+  if ((L.w8 || L.f4) && (matrix == 2 ? L.I : L.H) % 256) return COLI_E_UNSUPPORTED;
   return launch_block_dots(L, expert, matrix, q_act, T, dots, reinterpret_cast<hipStream_t>(stream));
 }
 

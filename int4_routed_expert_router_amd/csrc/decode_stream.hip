@@ -132,6 +132,13 @@ struct CodecI4 {
   static constexpr int Q = 1;
   static constexpr float kBias = (float)kNibBias;
   static constexpr int64_t bytes(int64_t codes) { return codes / 2; }
+  // fp16 scale of 32-value chunk c of row n of a K-wide matrix, whose
+  // scales start at byte base (one per 64 weights)
+  COLI_DEV static uint16_t scale_raw(const uint8_t *base, int64_t n, int K, int c) {
+    return reinterpret_cast<const uint16_t *>(base)[n * (K / 64) + c / 2];
+  }
+  COLI_DEV static float scale(uint16_t raw) { return f16_to_f32(raw); }
+
   COLI_DEV static void pairs(const uint32_t d[4], uint32_t out[4]) { x8_to_pairs(d, out); }
   // chunk dotted with pairs xp (and, when lp is given, with a second set of
   // pairs lp: the low half of a split activation), from accumulator a
@@ -166,6 +173,13 @@ struct CodecI8 {
   static constexpr int Q = 2;
   static constexpr float kBias = 0.0f;
   static constexpr int64_t bytes(int64_t codes) { return codes; }
+  // fp16 scale of 32-value chunk c of row n of a K-wide matrix, whose
+  // scales start at byte base (one per 64 weights)
+  COLI_DEV static uint16_t scale_raw(const uint8_t *base, int64_t n, int K, int c) {
+    return reinterpret_cast<const uint16_t *>(base)[n * (K / 64) + c / 2];
+  }
+  COLI_DEV static float scale(uint16_t raw) { return f16_to_f32(raw); }
+
   COLI_DEV static void pairs(const uint32_t d[4], uint32_t out[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = d[i];
@@ -185,6 +199,46 @@ struct CodecI8 {
       if (TWO) a = dot2_bf16(p01, lp[2 * dw], a);
       a = dot2_bf16(p23, xp[2 * dw + 1], a);
       if (TWO) a = dot2_bf16(p23, lp[2 * dw + 1], a);
+    }
+    return a;
+  }
+  COLI_DEV static int half_index(int w) { return w; }
+};
+
+// MXFP4 (E2M1 nibbles, one E8M0 scale byte per 32 weights): one quad per
+// chunk and one scale per chunk.  v_cvt_scalef32_pk_bf16_fp4 turns the two
+// E2M1 codes of a byte (low nibble first) into an exact bf16 pair (scale 1;
+// the chunk's power of two is applied after the dot); natural pairs.
+struct CodecF4 {
+  static constexpr int Q = 1;
+  static constexpr float kBias = 0.0f;
+  static constexpr int64_t bytes(int64_t codes) { return codes / 2; }
+  COLI_DEV static uint16_t scale_raw(const uint8_t *base, int64_t n, int K, int c) {
+    return base[n * (K / 32) + c];
+  }
+  // 2^(E - 127); E = 0 is the fp32 subnormal 2^-127
+  COLI_DEV static float scale(uint16_t e) {
+    return __uint_as_float(e ? (uint32_t)e << 23 : 0x00400000u);
+  }
+  COLI_DEV static void pairs(const uint32_t d[4], uint32_t out[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = d[i];
+  }
+  template <int B>  // byte B of v (the byte select is an instruction field)
+  COLI_DEV static uint32_t pair(uint32_t v) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, B));
+  }
+  template <bool TWO>
+  COLI_DEV static float dot(const uint4 *w, const uint32_t *xp, const uint32_t *lp, float a) {
+    const uint32_t wv[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      const uint32_t p[4] = {pair<0>(wv[dw]), pair<1>(wv[dw]), pair<2>(wv[dw]), pair<3>(wv[dw])};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        a = dot2_bf16(p[b], xp[4 * dw + b], a);
+        if (TWO) a = dot2_bf16(p[b], lp[4 * dw + b], a);
+      }
     }
     return a;
   }
@@ -256,8 +310,9 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
   const uint8_t *qg = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)n0 * row_bytes +
                       16 * C::Q * lane;
   const uint8_t *qu = qg + (int64_t)I * row_bytes;
-  const uint16_t *sgp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)n0 * (H / 64) + lane / 2;
-  const uint16_t *sup = sgp + (int64_t)I * H / 64;
+  const uint8_t *sgb = reinterpret_cast<const uint8_t *>(L.scales + (int64_t)sl.e * L.expert_scales);
+  const uint8_t *sub = reinterpret_cast<const uint8_t *>(L.scales + (int64_t)sl.e * L.expert_scales +
+                                                         (int64_t)I * H / 64);
   // One token: this thread's activation chunk (c = threadIdx.x < NCH) is
   // requested before the weights, so that staging it waits for it alone
   // (the memory counter retires loads in issue order).
@@ -274,14 +329,13 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int64_t ob = (int64_t)j * row_bytes + 1024 * C::Q * i;
-      const int64_t os = (int64_t)j * (H / 64) + 32 * i;
 #pragma unroll
       for (int q = 0; q < C::Q; ++q) {
         wg[j][i][q] = *reinterpret_cast<const uint4 *>(qg + ob + 16 * q);
         wu[j][i][q] = *reinterpret_cast<const uint4 *>(qu + ob + 16 * q);
       }
-      sg[j][i] = sgp[os];
-      su[j][i] = sup[os];
+      sg[j][i] = C::scale_raw(sgb, n0 + j, H, lane + 64 * i);
+      su[j][i] = C::scale_raw(sub, n0 + j, H, lane + 64 * i);
     }
     // a single token collapses to straight-line code, so the staging loads
   // below are issued while the weight loads are still in flight
@@ -330,9 +384,9 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
         const float nb = xbias[ti * NCH + lane + 64 * i];
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-          v[2 * j] = fmaf(f16_to_f32(sg[j][i]), C::template dot<false>(wg[j][i], xc.p, xc.p, nb),
+          v[2 * j] = fmaf(C::scale(sg[j][i]), C::template dot<false>(wg[j][i], xc.p, xc.p, nb),
                           v[2 * j]);
-          v[2 * j + 1] = fmaf(f16_to_f32(su[j][i]),
+          v[2 * j + 1] = fmaf(C::scale(su[j][i]),
                               C::template dot<false>(wu[j][i], xc.p, xc.p, nb), v[2 * j + 1]);
         }
       }
@@ -389,8 +443,8 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
   const int64_t row_bytes = C::bytes(I);
   const uint8_t *qd = L.q4 + (int64_t)sl.e * L.expert_bytes + C::bytes((int64_t)2 * I * H) +
                       (int64_t)(m0 + lr) * row_bytes + 16 * C::Q * lc;
-  const uint16_t *sdp = L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64 +
-                        (int64_t)(m0 + lr) * (I / 64) + lc / 2;
+  const uint8_t *sdb = reinterpret_cast<const uint8_t *>(
+      L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64);
   uint4 w[RG][CPL][C::Q];
   uint16_t sc[RG][CPL];
 #pragma unroll
@@ -402,7 +456,7 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
       for (int q = 0; q < C::Q; ++q)
         w[j][i][q] = *reinterpret_cast<const uint4 *>(qd + row * row_bytes + 16 * C::Q * LPR * i +
                                                       16 * q);
-      sc[j][i] = sdp[row * (I / 64) + LPR / 2 * i];
+      sc[j][i] = C::scale_raw(sdb, m0 + lr + row, I, lc + LPR * i);
     }
   if (ONE) {
 #pragma unroll
@@ -442,7 +496,7 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
       const float nb = codec_bias2<C>(hi.p, lo.p);
 #pragma unroll
       for (int j = 0; j < RG; ++j)
-        v[j] = fmaf(f16_to_f32(sc[j][i]), C::template dot<true>(w[j][i], hi.p, lo.p, nb), v[j]);
+        v[j] = fmaf(C::scale(sc[j][i]), C::template dot<true>(w[j][i], hi.p, lo.p, nb), v[j]);
     }
     const float tot = reduce_scatter<RG, LPR>(v, lc);
     constexpr int kSpan = LPR / RG;
@@ -555,6 +609,7 @@ bool launch_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
 // Returns false, launching nothing, otherwise.
 bool launch_decode_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
                           float *h, float *o, hipStream_t s, hipError_t *err) {
+  if (L.f4) return launch_stream<CodecF4>(L, r, x, T, h, o, s, err);
   return L.w8 ? launch_stream<CodecI8>(L, r, x, T, h, o, s, err)
               : launch_stream<CodecI4>(L, r, x, T, h, o, s, err);
 }
@@ -562,6 +617,7 @@ bool launch_decode_stream(const Layer &L, const coli_moe_route_t &r, const uint1
 bool decode_stream_supported(const Layer &L, int T) {
   int lpr, cpl;
   if (T > kMaxStreamT) return false;
+  if (L.f4) return stream_shape<CodecF4>(L, lpr, cpl);
   return L.w8 ? stream_shape<CodecI8>(L, lpr, cpl) : stream_shape<CodecI4>(L, lpr, cpl);
 }
 

@@ -17,9 +17,10 @@ struct Layer {
   float routed_scale;
   const uint8_t *q4;
   const uint16_t *scales;
-  int w8;                 // 0: int4 nibble codes, 1: int8 byte codes
-  int64_t expert_bytes;   // 3*I*H/2 (int4) or 3*I*H (int8)
-  int64_t expert_scales;  // 3*I*H/64
+  int w8;                 // int8 byte codes (else nibbles)
+  int f4;                 // MXFP4: E2M1 nibbles, one E8M0 scale byte per 32 weights
+  int64_t expert_bytes;   // 3*I*H/2 (int4, MXFP4) or 3*I*H (int8)
+  int64_t expert_scales;  // 3*I*H/64 16-bit units (fp16 per 64, or two E8M0 bytes)
 };
 
 // Workspace carving: every region 256-byte aligned.

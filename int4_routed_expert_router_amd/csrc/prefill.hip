@@ -569,10 +569,14 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
 // loads is in flight while the previous group is computed; two barriers per
 // group.
 constexpr int kGroup = 4;   // K steps per LDS stage
+// weight code formats of the four-step kernel
+constexpr int kFmtI4 = 0, kFmtI8 = 1, kFmtF4 = 2;
+// NB: weight scales per step, 1 (a 64-weight group) or 2 (one per 32-block)
+template <int NB>
 struct Stage4 {
   uint2 w[BR / 16][kGroup][2][64];  // [row tile][step][32-block][lane ^ swz]
   uint2 a[BM / 16][kGroup][2][64];  // [token tile][step][32-block][lane ^ swz]
-  float sw[kGroup][BR];             // weight group scales
+  float sw[kGroup * NB][BR];        // weight scales: [step] or [2 * step + block]
   float2 sa[kGroup][BM];            // d0/16, d1/16 of each token
 };
 // Operand entry e of the tile of (step s, block b) sits at e ^ swz(s, b).
@@ -622,8 +626,33 @@ COLI_DEV void load_group(const Src4 &src, int gi, Group4<W8> &G) {
 // Registers -> LDS.  Within each half-wavefront the 8-byte writes land on
 // distinct banks: lane bits 0-1 pick consecutive entries and the (step,
 // block) pair moves the address by a multiple of 4 entries (mod 32).
-template <int MODE, bool W8>
-COLI_DEV void store_group(const Group4<W8> &G, Stage4 &st, int wid) {
+// MXFP4: 8 E2M1 codes (a dword, low nibble first) -> 8 int8 2 * E2M1 in k
+// order, as two dwords.  Magnitudes index byte tables of 2|v| and -2|v|
+// (v_perm), and each byte takes the negative entry where its code's sign bit
+// is set: v_perm selectors 8-11 replicate bits 15 / 31 of its operands, so
+// shifted copies of the codes give 0xff per negative code.
+constexpr uint32_t kF4PosLo = 0x03020100u, kF4PosHi = 0x0C080604u;  // 0 1 2 3 | 4 6 8 12
+constexpr uint32_t kF4NegLo = 0xFDFEFF00u, kF4NegHi = 0xF4F8FAFCu;  // negated
+COLI_DEV void fp4x8_to_i8(uint32_t w, uint32_t &k0123, uint32_t &k4567) {
+  const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;  // even / odd k
+  // sign masks: even codes' sign bits 3, 11, 19, 27; odd codes' 7, 15, 23, 31
+  const uint32_t se = __builtin_amdgcn_perm(w << 4, w << 12, 0x0B090A08u);
+  const uint32_t so = __builtin_amdgcn_perm(w, w << 8, 0x0B090A08u);
+  // v_bitop3 truth table 0xCA is a ? b : c, bit by bit
+  const uint32_t ve = __builtin_amdgcn_bitop3_b32(
+      se, __builtin_amdgcn_perm(kF4NegHi, kF4NegLo, me), __builtin_amdgcn_perm(kF4PosHi, kF4PosLo, me),
+      0xCAu);  // se ? neg : pos
+  const uint32_t vo = __builtin_amdgcn_bitop3_b32(
+      so, __builtin_amdgcn_perm(kF4NegHi, kF4NegLo, mo), __builtin_amdgcn_perm(kF4PosHi, kF4PosLo, mo),
+      0xCAu);
+  // interleave: k0 k1 k2 k3 = ve.b0 vo.b0 ve.b1 vo.b1, k4..k7 = bytes 2, 3
+  k0123 = __builtin_amdgcn_perm(vo, ve, 0x05010400u);
+  k4567 = __builtin_amdgcn_perm(vo, ve, 0x07030602u);
+}
+
+template <int MODE, int WF, int NB>
+COLI_DEV void store_group(const Group4<WF == kFmtI8> &G, Stage4<NB> &st, int wid) {
+  constexpr bool W8 = WF == kFmtI8;
   const int l = threadIdx.x & 63;
   {
     const int c = (l >> 2) & 7, s = c >> 1, b = c & 1;
@@ -640,6 +669,15 @@ COLI_DEV void store_group(const Group4<W8> &G, Stage4 &st, int wid) {
         continue;
       }
       const uint32_t w[4] = {G.w[j][0].x, G.w[j][0].y, G.w[j][0].z, G.w[j][0].w};
+      if (WF == kFmtF4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t lo, hi;
+          fp4x8_to_i8(w[i], lo, hi);
+          st.w[rt][s][b][(rr + 16 * i) ^ swz(s, b)] = make_uint2(lo, hi);
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t even = (w[i] << 4) & 0xf0f0f0f0u;  // k 0,2,4,6 (x16)
@@ -664,11 +702,20 @@ COLI_DEV void store_group(const Group4<W8> &G, Stage4 &st, int wid) {
   const uint16_t h[4] = {(uint16_t)G.s.x, (uint16_t)(G.s.x >> 16), (uint16_t)G.s.y,
                          (uint16_t)(G.s.y >> 16)};
   if (wid < 2) {  // weight row t: the scales of steps 0..3
+    if (WF == kFmtF4) {  // 8 E8M0 bytes, block 2s + b; 2^(E-128) for the doubled codes
+      const uint32_t e[2] = {G.s.x, G.s.y};
 #pragma unroll
-    for (int s = 0; s < kGroup; ++s) st.sw[s][t] = f16_to_f32(h[s]);
+      for (int q = 0; q < 2 * kGroup; ++q) {
+        const uint32_t E = (e[q >> 2] >> (8 * (q & 3))) & 0xffu;
+        st.sw[q][t] = __uint_as_float(E > 1 ? (E - 1) << 23 : (0x00400000u >> (1 - E)));
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s) st.sw[s][t] = f16_to_f32(h[s]);
+    }
   } else {  // token (t-128)/2: steps 2*(t&1) and 2*(t&1)+1, two blocks each
     // int4 codes sit in the stage x16: their activation scales carry 1/16
-    constexpr float f = W8 ? 1.0f : 0.0625f;
+    constexpr float f = WF == kFmtI4 ? 0.0625f : 1.0f;
     const int m = (t - BR) >> 1, s0 = 2 * (t & 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -676,14 +723,16 @@ COLI_DEV void store_group(const Group4<W8> &G, Stage4 &st, int wid) {
   }
 }
 
-template <int MODE, bool W8>
+template <int MODE, int WF>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
              const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
              int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
              int8_t *__restrict__ qh_out, uint16_t *__restrict__ dh_out,
              float *__restrict__ o_out, int32_t *__restrict__ dots_out) {
-  __shared__ Stage4 st;
+  constexpr bool W8 = WF == kFmtI8;
+  constexpr int NB = WF == kFmtF4 ? 2 : 1;
+  __shared__ Stage4<NB> st;
   __shared__ int rowid[BM];
   __shared__ int outrow[BM];
   const int lane = threadIdx.x & 63;
@@ -758,12 +807,14 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
       for (int a = 0; a < 4; ++a)
         o.a[a] = st.w[wave_row_tile<MODE>(wn, a)][s][blk][lane ^ swz(s, blk)];
     };
-    auto load_scl = [&](int s, Scl &c) {
+    // scales of block q (NB = 2) or of step q (NB = 1); activations by step
+    auto load_scl = [&](int q, Scl &c) {
       if (MODE == kDots) return;
+      const int s = NB == 2 ? q >> 1 : q;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const float4 w4 = *reinterpret_cast<const float4 *>(
-            &st.sw[s][16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
+            &st.sw[q][16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
         c.w[a][0] = w4.x, c.w[a][1] = w4.y, c.w[a][2] = w4.z, c.w[a][3] = w4.w;
       }
 #pragma unroll
@@ -793,7 +844,7 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
               const int n = it.n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
               if (n >= g.rows) continue;
               dots_out[((int64_t)(it.row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks + blk] =
-                  (d[a * 2 + ms][i] - (int)kMagic) >> (W8 ? 0 : 4);
+                  (d[a * 2 + ms][i] - (int)kMagic) >> (WF == kFmtI4 ? 4 : 0);
             }
           }
       } else {
@@ -827,21 +878,26 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
         // block q's results are in d[q & 1], block q+1's operands in o[(q+1) & 1]
         if (q + 1 < 2 * kGroup) mfmas((q & 1) ? o0 : o1, (q & 1) ? d0 : d1);
         if (q + 2 < 2 * kGroup) load_ops(q + 2, (q & 1) ? o1 : o0);
-        if ((q & 1) == 0 && q + 2 < 2 * kGroup) load_scl((q >> 1) + 1, ((q >> 1) & 1) ? c0 : c1);
-        finish(gi, q, ((q >> 1) & 1) ? c1 : c0, (q & 1) ? d1 : d0);
+        if (NB == 2) {  // one scale set per block: block q + 1's next
+          if (q + 1 < 2 * kGroup) load_scl(q + 1, (q & 1) ? c0 : c1);
+          finish(gi, q, (q & 1) ? c1 : c0, (q & 1) ? d1 : d0);
+        } else {        // one per step: step s + 1's during step s's first block
+          if ((q & 1) == 0 && q + 2 < 2 * kGroup) load_scl((q >> 1) + 1, ((q >> 1) & 1) ? c0 : c1);
+          finish(gi, q, ((q >> 1) & 1) ? c1 : c0, (q & 1) ? d1 : d0);
+        }
       }
     };
 
     Group4<W8> grp;
     load_group(src, 0, grp);
-    store_group<MODE, W8>(grp, st, wid);
+    store_group<MODE, WF, NB>(grp, st, wid);
     __syncthreads();
     if (ngroups > 1) load_group(src, 1, grp);
     for (int gi = 0; gi < ngroups; ++gi) {
       compute_stage(gi);
       if (gi + 1 < ngroups) {
         __syncthreads();  // every wavefront is done with the stage
-        store_group<MODE, W8>(grp, st, wid);
+        store_group<MODE, WF, NB>(grp, st, wid);
         __syncthreads();
         if (gi + 2 < ngroups) load_group(src, gi + 2, grp);
       }
@@ -926,14 +982,16 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.rows = L.I;
     g.K = L.H;
     g.rs = L.w8 ? 0 : 1;
+    const int wf = L.f4 ? kFmtF4 : (L.w8 ? kFmtI8 : kFmtI4);
     g.act = w.qx;
     g.act_d = w.dx;
     g.up_offset_q = ((int64_t)L.I * L.H) >> g.rs;
     g.up_offset_s = (int64_t)L.I * L.H / 64;
     const int nn = (L.I + 63) / 64;
     launch_k(COLI_K_GEMM_GATEUP,
-             L.w8 ? gemm4_kernel<kGateUp, true>
-                  : (L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp, false>),
+             wf == kFmtF4 ? gemm4_kernel<kGateUp, kFmtF4>
+             : wf == kFmtI8 ? gemm4_kernel<kGateUp, kFmtI8>
+             : (L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp, kFmtI4>),
              dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh, nullptr, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
@@ -941,6 +999,7 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
   {  // down
     GemmArgs g{};
     g.rs = L.w8 ? 0 : 1;
+    const int wf = L.f4 ? kFmtF4 : (L.w8 ? kFmtI8 : kFmtI4);
     g.wq = L.q4 + (((int64_t)2 * L.I * L.H) >> g.rs);
     g.ws = L.scales + (int64_t)2 * L.I * L.H / 64;
     g.rows = L.H;
@@ -949,8 +1008,9 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.act_d = w.dh;
     const int nn = (L.H + BR - 1) / BR;
     launch_k(COLI_K_GEMM_DOWN,
-             L.w8 ? gemm4_kernel<kDown, true>
-                  : (L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown, false>),
+             wf == kFmtF4 ? gemm4_kernel<kDown, kFmtF4>
+             : wf == kFmtI8 ? gemm4_kernel<kDown, kFmtI8>
+             : (L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown, kFmtI4>),
              dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr, nullptr, w.o, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
@@ -963,6 +1023,7 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
                       int32_t *dots, hipStream_t s) {
   GemmArgs g{};
   g.rs = L.w8 ? 0 : 1;
+  const int wf = L.f4 ? kFmtF4 : (L.w8 ? kFmtI8 : kFmtI4);
   const int64_t moff = ((int64_t)matrix * L.I * L.H) >> g.rs;
   g.wq = L.q4 + moff;
   g.ws = L.scales + (int64_t)matrix * L.I * L.H / 64;
@@ -974,8 +1035,9 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
   const int ntile = (T + BM - 1) / BM;
   coli_moe_route_t none{};
   launch_k(COLI_K_BLOCK_DOTS,
-           L.w8 ? gemm4_kernel<kDots, true>
-                : (g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots, false>),
+           wf == kFmtF4 ? gemm4_kernel<kDots, kFmtF4>
+           : wf == kFmtI8 ? gemm4_kernel<kDots, kFmtI8>
+           : (g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots, kFmtI4>),
            dim3(grid_for(band_items_host(ntile, nn))),
            dim3(kThreads), 0, s, g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes,
            L.expert_scales, nullptr, nullptr, nullptr, dots);

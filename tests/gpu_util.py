@@ -113,8 +113,10 @@ def prefill_flip_budget(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarr
     ref, h = oracle.forward_prefill(H, I, len(used), S, k, q4h, sch, remap[idx], w, xb,
                                     want_h=True, weights=spec.weights)
     mb = I * H if spec.int8 else I * H // 2
-    eb, es = 3 * mb, 3 * I * H // 64
-    scf = sch.view(np.float16).astype(np.float64)
+    ms = I * H // (32 if spec.mxfp4 else 64)      # scale elements per matrix
+    eb, es = 3 * mb, 3 * ms
+    scf = (np.exp2(sch.astype(np.float64) - 128.0) if spec.mxfp4       # halved: codes are 2v
+           else sch.view(np.float16).astype(np.float64))
     budget = np.zeros((len(tokens), H))
     for ti in range(len(tokens)):
         for j in range(k + S):
@@ -146,9 +148,14 @@ def prefill_flip_budget(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarr
             else:
                 b = np.asarray(q4h[base:base + mb], np.uint8).reshape(H, I // 2)[:, cols // 2]
                 nib = np.where(cols % 2 == 1, b >> 4, b & 15).astype(np.int64)
-                wq = np.where(nib >= 8, nib - 16, nib).astype(np.float64)
-            s = scf[le * es + 2 * (I * H // 64):le * es + 3 * (I * H // 64)].reshape(H, I // 64)
-            wabs = np.abs(wq) * s[:, cols // 64]
+                if spec.mxfp4:
+                    from bruteforce import E2M1
+                    wq = 2.0 * E2M1[nib & 7]
+                else:
+                    wq = np.where(nib >= 8, nib - 16, nib).astype(np.float64)
+            gsz = 32 if spec.mxfp4 else 64
+            s = scf[le * es + 2 * ms:le * es + 3 * ms].reshape(H, I // gsz)
+            wabs = np.abs(wq) * s[:, cols // gsz]
             budget[ti] += wj * (wabs @ col[cols])
     return ref, budget
 
