@@ -518,6 +518,13 @@ def main():
         g8 = dataclasses.replace(w.spec, int8=True)
         secondary.append(secondary_decode("glm_mtp_int8_decode_T4", g8, 4, w.zipf_alpha, 2,
                                           50, 5))
+        # MXFP4 experts (fp4 expert families): GLM-shaped decode, OLMoE-shaped prefill
+        g4 = dataclasses.replace(w.spec, mxfp4=True)
+        secondary.append(secondary_decode("glm_mxfp4_decode_stack_T1", g4, 1, w.zipf_alpha, 4,
+                                          100, 10))
+        secondary.append(secondary_prefill("olmoe_mxfp4_prefill_T512",
+                                           dataclasses.replace(ow.spec, mxfp4=True), 512, 0.0,
+                                           20, 3, copies=4))
         aw = synth.WORKLOADS["a3b"]
         for t in aw.tokens:
             secondary.append(secondary_decode("a3b_decode_T%d" % t, aw.spec, t, aw.zipf_alpha, 4,
