@@ -273,10 +273,13 @@ def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=N
     nbytes = statistics.mean(union_bytes(spec, stack.logits[r], spec.top_k)
                              for r in range(len(stack.logits)))
     gbps = nbytes / (ms * 1e-3) / 1e9
+    # per-kernel times per layer, from dispatch-stamped events over eager steps
+    kern = traced_kernels(lambda: stack.step_eager(1), reps=4)
     return {"workload": name, "path": "decode", "weights": spec.weights,
             "tokens": T, "layers": layers,
             "ms_per_step": round(ms, 4), "tokens_per_s": round(T * layers / (ms * 1e-3), 1),
-            "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
 
 
 def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
@@ -419,6 +422,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="main workload only")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the 2048-token GLM prefill workload (for profiling it)")
+    ap.add_argument("--decode-t4-only", action="store_true",
+                    help="only the GLM-shaped decode stack with 4 tokens (verify batch)")
     ap.add_argument("--convert-only", action="store_true",
                     help="only the float -> int4 quantiser on 32 GLM-shaped experts")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -447,6 +452,11 @@ def main():
         pw = synth.WORKLOADS["glm_prefill"]
         print(json.dumps(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
                                            args.steps, args.warmup, copies=1)), flush=True)
+        return
+    if args.decode_t4_only:
+        w = synth.WORKLOADS["glm"]
+        print(json.dumps(secondary_decode("glm_decode_stack_T4", w.spec, 4, w.zipf_alpha,
+                                          w.layers, args.steps, args.warmup)), flush=True)
         return
     if args.convert_only:
         print(json.dumps(secondary_convert("glm_convert_32experts_bf16", synth.WORKLOADS["glm"].spec,
