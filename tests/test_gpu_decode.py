@@ -47,6 +47,9 @@ def test_decode_workloads(name, T):
     (synth.LayerSpec(64, 64, 1, 0, 1, sigmoid=False, renorm=False), 1),
     # the maximum decode batch, every expert hot
     (synth.LayerSpec(512, 256, 16, 1, 4, sigmoid=True, renorm=True), 64),
+    # the largest hidden size, and the largest decode intermediate size
+    (synth.LayerSpec(16384, 128, 4, 1, 2, sigmoid=True, renorm=True), 3),
+    (synth.LayerSpec(128, 15360, 3, 1, 1, sigmoid=False, renorm=False), 2),
 ])
 def test_decode_edge_shapes(spec, T):
     _decode_case(spec, T, seed=7, zipf=0.5)

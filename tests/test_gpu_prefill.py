@@ -119,6 +119,17 @@ def test_prefill_edge_shapes(spec, T):
     _prefill_case(spec, T, seed=3, zipf=0.6)
 
 
+def test_prefill_maximum_batch_sampled():
+    """65,536 tokens (the largest batch the entry point takes) on a small layer."""
+    spec = synth.LayerSpec(256, 128, 8, 1, 2, sigmoid=True, renorm=True)
+    _prefill_case(spec, 65536, seed=4, zipf=0.5, tokens=[0, 1, 4095, 32768, 65534, 65535])
+
+
+def test_prefill_largest_hidden_sampled():
+    spec = synth.LayerSpec(16384, 256, 4, 1, 2, sigmoid=False, renorm=True)
+    _prefill_case(spec, 40, seed=5, tokens=[0, 39])
+
+
 def test_prefill_deterministic_bf16_and_zero_scales():
     spec = synth.WORKLOADS["a3b"].spec
     L, r, x, y, ref, toks = _prefill_case(spec, 96, zipf=synth.ZIPF_ALPHA)

@@ -45,6 +45,7 @@ def test_route_workloads(name, T):
 @pytest.mark.parametrize("E,k,T,flags", [
     (8, 8, 3, 0), (5, 1, 17, 1), (300, 17, 33, 257), (1024, 32, 40, 1), (1024, 8, 4096, 256),
     (64, 8, 16, 257), (64, 8, 17, 257), (1, 1, 5, 0), (256, 8, 65536 // 8, 257),
+    (64, 16, 65536, 257),  # the maximum batch: 65,536 tokens, 2^20 pairs
 ])
 def test_route_edges(E, k, T, flags):
     spec = synth.LayerSpec(64, 64, E, 0, k, sigmoid=bool(flags & 1), renorm=bool(flags & 256),
