@@ -45,11 +45,13 @@ def _bind(path):
                                       i32]
     lib.oracle_router_logits.argtypes = [i64, i64, i64, p, p, p]
     lib.oracle_quantize_int4_gs64.argtypes = [p, i64, i64, p, p]
+    lib.oracle_quantize_int8_gs64.argtypes = [p, i64, i64, p, p]
+    lib.oracle_quantize_mxfp4.argtypes = [p, i64, i64, p, p]
     lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_f16.restype = ctypes.c_uint16
     for f in ("oracle_route", "oracle_forward_decode", "oracle_forward_prefill",
               "oracle_quantize_q8_0", "oracle_block_dots", "oracle_router_logits",
-              "oracle_quantize_int4_gs64"):
+              "oracle_quantize_int4_gs64", "oracle_quantize_int8_gs64", "oracle_quantize_mxfp4"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -138,6 +140,32 @@ def quantize_int4_gs64(w):
     if lib.oracle_quantize_int4_gs64(_ptr(w), rows, K, _ptr(q4), _ptr(sc)) != 0:
         raise ValueError("oracle_quantize_int4_gs64: invalid arguments")
     return q4, sc
+
+
+def quantize_int8_gs64(w):
+    """int8 gs64 container of fp32 weights [rows, K] -> (int8 [rows, K],
+    uint16 fp16-bits [rows, K/64])."""
+    lib = _load()
+    w = _c(w, np.float32)
+    rows, K = w.shape
+    q = np.zeros((rows, K), np.int8)
+    sc = np.zeros((rows, K // 64), np.uint16)
+    if lib.oracle_quantize_int8_gs64(_ptr(w), rows, K, _ptr(q), _ptr(sc)) != 0:
+        raise ValueError("oracle_quantize_int8_gs64: invalid arguments")
+    return q, sc
+
+
+def quantize_mxfp4(w):
+    """MXFP4 of fp32 weights [rows, K] -> (uint8 nibbles [rows, K/2], uint8
+    E8M0 [rows, K/32])."""
+    lib = _load()
+    w = _c(w, np.float32)
+    rows, K = w.shape
+    q = np.zeros((rows, K // 2), np.uint8)
+    e = np.zeros((rows, K // 32), np.uint8)
+    if lib.oracle_quantize_mxfp4(_ptr(w), rows, K, _ptr(q), _ptr(e)) != 0:
+        raise ValueError("oracle_quantize_mxfp4: invalid arguments")
+    return q, e
 
 
 def router_logits(w_bf16, x_bf16):

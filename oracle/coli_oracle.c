@@ -408,6 +408,86 @@ int oracle_quantize_int4_gs64(const float *w, int64_t rows, int64_t K, uint8_t *
   return OR_OK;
 }
 
+/* int8 gs64 container from float weights: the int4 rule above with 127 in
+ * place of 7 and byte codes: per group of 64, s = max|w| / 127 (fp32
+ * division), s16 = fp16_RNE(s), q = round-half-away(w / s16) clamped to
+ * [-128, 127] (0 when s16 == 0); q[n][k] at byte n*K + k.  The pages give
+ * int8 experts (tantan.ink post, section "我看到的几个坑") but no quantiser;
+ * this rule, the int4 one widened, is the reading taken. */
+int oracle_quantize_int8_gs64(const float *w, int64_t rows, int64_t K, int8_t *q,
+                              uint16_t *scales) {
+  if (rows < 0 || K <= 0 || K % 64) return OR_EINVAL;
+  for (int64_t n = 0; n < rows; ++n)
+    for (int64_t g = 0; g < K / 64; ++g) {
+      const float *wg = w + n * K + 64 * g;
+      float a = 0.0f;
+      for (int i = 0; i < 64; ++i)
+        if (fabsf(wg[i]) > a) a = fabsf(wg[i]);
+      volatile float t = a / 127.0f;
+      const uint16_t t16 = oracle_f32_to_f16(t);
+      scales[n * (K / 64) + g] = t16;
+      const float tf = (float)or_f16(t16);
+      for (int i = 0; i < 64; ++i) {
+        int r = 0;
+        if (tf != 0.0f) {
+          volatile float v = wg[i] / tf;
+          r = (int)roundf(v); /* halfway cases away from zero */
+          if (r > 127) r = 127;
+          if (r < -128) r = -128;
+        }
+        q[n * K + 64 * g + i] = (int8_t)r;
+      }
+    }
+  return OR_OK;
+}
+
+/* MXFP4 from float weights, following the OCP microscaling formats
+ * conversion: per block of 32 consecutive weights of a row, the shared
+ * exponent is X = floor(log2(max|w|)) - 2 (2 = the largest E2M1 exponent),
+ * stored as E8M0 byte E = X + 127 clamped to [0, 254] (E = 0 for an all-zero
+ * block); each weight becomes the E2M1 code nearest to w / 2^(E-127), ties
+ * to the even code, saturating at +-6 (sign kept, also for zero).  Codes are
+ * packed like the int4 nibbles (even k low).  The pages list fp4 experts
+ * (ai-tools-nav review, model family table) without the converter; this is
+ * the published MX conversion. */
+int oracle_quantize_mxfp4(const float *w, int64_t rows, int64_t K, uint8_t *q4, uint8_t *e8) {
+  static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  if (rows < 0 || K <= 0 || K % 32) return OR_EINVAL;
+  for (int64_t n = 0; n < rows; ++n)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      const float *wb = w + n * K + 32 * b;
+      double a = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs((double)wb[i]) > a) a = fabs((double)wb[i]);
+      int E = 0;
+      if (a > 0.0) {
+        int ex;
+        frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+        E = (ex - 1) - 2 + 127;
+        if (E < 0) E = 0;
+        if (E > 254) E = 254;
+      }
+      e8[n * (K / 32) + b] = (uint8_t)E;
+      for (int i = 0; i < 32; ++i) {
+        const double v = ldexp((double)wb[i], 127 - E);
+        const double m = fabs(v);
+        int c = 7; /* saturate above 6 */
+        for (int j = 0; j < 7; ++j) {
+          const double mid = 0.5 * (grid[j] + grid[j + 1]);
+          if (m < mid || (m == mid && (j & 1) == 0)) { /* tie: the even code j */
+            c = j;
+            break;
+          }
+        }
+        const uint8_t nib = (uint8_t)(c | ((wb[i] < 0.0f || (wb[i] == 0.0f && signbit(wb[i]))) ? 8 : 0));
+        const int64_t k = 32 * b + i;
+        uint8_t *dst = q4 + n * (K / 2) + k / 2;
+        *dst = (k & 1) ? (uint8_t)((*dst & 0x0f) | (nib << 4)) : (uint8_t)((*dst & 0xf0) | nib);
+      }
+    }
+  return OR_OK;
+}
+
 /* Exact int32 dot of one 32-block: weights of row n of a code matrix
  * against int8 activations a[K], over k in [32b, 32b+32). */
 static int32_t or_block_dot(const uint8_t *mat, int64_t K, int64_t n, int fmt,

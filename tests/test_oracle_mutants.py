@@ -22,6 +22,7 @@ CHECKS = [
     pins.check_int4_quant_closed_form, pins.check_int4_quant_properties,
     pins.check_int8_decode_prefill_vs_bruteforce, pins.check_int8_block_dots,
     pins.check_mxfp4_decode_prefill_vs_bruteforce, pins.check_mxfp4_block_dots,
+    pins.check_int8_quant, pins.check_mxfp4_quant,
 ]
 
 # (name, text in the oracle, replacement)
@@ -87,6 +88,16 @@ MUTANTS = [
     ("int4 nibbles packed high first",
      "*byte = (k & 1) ? (uint8_t)((*byte & 0x0f) | (nib << 4)) : (uint8_t)((*byte & 0xf0) | nib);",
      "*byte = (k & 1) ? (uint8_t)((*byte & 0xf0) | nib) : (uint8_t)((*byte & 0x0f) | (nib << 4));"),
+    ("int8 scale from max / 128", "volatile float t = a / 127.0f;",
+     "volatile float t = a / 128.0f;"),
+    ("int8 clamps at -127", "if (r < -128) r = -128;", "if (r < -127) r = -127;"),
+    ("mxfp4 shared exponent off by one", "E = (ex - 1) - 2 + 127;", "E = (ex - 1) - 1 + 127;"),
+    ("mxfp4 ties away from zero", "if (m < mid || (m == mid && (j & 1) == 0)) {", "if (m < mid) {"),
+    ("mxfp4 codes packed high first",
+     "*dst = (k & 1) ? (uint8_t)((*dst & 0x0f) | (nib << 4)) : (uint8_t)((*dst & 0xf0) | nib);",
+     "*dst = (k & 1) ? (uint8_t)((*dst & 0xf0) | nib) : (uint8_t)((*dst & 0x0f) | (nib << 4));"),
+    ("mxfp4 drops the sign of zero", "(wb[i] < 0.0f || (wb[i] == 0.0f && signbit(wb[i])))",
+     "(wb[i] < 0.0f)"),
     ("router weight transposed", "acc += or_bf16(x[t * H + k]) * or_bf16(w[e * H + k]);",
      "acc += or_bf16(x[t * H + k]) * or_bf16(w[k * E + e]);"),
     ("router drops the last column", "for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])",

@@ -614,6 +614,103 @@ def check_int4_quant_properties():
     assert np.all(np.abs(np.take_along_axis(qg, g[:, :, None], 2)) == 7)
 
 
+def _int8_bruteforce(w):
+    w = np.asarray(w, np.float32)
+    rows, K = w.shape
+    g = w.reshape(rows, K // 64, 64)
+    a = np.max(np.abs(g), axis=2)
+    s16 = (a / np.float32(127.0)).astype(np.float16)
+    sf = s16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (g / sf[:, :, None]).astype(np.float64)
+    r = np.sign(ratio) * np.floor(np.abs(ratio) + 0.5)
+    r = np.where(sf[:, :, None] == 0, 0, np.clip(r, -128, 127))
+    return r.astype(np.int8).reshape(rows, K), s16.view(np.uint16)
+
+
+def check_int8_quant():
+    w = _int4_cases()
+    # a negative maximum whose fp16 scale (a subnormal, 10 * 2^-24) rounds
+    # down by 4.5 %: its code would be -132.7, clamped to -128
+    w[5, :64] = np.linspace(-7e-5, 7e-5, 64)
+    w[5, 0] = -127 * 10.45 * 2.0 ** -24
+    q, sc = oracle.quantize_int8_gs64(w)
+    bq, bs = _int8_bruteforce(w)
+    assert np.array_equal(sc, bs) and np.array_equal(q, bq)
+    assert (q == -128).any()                     # the subnormal-scale groups reach -128
+    # closed form: w = q * 2^-6 with max |q| = 127 gives back q and 2^-6
+    rng = np.random.default_rng(34)
+    qq = rng.integers(-127, 128, size=(3, 128))
+    qq[:, 0], qq[:, 64] = 127, -127
+    q2, s2 = oracle.quantize_int8_gs64((qq * 2.0 ** -6).astype(np.float32))
+    assert np.all(s2 == 0x2400) and np.array_equal(q2, qq)
+
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mxfp4_bruteforce(w):
+    """Shared exponent from the fp32 bit patterns; each element the nearest
+    of the 16 codes' values, ties to the code with an even magnitude index."""
+    w = np.asarray(w, np.float32)
+    rows, K = w.shape
+    blk = w.reshape(rows, K // 32, 32)
+    a = np.max(np.abs(blk), axis=2)
+    bits = a.view(np.uint32)
+    expf = ((bits >> 23) & 0xFF).astype(np.int64)
+    floor_log2 = np.where(expf > 0, expf - 127, 0)
+    sub = (expf == 0) & (a > 0)
+    if sub.any():                                   # subnormal maxima: E clamps to 0 anyway
+        floor_log2 = np.where(sub, -150, floor_log2)
+    E = np.where(a > 0, np.clip(floor_log2 - 2 + 127, 0, 254), 0).astype(np.int64)
+    v = blk.astype(np.float64) * np.exp2(127.0 - E)[:, :, None]
+    m = np.abs(v)
+    dist = np.abs(m[..., None] - E2M1_VALUES)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    idx = np.where(m > 6.0, 7, idx)
+    code = idx | np.where(np.signbit(blk), 8, 0)
+    code = code.reshape(rows, K).astype(np.uint8)
+    return code[:, 0::2] | (code[:, 1::2] << 4), E.astype(np.uint8)
+
+
+def check_mxfp4_quant():
+    rng = np.random.default_rng(35)
+    w = (rng.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    w[0, :32] = 0.0
+    w[0, 32:64] = -0.0
+    w[1, :32] = rng.uniform(-1e-39, 1e-39, 32)               # subnormal maximum
+    w[2, :32] = np.array([6, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25, 5] * 4) * 2.0 ** -9  # ties
+    w[2, 32:64] = np.array([7, 6.5, -7.9, 0.3] * 8) * 2.0 ** -9                      # saturation
+    w[3] = rng.uniform(-3e38, 3e38, 128)                     # near the fp32 maximum
+    w[4, :32] = 2.0 ** -126                                  # exact power of two maxima
+    q, e = oracle.quantize_mxfp4(w)
+    bq, be = _mxfp4_bruteforce(w)
+    assert np.array_equal(e, be) and np.array_equal(q, bq)
+    # the tie row: max 6 * 2^-9 gives X = -9 (E 118); ties go to the even code
+    assert e[2, 0] == 118
+    codes = np.stack([q[2] & 15, q[2] >> 4], axis=1).reshape(-1)[:8]
+    assert list(codes) == [7, 6, 4, 4, 2, 2, 0, 6]
+    # closed form: values on the grid times 2^X round-trip
+    vals = rng.choice(np.concatenate([E2M1_VALUES, -E2M1_VALUES[1:]]), size=(2, 64))
+    vals[:, 0] = vals[:, 32] = 6.0
+    q2, e2 = oracle.quantize_mxfp4((vals * 2.0 ** -5).astype(np.float32))
+    assert np.all(e2 == 127 - 5)
+    c2 = np.stack([q2 & 15, q2 >> 4], axis=2).reshape(2, 64)
+    dec = E2M1_VALUES[c2 & 7] * np.where(c2 & 8, -1.0, 1.0)
+    assert np.array_equal(dec, vals)
+
+
+def test_int8_quant():
+    check_int8_quant()
+
+
+def test_mxfp4_quant():
+    check_mxfp4_quant()
+
+
 def test_int4_quant_vs_bruteforce():
     check_int4_quant_vs_bruteforce()
 
