@@ -372,8 +372,9 @@ def secondary_router(name, spec, T, steps, warmup):
             "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
 
 
-def secondary_convert(name, spec, experts, src, steps, warmup):
-    """Float weights -> int4 gs64 container (coli_moe_quantize_int4_gs64) for
+def secondary_convert(name, spec, experts, src, steps, warmup, fmt="int4"):
+    """Float weights -> an expert container (int4 gs64, int8 gs64 or MXFP4:
+    coli_moe_quantize_int4_gs64 / _int8_gs64 / coli_moe_quantize_mxfp4) for
     `experts` experts of the spec's shape stored back to back, in one call."""
     import torch
 
@@ -384,12 +385,16 @@ def secondary_convert(name, spec, experts, src, steps, warmup):
                    "f32": (torch.float32, coli.COLI_SRC_F32)}[src]
     n = experts * 3 * spec.inter * spec.hidden
     w = synth.make_float_weights(n, seed=0, device="cuda", dtype=dtype)
-    q4 = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
-    sc = torch.empty(n // 64, dtype=torch.int16, device="cuda")
+    # codes: n/2 bytes (n for int8); scales: n/32 bytes in every format (an
+    # fp16 per 64 weights, or an E8M0 byte per 32)
+    q4 = torch.empty(n if fmt == "int8" else n // 2, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
     rows = n // spec.hidden
+    fn = {"int4": coli.coli_moe_quantize_int4_gs64, "int8": coli.coli_moe_quantize_int8_gs64,
+          "mxfp4": coli.coli_moe_quantize_mxfp4}[fmt]
 
     def step(i):
-        coli.coli_moe_quantize_int4_gs64(w, code, rows, spec.hidden, q4, sc)
+        fn(w, code, rows, spec.hidden, q4, sc)
 
     for i in range(warmup):
         step(i)
@@ -402,13 +407,13 @@ def secondary_convert(name, spec, experts, src, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     kern = traced_kernels(lambda: step(0), reps=max(4, steps // 2))
-    us = kern["quantize_int4"]["avg_us"]
-    nbytes = n * w.element_size() + n // 2 + 2 * (n // 64)  # read once, write once
+    us = kern["quantize_" + fmt]["avg_us"]
+    nbytes = n * w.element_size() + q4.numel() + sc.numel()  # read once, write once
     del w, q4, sc
-    return {"workload": name, "path": "convert", "experts": experts, "values": n,
-            "src": src, "ms_per_call": round(ms, 4),
+    return {"workload": name, "path": "convert", "weights": fmt, "experts": experts,
+            "values": n, "src": src, "ms_per_call": round(ms, 4),
             "weights_per_s": round(n / (ms * 1e-3), 1),
-            "quantize_int4_us": round(us, 2),
+            "quantize_us": round(us, 2),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
@@ -459,8 +464,10 @@ def main():
                                           w.layers, args.steps, args.warmup)), flush=True)
         return
     if args.convert_only:
-        print(json.dumps(secondary_convert("glm_convert_32experts_bf16", synth.WORKLOADS["glm"].spec,
-                                           32, "bf16", args.steps, args.warmup)), flush=True)
+        for fmt in ("int4", "int8", "mxfp4"):
+            print(json.dumps(secondary_convert("glm_convert_%s_32experts_bf16" % fmt,
+                                               synth.WORKLOADS["glm"].spec, 32, "bf16",
+                                               args.steps, args.warmup, fmt=fmt)), flush=True)
         return
     w = synth.WORKLOADS["glm"]
     spec, T, layers = w.spec, 1, w.layers
@@ -516,6 +523,10 @@ def main():
                                            20, 3))
         secondary.append(secondary_convert("glm_convert_8experts_f32", w.spec, 8, "f32",
                                            20, 3))
+        secondary.append(secondary_convert("glm_convert_int8_32experts_bf16", w.spec, 32, "bf16",
+                                           20, 3, fmt="int8"))
+        secondary.append(secondary_convert("glm_convert_mxfp4_32experts_bf16", w.spec, 32,
+                                           "bf16", 20, 3, fmt="mxfp4"))
         ow = synth.WORKLOADS["olmoe"]
         secondary.append(secondary_decode("olmoe_decode_T1", ow.spec, 1, 0.0, 4, 200, 10))
         secondary.append(secondary_prefill("olmoe_prefill_T512", ow.spec, 512, 0.0, 20, 3, copies=4))

@@ -274,6 +274,31 @@ int coli_moe_quantize_q8_0(const void *src, int32_t src_dtype, int64_t n,
 int coli_moe_quantize_int4_gs64(const void *src, int32_t src_dtype, int64_t rows,
                                 int64_t K, uint8_t *q4, uint16_t *scales, void *stream);
 
+/* The int8 gs64 container (COLI_WEIGHTS_INT8) from float weights: the int4
+ * rule above widened to bytes -- per group of 64, s16 = fp16_RNE(max|w| /
+ * 127), q = round-half-away-from-zero(w / float(s16)) clamped to [-128, 127]
+ * (0 for a group whose s16 is 0).  The pages require int8 experts in the
+ * MTP layer (tantan.ink post, section "我看到的几个坑") without the rule.
+ *  src [rows*K] bf16 or fp32, 16-byte aligned, finite, max|w| <= 127 * 65504;
+ *  q [rows*K] int8, 8-byte aligned (byte k of row n at n*K + k);
+ *  scales [rows*K/64] fp16 bits, 2-byte aligned.  K % 64 == 0,
+ *  rows*K <= 2^36.  Errors as for coli_moe_quantize_int4_gs64. */
+int coli_moe_quantize_int8_gs64(const void *src, int32_t src_dtype, int64_t rows,
+                                int64_t K, int8_t *q, uint16_t *scales, void *stream);
+
+/* MXFP4 (COLI_WEIGHTS_MXFP4) from float weights by the OCP microscaling
+ * conversion: per block of 32 consecutive weights, E = floor(log2 max|w|) -
+ * 2 + 127 clamped to [0, 254] (0 for an all-zero block), stored as the E8M0
+ * byte; each weight becomes the FP4 E2M1 code nearest to w / 2^(E-127),
+ * ties to the even code, saturating at +-6, with the sign of w (also of a
+ * zero).  The pages list fp4 experts (ai-tools-nav review, model family
+ * table); this is the published MX conversion.
+ *  src [rows*K] bf16 or fp32, 16-byte aligned, finite;  q4 [rows*K/2]
+ *  nibbles (even k low), 4-byte aligned;  e8m0 [rows*K/32] bytes.
+ *  K % 32 == 0, rows*K <= 2^36.  Errors as for coli_moe_quantize_int4_gs64. */
+int coli_moe_quantize_mxfp4(const void *src, int32_t src_dtype, int64_t rows, int64_t K,
+                            uint8_t *q4, uint8_t *e8m0, void *stream);
+
 /* The exact int32 block dot products of one weight matrix of one expert
  * with T rows of int8 activations:
  *   dots[t][n][b] = sum_{k in [32b, 32b+32)} qw[n][k] * q_act[t][k]
@@ -300,7 +325,8 @@ enum {
   COLI_K_ROUTE_FUSED = 0, COLI_K_TOPK = 1, COLI_K_GROUP = 2, COLI_K_DECODE_GATEUP = 3,
   COLI_K_DECODE_DOWN = 4, COLI_K_COMBINE = 5, COLI_K_QUANTIZE = 6, COLI_K_PLAN = 7,
   COLI_K_GEMM_GATEUP = 8, COLI_K_GEMM_DOWN = 9, COLI_K_BLOCK_DOTS = 10,
-  COLI_K_ROUTER_LOGITS = 11, COLI_K_QUANTIZE_INT4 = 12, COLI_K_COUNT = 13
+  COLI_K_ROUTER_LOGITS = 11, COLI_K_QUANTIZE_INT4 = 12, COLI_K_QUANTIZE_INT8 = 13,
+  COLI_K_QUANTIZE_MXFP4 = 14, COLI_K_COUNT = 15
 };
 typedef struct coli_moe_trace {
   void **start;     /* hipEvent_t[capacity] */

@@ -43,7 +43,7 @@ class _TraceC(ctypes.Structure):
 
 KERNEL_NAMES = ["route_fused", "route_topk", "route_group", "decode_gateup", "decode_down",
                 "combine", "quantize_q8_0", "plan", "gemm_gateup", "gemm_down", "block_dots",
-                "router_logits", "quantize_int4"]
+                "router_logits", "quantize_int4", "quantize_int8", "quantize_mxfp4"]
 
 
 class _RouteC(ctypes.Structure):
@@ -77,6 +77,8 @@ def _load():
         lib.coli_moe_forward_prefill.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
         lib.coli_moe_quantize_q8_0.argtypes = [vp, i32, i64, vp, vp, vp]
         lib.coli_moe_quantize_int4_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+        lib.coli_moe_quantize_int8_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+        lib.coli_moe_quantize_mxfp4.argtypes = [vp, i32, i64, i64, vp, vp, vp]
         lib.coli_moe_block_dots.argtypes = [P(_LayerC), i32, i32, vp, i32, vp, vp]
         lib.coli_moe_strerror.argtypes = [ctypes.c_int]
         lib.coli_moe_strerror.restype = ctypes.c_char_p
@@ -86,7 +88,8 @@ def _load():
         lib.coli_moe_version.restype = ctypes.c_char_p
         for f in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
                   "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
-                  "coli_moe_quantize_int4_gs64"):
+                  "coli_moe_quantize_int4_gs64", "coli_moe_quantize_int8_gs64",
+                  "coli_moe_quantize_mxfp4"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -214,6 +217,17 @@ def coli_moe_quantize_int4_gs64(src, src_dtype: int, rows: int, K: int, q4, scal
                                 stream=None):
     _check("coli_moe_quantize_int4_gs64", _load().coli_moe_quantize_int4_gs64(
         _ptr(src), src_dtype, rows, K, _ptr(q4), _ptr(scales), _stream(stream)))
+
+
+def coli_moe_quantize_int8_gs64(src, src_dtype: int, rows: int, K: int, q, scales,
+                                stream=None):
+    _check("coli_moe_quantize_int8_gs64", _load().coli_moe_quantize_int8_gs64(
+        _ptr(src), src_dtype, rows, K, _ptr(q), _ptr(scales), _stream(stream)))
+
+
+def coli_moe_quantize_mxfp4(src, src_dtype: int, rows: int, K: int, q4, e8m0, stream=None):
+    _check("coli_moe_quantize_mxfp4", _load().coli_moe_quantize_mxfp4(
+        _ptr(src), src_dtype, rows, K, _ptr(q4), _ptr(e8m0), _stream(stream)))
 
 
 def coli_moe_block_dots(layer: Layer, expert: int, matrix: int, q_act, T: int, dots,

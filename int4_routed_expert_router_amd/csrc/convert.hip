@@ -37,18 +37,23 @@ COLI_DEV uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
 }
 
+// 8-lane maximum of a >= 0 (non-negative floats order as their bit
+// patterns do); the 8 lanes are consecutive and aligned.
+COLI_DEV float max8(float a) {
+  uint32_t ab = __float_as_uint(a);
+  ab = max(ab, dpp_u32<kQuadXor1>(ab));
+  ab = max(ab, dpp_u32<kQuadXor2>(ab));
+  ab = max(ab, dpp_u32<kHalfRowMirror>(ab));  // lane i <-> 7 - i: the other quad
+  return __uint_as_float(ab);
+}
+
 // One lane's share of a group: its 8 values in, its 8 nibbles and the
 // group's scale out.  The 8 lanes of a group are consecutive and aligned.
 COLI_DEV void quantize_chunk(const float v[8], uint32_t &packed, uint16_t &s16_out) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-  // a >= 0, and non-negative floats order as their bit patterns do
-  uint32_t ab = __float_as_uint(a);
-  ab = max(ab, dpp_u32<kQuadXor1>(ab));
-  ab = max(ab, dpp_u32<kQuadXor2>(ab));
-  ab = max(ab, dpp_u32<kHalfRowMirror>(ab));  // lane i <-> 7 - i: the other quad
-  a = __uint_as_float(ab);
+  a = max8(a);
   const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(a, 7.0f));
   const float sf = f16_to_f32(s16);
   packed = 0;
@@ -91,6 +96,69 @@ COLI_DEV void quantize_chunk(const float v[8], uint32_t &packed, uint16_t &s16_o
   s16_out = s16;
 }
 
+// int8 gs64: the same rule with 127 and byte codes.  Division and rounding
+// as in quantize_chunk (round half away from zero from t = trunc(2q), where
+// clamping t to [-256, 254] clamps the code to [-128, 127]).
+COLI_DEV void quantize_chunk8(const float v[8], uint32_t &lo, uint32_t &hi,
+                              uint16_t &s16_out) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = max8(a);
+  const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(a, 127.0f));
+  const float sf = f16_to_f32(s16);
+  uint32_t b[2] = {0u, 0u};
+  if (sf != 0.0f) {
+    const float h = 0.5f * sf;
+    const float y0 = __builtin_amdgcn_rcpf(h);
+    const float y = fmaf(fmaf(-h, y0, 1.0f), y0, y0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q2 = v[i] * y;
+      q2 = fmaf(fmaf(-h, q2, v[i]), y, q2);
+      q2 = fmaf(fmaf(-h, q2, v[i]), y, q2);
+      int t = (int)q2;
+      t = max(-256, min(254, t));
+      const int r = (t + 1 + (t >> 31)) >> 1;
+      b[i >> 2] |= (uint32_t)(r & 0xff) << (8 * (i & 3));
+    }
+  }
+  lo = b[0];
+  hi = b[1];
+  s16_out = s16;
+}
+
+// MXFP4 (OCP MX conversion): a block of 32 is 4 consecutive lanes.  The
+// shared exponent floor(log2 max|w|) - 2 is read from the maximum's fp32
+// exponent field e: E8M0 byte E = max(e - 2, 0) (a subnormal or zero maximum
+// gives 0).  Each value is scaled by 2^(127 - E) (exact: the result is below
+// 8, and a result that small to be rounded is code 0 anyway) and its E2M1
+// magnitude code counts the grid midpoints it reaches -- strictly for the
+// midpoints above an even code, inclusively for those above an odd code, so
+// ties go to the even code -- saturating at 7 (6.0).  The sign bit is the
+// value's own, zero included.
+COLI_DEV void quantize_chunk_fp4(const float v[8], uint32_t &packed, uint8_t &e_out) {
+  uint32_t ab = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ab = max(ab, __float_as_uint(v[i]) & 0x7fffffffu);
+  ab = max(ab, dpp_u32<kQuadXor1>(ab));
+  ab = max(ab, dpp_u32<kQuadXor2>(ab));
+  const int e = (int)(ab >> 23);
+  const uint32_t E = (uint32_t)max(e - 2, 0);
+  const float f = __uint_as_float((254u - E) << 23);  // 2^(127 - E)
+  packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float m = fabsf(v[i] * f);
+    const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                       (uint32_t)(m > 5.0f);
+    const uint32_t nib = c | ((__float_as_uint(v[i]) >> 28) & 8u);
+    packed |= nib << (4 * i);
+  }
+  e_out = (uint8_t)E;
+}
+
 COLI_DEV void load_chunk(const void *src, int src_dtype, int64_t t, float v[8]) {
   if (src_dtype == COLI_SRC_BF16) {
     const uint4 u = reinterpret_cast<const uint4 *>(src)[t];
@@ -124,6 +192,38 @@ __global__ void __launch_bounds__(kThreads) quantize_int4_kernel(const void *__r
   if ((t & 7) == 0) scales[t >> 3] = s16;
 }
 
+template <int SRC>
+__global__ void __launch_bounds__(kThreads) quantize_int8_kernel(const void *__restrict__ src,
+                                                                 int64_t ngroups,
+                                                                 uint2 *__restrict__ q,
+                                                                 uint16_t *__restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 8-value chunk
+  if ((t >> 3) >= ngroups) return;  // whole 8-lane groups leave together
+  float v[8];
+  load_chunk(src, SRC, t, v);
+  uint32_t lo, hi;
+  uint16_t s16;
+  quantize_chunk8(v, lo, hi, s16);
+  q[t] = make_uint2(lo, hi);
+  if ((t & 7) == 0) scales[t >> 3] = s16;
+}
+
+template <int SRC>
+__global__ void __launch_bounds__(kThreads) quantize_mxfp4_kernel(const void *__restrict__ src,
+                                                                  int64_t nblocks,
+                                                                  uint32_t *__restrict__ q4,
+                                                                  uint8_t *__restrict__ e8) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 8-value chunk
+  if ((t >> 2) >= nblocks) return;  // whole 4-lane blocks leave together
+  float v[8];
+  load_chunk(src, SRC, t, v);
+  uint32_t packed;
+  uint8_t E;
+  quantize_chunk_fp4(v, packed, E);
+  q4[t] = packed;
+  if ((t & 3) == 0) e8[t >> 2] = E;
+}
+
 }  // namespace
 
 int launch_quantize_int4(const void *src, int src_dtype, int64_t n, uint8_t *q4,
@@ -137,6 +237,34 @@ int launch_quantize_int4(const void *src, int src_dtype, int64_t n, uint8_t *q4,
   else
     launch_k(COLI_K_QUANTIZE_INT4, quantize_int4_kernel<COLI_SRC_F32>, grid, dim3(kThreads),
              0, s, src, n / 64, q, scales);
+  return hip_status(hipGetLastError());
+}
+
+int launch_quantize_int8(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *scales,
+                         hipStream_t s) {
+  const int64_t chunks = n / 8;
+  const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
+  uint2 *qq = reinterpret_cast<uint2 *>(q);
+  if (src_dtype == COLI_SRC_BF16)
+    launch_k(COLI_K_QUANTIZE_INT8, quantize_int8_kernel<COLI_SRC_BF16>, grid, dim3(kThreads), 0,
+             s, src, n / 64, qq, scales);
+  else
+    launch_k(COLI_K_QUANTIZE_INT8, quantize_int8_kernel<COLI_SRC_F32>, grid, dim3(kThreads), 0,
+             s, src, n / 64, qq, scales);
+  return hip_status(hipGetLastError());
+}
+
+int launch_quantize_mxfp4(const void *src, int src_dtype, int64_t n, uint8_t *q4, uint8_t *e8,
+                          hipStream_t s) {
+  const int64_t chunks = n / 8;
+  const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
+  uint32_t *q = reinterpret_cast<uint32_t *>(q4);
+  if (src_dtype == COLI_SRC_BF16)
+    launch_k(COLI_K_QUANTIZE_MXFP4, quantize_mxfp4_kernel<COLI_SRC_BF16>, grid, dim3(kThreads),
+             0, s, src, n / 32, q, e8);
+  else
+    launch_k(COLI_K_QUANTIZE_MXFP4, quantize_mxfp4_kernel<COLI_SRC_F32>, grid, dim3(kThreads),
+             0, s, src, n / 32, q, e8);
   return hip_status(hipGetLastError());
 }
 

@@ -61,6 +61,10 @@ int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, u
                          hipStream_t s);
 int launch_quantize_int4(const void *src, int src_dtype, int64_t n, uint8_t *q4,
                          uint16_t *scales, hipStream_t s);
+int launch_quantize_int8(const void *src, int src_dtype, int64_t n, int8_t *q, uint16_t *scales,
+                         hipStream_t s);
+int launch_quantize_mxfp4(const void *src, int src_dtype, int64_t n, uint8_t *q4, uint8_t *e8,
+                          hipStream_t s);
 int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_act, int T,
                       int32_t *dots, hipStream_t s);
 
