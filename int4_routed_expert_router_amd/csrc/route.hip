@@ -38,32 +38,69 @@ COLI_DEV uint64_t select_key(float s, int e) {
   return ((uint64_t)hi << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-COLI_DEV uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// Wave-wide reductions with DPP moves (no LDS round trips): four steps
+// inside each row of 16 lanes (swap neighbours, swap pairs, mirror halves of
+// 8, mirror the row), then row_bcast:15 and row_bcast:31 carry the row
+// results up, so that lane 63 holds the reduction of all 64 lanes; it is read
+// into a scalar register.  Rows a broadcast does not write keep `idle`, the
+// operation's neutral value.  The operation order is fixed, so a token's
+// result never depends on which wavefront or batch computes it.
+template <int CTRL, int ROWS = 0xf>
+COLI_DEV uint32_t dpp_u32(uint32_t idle, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)idle, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS = 0xf>
+COLI_DEV float dpp_f32(float idle, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(idle), __float_as_int(v), CTRL,
+                                                    ROWS, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kRowMirror = 0x140;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
 
-// DPP move of a 64-bit value within rows of 16 lanes.
-template <int CTRL>
-COLI_DEV uint64_t dpp64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+COLI_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kQuadXor1>(0u, v));
+  v = max(v, dpp_u32<kQuadXor2>(0u, v));
+  v = max(v, dpp_u32<kHalfMirror>(0u, v));
+  v = max(v, dpp_u32<kRowMirror>(0u, v));
+  v = max(v, dpp_u32<kBcast15, 0xa>(0u, v));
+  v = max(v, dpp_u32<kBcast31, 0xc>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+COLI_DEV float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kQuadXor1>(-FLT_MAX, v));
+  v = fmaxf(v, dpp_f32<kQuadXor2>(-FLT_MAX, v));
+  v = fmaxf(v, dpp_f32<kHalfMirror>(-FLT_MAX, v));
+  v = fmaxf(v, dpp_f32<kRowMirror>(-FLT_MAX, v));
+  v = fmaxf(v, dpp_f32<kBcast15, 0xa>(-FLT_MAX, v));
+  v = fmaxf(v, dpp_f32<kBcast31, 0xc>(-FLT_MAX, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+COLI_DEV float wave_sum_f32(float v) {
+  v += dpp_f32<kQuadXor1>(0.0f, v);
+  v += dpp_f32<kQuadXor2>(0.0f, v);
+  v += dpp_f32<kHalfMirror>(0.0f, v);
+  v += dpp_f32<kRowMirror>(0.0f, v);
+  v += dpp_f32<kBcast15, 0xa>(0.0f, v);
+  v += dpp_f32<kBcast31, 0xc>(0.0f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Wave-wide maximum of a 64-bit key: four DPP steps inside each 16-lane row
-// (swap neighbours, swap pairs, mirror halves of 8, mirror the row), then
-// the four row maxima are read into scalar registers.
-COLI_DEV uint64_t wave_max_key(uint64_t k) {
-  k = umax64(k, dpp64<0xB1>(k));   // quad_perm [1,0,3,2]
-  k = umax64(k, dpp64<0x4E>(k));   // quad_perm [2,3,0,1]
-  k = umax64(k, dpp64<0x141>(k));  // row_half_mirror
-  k = umax64(k, dpp64<0x140>(k));  // row_mirror
-  uint64_t r = 0;
+// Sorts a lane's NPL (key, logit) entries by key, descending (odd-even
+// transposition: NPL rounds of neighbour compare-exchanges).
+template <int NPL>
+COLI_DEV void sort_lane(uint64_t (&key)[NPL], float (&lg)[NPL]) {
 #pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
-    r = umax64(r, ((uint64_t)hi << 32) | lo);
-  }
-  return r;
+  for (int rnd = 0; rnd < NPL; ++rnd)
+#pragma unroll
+    for (int i = rnd & 1; i + 1 < NPL; i += 2) {
+      const bool sw = key[i + 1] > key[i];
+      const uint64_t ka = key[i], kb = key[i + 1];
+      const float la = lg[i], lb = lg[i + 1];
+      key[i] = sw ? kb : ka;
+      key[i + 1] = sw ? ka : kb;
+      lg[i] = sw ? lb : la;
+      lg[i + 1] = sw ? la : lb;
+    }
 }
 
 // One wavefront selects the k experts of one token.  Lane j < k ends with
@@ -95,37 +132,45 @@ COLI_DEV float topk_wave(const float *__restrict__ lg_row, const float *__restri
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + 64 * i < E) m = fmaxf(m, lg[i]);
-    m = wave_max(m);
+    m = wave_max_f32(m);
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + 64 * i < E) z += expf(lg[i] - m);
-    z = wave_sum(z);
+    z = wave_sum_f32(z);
   }
+  // Each lane keeps its entries sorted, so its best is key[0].  A round takes
+  // the largest score image over the wave (32-bit DPP max); among lanes whose
+  // best has that score (ties are rare) the lower expert index, i.e. the
+  // larger low word, wins.  The owner drops its head.
+  sort_lane<NPL>(key, lg);
   float my_l = 0.0f;
   int me = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) best = umax64(best, key[i]);
-    const uint64_t win = wave_max_key(best);
-    const int e = (int)(~(uint32_t)win);
-    const int owner = e & 63, slot = e >> 6;
-    float wl = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      if (i == slot) {
-        wl = lg[i];
-        if (lane == owner) key[i] = 0ull;  // taken
-      }
+    const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+    const uint32_t mx = wave_max_u32(hi);
+    uint64_t ball = __ballot(hi == mx);
+    if (__popcll(ball) > 1) {  // all lanes take part in the reduction
+      const uint32_t mlo = wave_max_u32(hi == mx ? lo : 0u);
+      ball = __ballot(hi == mx && lo == mlo);
     }
-    wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), owner));
+    const int owner = __ffsll((long long)ball) - 1;
+    const int e = (int)~(uint32_t)__builtin_amdgcn_readlane((int)lo, owner);
+    const float wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg[0]), owner));
+    if (lane == owner) {
+#pragma unroll
+      for (int i = 0; i + 1 < NPL; ++i) {
+        key[i] = key[i + 1];
+        lg[i] = lg[i + 1];
+      }
+      key[NPL - 1] = 0ull;
+    }
     if (lane == j) {
       me = e;
       my_l = wl;
     }
   }
   float w = (flags & COLI_ROUTE_SIGMOID) ? 1.0f / (1.0f + expf(-my_l)) : expf(my_l - m) / z;
-  if (flags & COLI_ROUTE_RENORM) w = w / wave_sum(lane < k ? w : 0.0f);
+  if (flags & COLI_ROUTE_RENORM) w = w / wave_sum_f32(lane < k ? w : 0.0f);
   *my_e = me;
   return w * routed_scale;
 }
@@ -146,29 +191,36 @@ __device__ int topk_token(const float *__restrict__ lg_row, const float *__restr
 }
 
 // Single token: one wavefront does the selection and the grouping, which
-// for one token has a closed form -- pair j's position is the rank of its
-// expert among the k winners, and offsets[e] counts the winners below e.
+// for one token has a closed form -- offsets[e] counts the winners below e,
+// and pair j's position is offsets[its expert].  The winners are marked in
+// an LDS table of E flags; one ballot per 64 experts gives their bit masks,
+// and the counts below follow from popcounts.
 template <int NPL>
 __global__ void __launch_bounds__(64) single_kernel(const float *__restrict__ logits,
                                                     const float *__restrict__ bias, int E, int k,
                                                     uint32_t flags, float routed_scale,
                                                     coli_moe_route_t r) {
+  __shared__ uint32_t won[64 * NPL];
   const int lane = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) won[lane + 64 * i] = 0u;
   int me;
   const float w = topk_wave<NPL>(logits, bias, E, k, flags, routed_scale, &me);
-  int rank = 0;
-  int cnt_lt[NPL], hit[NPL];
+  if (lane < k) won[me] = 1u;
+  __syncthreads();
+  int hit[NPL], cnt_lt[NPL];
+  int below = 0;           // winners in the 64-expert words before word i
+  int rank = 0;            // winners below this lane's own expert (lanes < k)
+  const int my_word = me >> 6;
+  const uint64_t my_bits = (1ull << (me & 63)) - 1ull;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) cnt_lt[i] = hit[i] = 0;
-  for (int j = 0; j < k; ++j) {
-    const int ej = __builtin_amdgcn_readlane(me, j);
-    rank += ej < me;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      cnt_lt[i] += ej < e;
-      hit[i] |= ej == e;
-    }
+  for (int i = 0; i < NPL; ++i) {
+    hit[i] = (int)won[lane + 64 * i];
+    const uint64_t mask = __ballot(hit[i] != 0);
+    cnt_lt[i] = below + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    if (my_word == i) rank = below + __popcll(mask & my_bits);
+    below += __popcll(mask);
   }
   if (lane < k) {
     r.topk_idx[lane] = me;
