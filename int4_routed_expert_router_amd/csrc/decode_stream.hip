@@ -17,7 +17,9 @@
 // fp32 conversion of each sign-extended byte (see the codecs below).  Lane partials of
 // several rows are combined with a reduce-scatter (each shuffle step halves
 // the values a lane carries).  A token's arithmetic does not depend on the
-// other tokens of the batch.
+// other tokens of the batch.  With I = 2048, down runs on the bf16 matrix
+// cores instead (down_mfma_kernel): the weights dequantised the same way are
+// the B operand and the tokens' h halves the A operand.
 #include "device_common.h"
 #include "internal.h"
 
@@ -130,6 +132,7 @@ COLI_DEV void opaque(uint4 &w) {
 // each 8 weights; bf16 136 + q from one v_bitop3 per pair.
 struct CodecI4 {
   static constexpr int Q = 1;
+  static constexpr int kChunksPerScale = 2;
   static constexpr float kBias = (float)kNibBias;
   static constexpr int64_t bytes(int64_t codes) { return codes / 2; }
   // fp16 scale of 32-value chunk c of row n of a K-wide matrix, whose
@@ -163,6 +166,15 @@ struct CodecI4 {
     const int o = w >> 3, k = w & 7;
     return 2 * (4 * o + (k & 3)) + (k >> 2);
   }
+  // eight weights (one dword) as four bf16 pairs in the activation pair order
+  COLI_DEV static void kgroup(const uint32_t *dw, uint32_t out[4]) {
+    nib8_to_bf16x4(dw[0], out[0], out[1], out[2], out[3]);
+  }
+  // raw scale of chunk cw (0..15) from 16 bytes holding 8 fp16 group scales
+  COLI_DEV static uint16_t scale16(const uint4 &v, int cw) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    return (uint16_t)(d[cw >> 2] >> (16 * ((cw >> 1) & 1)));
+  }
 };
 
 // int8 (one byte per weight): two quads per chunk; natural pairs (k, k+1).
@@ -171,6 +183,7 @@ struct CodecI4 {
 // zero), so the pairs hold q itself: no bias, no cancellation.
 struct CodecI8 {
   static constexpr int Q = 2;
+  static constexpr int kChunksPerScale = 2;
   static constexpr float kBias = 0.0f;
   static constexpr int64_t bytes(int64_t codes) { return codes; }
   // fp16 scale of 32-value chunk c of row n of a K-wide matrix, whose
@@ -203,6 +216,19 @@ struct CodecI8 {
     return a;
   }
   COLI_DEV static int half_index(int w) { return w; }
+  // eight weights (two dwords) as four bf16 pairs, natural order
+  COLI_DEV static void kgroup(const uint32_t *dw, uint32_t out[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t v = dw[i];
+      out[2 * i] = bf16_pair((float)(int8_t)v, (float)(int8_t)(v >> 8));
+      out[2 * i + 1] = bf16_pair((float)(int8_t)(v >> 16), (float)(int8_t)(v >> 24));
+    }
+  }
+  COLI_DEV static uint16_t scale16(const uint4 &v, int cw) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    return (uint16_t)(d[cw >> 2] >> (16 * ((cw >> 1) & 1)));
+  }
 };
 
 // MXFP4 (E2M1 nibbles, one E8M0 scale byte per 32 weights): one quad per
@@ -211,6 +237,7 @@ struct CodecI8 {
 // the chunk's power of two is applied after the dot); natural pairs.
 struct CodecF4 {
   static constexpr int Q = 1;
+  static constexpr int kChunksPerScale = 1;
   static constexpr float kBias = 0.0f;
   static constexpr int64_t bytes(int64_t codes) { return codes / 2; }
   COLI_DEV static uint16_t scale_raw(const uint8_t *base, int64_t n, int K, int c) {
@@ -243,6 +270,17 @@ struct CodecF4 {
     return a;
   }
   COLI_DEV static int half_index(int w) { return w; }
+  COLI_DEV static void kgroup(const uint32_t *dw, uint32_t out[4]) {
+    out[0] = pair<0>(dw[0]);
+    out[1] = pair<1>(dw[0]);
+    out[2] = pair<2>(dw[0]);
+    out[3] = pair<3>(dw[0]);
+  }
+  // 16 E8M0 bytes, one per chunk
+  COLI_DEV static uint16_t scale16(const uint4 &v, int cw) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    return (uint16_t)((d[cw >> 2] >> (8 * (cw & 3))) & 0xffu);
+  }
 };
 
 template <class C>
@@ -505,6 +543,229 @@ __global__ void __launch_bounds__(kThreads) down_stream_kernel(
   }
 }
 
+// ------------------------------------------------- down on the matrix cores
+
+// I = 2048.  The down GEMV as v_mfma_f32_16x16x32_bf16 products: the weights
+// are the B operand (its 16 columns are 16 output rows m), the slot's tokens
+// the A operand, token t's h as two rows -- 2t its high bf16 half, 2t + 1 its
+// low half -- so one instruction covers both halves of up to 8 tokens (NA =
+// 2 operand tiles for 9..16).  Lane l supplies the eight k values 8 (l / 16)
+// .. + 7 of a 32-value chunk for row / column l % 16 of each operand.
+//
+// A workgroup computes TPW tiles of 16 rows of one slot; wavefront w takes
+// k in [512 w, 512 w + 512).  A lane's 16-byte load holds 32 nibbles of one
+// row (int4, MXFP4: one chunk; int8: half of one), so lane groups g = 0..3
+// load consecutive 16-byte pieces and four permlane swaps transpose them into
+// per-chunk operands.  Per 64-weight group (int4, int8; per 32 for MXFP4)
+// the accumulator starts from the nibble bias -136 sum(a) (int4) and is
+// scaled into the running sums; the four wavefronts' sums are added in LDS
+// in a fixed order.  A token's arithmetic is the same in any batch.
+typedef __bf16 coli_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float coli_f32x4 __attribute__((ext_vector_type(4)));
+
+COLI_DEV void swap32(uint32_t &x, uint32_t &y) {
+  const auto p = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = p[0];
+  y = p[1];
+}
+COLI_DEV void swap16(uint32_t &x, uint32_t &y) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = p[0];
+  y = p[1];
+}
+COLI_DEV coli_bf16x8 as_bf16x8(const uint32_t p[4]) {
+  const uint4 v = make_uint4(p[0], p[1], p[2], p[3]);
+  return __builtin_bit_cast(coli_bf16x8, v);
+}
+
+constexpr int kMfmaKw = 512;  // k per wavefront (I / 4)
+
+// Activation quad q (0..3 high half, 4..7 low half) of chunk c of A row a:
+// from the LDS copy of the token's h row (one token) or from h itself (A row
+// a is slot token min(a / 2, cnt - 1); rows past the slot's tokens repeat
+// the last one, and their products are not used).
+template <bool ONE, int NCHK>
+COLI_DEV uint4 mfma_a_quad(const uint4 *hsm, const float *__restrict__ h_in, int pos0, int cnt,
+                           int I, int a, int c, int q) {
+  if (ONE) return hsm[q * NCHK + c];
+  const int tok = min(a >> 1, cnt - 1);
+  return reinterpret_cast<const uint4 *>(h_in + (int64_t)(pos0 + tok) * I + 32 * c)[q];
+}
+
+template <class C>
+constexpr int mfma_tpw() { return C::Q == 1 ? 2 : 1; }  // 16-row tiles per wavefront
+
+template <int NA, bool ONE, class C>
+__global__ void __launch_bounds__(kThreads) down_mfma_kernel(
+    Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
+    float *__restrict__ o_out) {
+  constexpr int TPW = mfma_tpw<C>();
+  constexpr int NCHK = 64;                     // chunks of an h row (I = 2048)
+  constexpr int CPW = kMfmaKw / 32;            // chunks per wavefront (16)
+  constexpr int LPT = CPW * C::Q / 4;          // 16-byte loads per tile (int8: 8, else 4)
+  constexpr int CPL = 4 / C::Q;                // chunks per load
+  constexpr int CPS = C::kChunksPerScale;      // chunks sharing one scale
+  constexpr int ROWS = 16 * NA;                // A rows
+  constexpr bool kHasBias = C::kBias != 0.0f;
+  constexpr int UNITS = kHasBias ? NCHK / 2 : 1;  // 64-value bias groups of a row
+  // bias table: per group, the A rows (one token: [hi, lo, hi, lo], which is
+  // what every lane group reads, since its A rows all repeat the token)
+  constexpr int BROWS = ONE ? 4 : ROWS;
+  __shared__ uint4 hsm[ONE ? 8 * NCHK : 1];
+  __shared__ __align__(16) float bias_sm[UNITS * BROWS];
+  __shared__ float red[kWaves * TPW * NA * 64 * 2];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, rr = lane & 15;
+  const int H = L.H, I = L.I;
+  const int wg_per_slot = H / (16 * TPW);
+  const int slot = blockIdx.x / wg_per_slot;
+  if (!ONE && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
+  const Slot sl = slot_of<ONE>(r, L, T, slot);
+  const int cnt = ONE ? 1 : sl.cnt;
+  const int m0 = (blockIdx.x % wg_per_slot) * (16 * TPW);
+  const int k0 = wv * kMfmaKw;
+  // one token: the h row (8 KB), requested before the weights
+  uint4 hp0 = make_uint4(0u, 0u, 0u, 0u), hp1 = hp0;
+  if (ONE) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(h_in + (int64_t)sl.pos0 * I);
+    hp0 = src[threadIdx.x];
+    hp1 = src[threadIdx.x + kThreads];
+  }
+  // weights: tile t, load j holds bytes 64 j + 16 g of row m0 + 16 t + rr
+  // within the wavefront's k range
+  const int64_t row_bytes = C::bytes(I);
+  const uint8_t *qd = L.q4 + (int64_t)sl.e * L.expert_bytes + C::bytes((int64_t)2 * I * H) +
+                      (int64_t)(m0 + rr) * row_bytes + C::bytes(k0) + 16 * g;
+  uint4 w[TPW][LPT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int j = 0; j < LPT; ++j)
+      w[t][j] = *reinterpret_cast<const uint4 *>(qd + (int64_t)16 * t * row_bytes + 64 * j);
+  // the scales of those 16 chunks of the row: 16 bytes (8 fp16, or 16 E8M0)
+  const uint8_t *sdb = reinterpret_cast<const uint8_t *>(
+      L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64);
+  uint4 sc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t row = m0 + 16 * t + rr;
+    const int64_t off = CPS == 2 ? 2 * (row * (I / 64) + k0 / 64) : row * (I / 32) + k0 / 32;
+    sc[t] = *reinterpret_cast<const uint4 *>(sdb + off);
+  }
+  if (ONE) {
+    const int q0 = threadIdx.x, q1 = threadIdx.x + kThreads;
+    hsm[(q0 & 7) * NCHK + (q0 >> 3)] = hp0;
+    hsm[(q1 & 7) * NCHK + (q1 >> 3)] = hp1;
+    __syncthreads();
+  }
+  if (kHasBias) {
+    // -136 * (sum of A row a over group u), chunk 2u then 2u + 1, in order;
+    // rows past the slot's tokens are not used and get 0
+    for (int idx = threadIdx.x; idx < UNITS * BROWS; idx += kThreads) {
+      const int u = idx / BROWS, a = idx - u * BROWS;
+      if (ONE ? a >= 2 : a >= 2 * cnt) {
+        if (!ONE) bias_sm[idx] = 0.0f;
+        continue;
+      }
+      float sum = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = mfma_a_quad<ONE, NCHK>(hsm, h_in, sl.pos0, cnt, I, a, 2 * u + h, 4 * (a & 1) + q);
+          sum = dot2_bf16(v.x, kBf16Ones, sum);
+          sum = dot2_bf16(v.y, kBf16Ones, sum);
+          sum = dot2_bf16(v.z, kBf16Ones, sum);
+          sum = dot2_bf16(v.w, kBf16Ones, sum);
+        }
+      bias_sm[idx] = -(float)kNibBias * sum;
+      if (ONE) bias_sm[idx + 2] = -(float)kNibBias * sum;
+    }
+    __syncthreads();
+  }
+  coli_f32x4 acc[TPW][NA], d[TPW][NA];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[t][a] = coli_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    uint32_t dw[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      dw[t][0] = w[t][j].x, dw[t][1] = w[t][j].y, dw[t][2] = w[t][j].z, dw[t][3] = w[t][j].w;
+      if (C::Q == 1) {  // lane group g held chunk g: now dword b holds chunk b
+        swap32(dw[t][0], dw[t][2]);
+        swap32(dw[t][1], dw[t][3]);
+        swap16(dw[t][0], dw[t][1]);
+        swap16(dw[t][2], dw[t][3]);
+      } else {  // group g held half g & 1 of chunk g >> 1: now dwords 2b, 2b + 1
+        swap16(dw[t][0], dw[t][2]);  // hold k group g of chunk b
+        swap16(dw[t][1], dw[t][3]);
+        swap32(dw[t][0], dw[t][2]);
+        swap32(dw[t][1], dw[t][3]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < CPL; ++b) {
+      const int cw = j * CPL + b;  // chunk within the wavefront's range
+      const int c = k0 / 32 + cw;  // chunk within the row
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        // the chunk's activations (and its group's bias) serve every tile
+        const int arow = 16 * a + rr;
+        const uint4 av = mfma_a_quad<ONE, NCHK>(hsm, h_in, sl.pos0, cnt, I, arow, c,
+                                                4 * (arow & 1) + g);
+        const uint32_t ap[4] = {av.x, av.y, av.z, av.w};
+        const coli_bf16x8 aop = as_bf16x8(ap);
+        coli_f32x4 cin = coli_f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kHasBias && cw % CPS == 0) {
+          const float4 bv = *reinterpret_cast<const float4 *>(
+              &bias_sm[(c >> 1) * BROWS + (ONE ? 0 : 16 * a + 4 * g)]);
+          cin = coli_f32x4{bv.x, bv.y, bv.z, bv.w};
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          uint32_t bp[4];
+          C::kgroup(dw[t] + C::Q * b, bp);
+          if (cw % CPS == 0) d[t][a] = cin;
+          d[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, as_bf16x8(bp), d[t][a], 0, 0, 0);
+          if (cw % CPS == CPS - 1) {
+            const float sv = C::scale(C::scale16(sc[t], cw));
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][a][v] = fmaf(sv, d[t][a][v], acc[t][a][v]);
+          }
+        }
+      }
+    }
+    // keeps each load's operand reads (LDS) next to its products, so the
+    // scheduler does not hold every chunk's operands in registers at once
+    asm volatile("" ::: "memory");
+  }
+  // lane (g, rr), value v: A row 16 a + 4 g + v, output row m0 + 16 t + rr;
+  // rows 2i and 2i + 1 are the halves of slot token i = 8 a + 2 g + v / 2
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      float *dst = red + ((wv * TPW + t) * NA + a) * 128 + 2 * lane;
+      dst[0] = acc[t][a][0] + acc[t][a][1];
+      dst[1] = acc[t][a][2] + acc[t][a][3];
+    }
+  __syncthreads();
+  // the four wavefronts' sums, in wavefront order
+  for (int idx = threadIdx.x; idx < TPW * 16 * cnt; idx += kThreads) {
+    const int i = idx / (TPW * 16), rem = idx - i * (TPW * 16);
+    const int t = rem >> 4, row = rem & 15;
+    const int a = i >> 3, gi = (i & 7) >> 1, vi = i & 1;
+    const int off = (t * NA + a) * 128 + 2 * (16 * gi + row) + vi;
+    float v = red[off];
+#pragma unroll
+    for (int w2 = 1; w2 < kWaves; ++w2) v += red[w2 * TPW * NA * 128 + off];
+    o_out[(int64_t)(sl.pos0 + i) * H + m0 + 16 * t + row] = v;
+  }
+}
+
 constexpr int kMaxStage = 4;  // tokens of one slot staged in LDS at once
 
 // gate/up rows per wavefront: two with int4 codes, one with int8 codes
@@ -556,6 +817,23 @@ hipError_t down_shape(const Layer &L, const coli_moe_route_t &r, int T, const fl
   return hipGetLastError();
 }
 
+// I = 2048: the down GEMV on the matrix cores, NA operand tiles of 8 tokens
+template <class C>
+hipError_t down_mfma(const Layer &L, const coli_moe_route_t &r, int T, const float *h, float *o,
+                     int nslots, hipStream_t s) {
+  const dim3 grid(nslots * (L.H / (16 * mfma_tpw<C>())));
+  if (T == 1)
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, true, C>, grid, dim3(kThreads), 0, s, L, r,
+             T, h, o);
+  else if (T <= 8)
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, false, C>, grid, dim3(kThreads), 0, s, L,
+             r, T, h, o);
+  else
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, false, C>, grid, dim3(kThreads), 0, s, L,
+             r, T, h, o);
+  return hipGetLastError();
+}
+
 // Shape of the streaming path for this layer, or false if it has none.
 template <class C>
 bool stream_shape(const Layer &L, int &lpr, int &cpl) {
@@ -592,7 +870,7 @@ bool launch_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
   if (e == hipSuccess) {
     if (lpr == 16) e = down_shape<16, 1, C>(L, r, T, h, o, nslots, s);
     else if (lpr == 32) e = down_shape<32, 1, C>(L, r, T, h, o, nslots, s);
-    else if (cpl == 1) e = down_shape<64, 1, C>(L, r, T, h, o, nslots, s);
+    else if (cpl == 1) e = down_mfma<C>(L, r, T, h, o, nslots, s);
     else if (cpl == 2) e = down_shape<64, 2, C>(L, r, T, h, o, nslots, s);
     else if (cpl == 3) e = down_shape<64, 3, C>(L, r, T, h, o, nslots, s);
     else e = down_shape<64, 4, C>(L, r, T, h, o, nslots, s);
