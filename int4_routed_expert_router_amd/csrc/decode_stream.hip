@@ -170,9 +170,9 @@ struct CodecI4 {
   COLI_DEV static void kgroup(const uint32_t *dw, uint32_t out[4]) {
     nib8_to_bf16x4(dw[0], out[0], out[1], out[2], out[3]);
   }
-  // raw scale of chunk cw (0..15) from 16 bytes holding 8 fp16 group scales
-  COLI_DEV static uint16_t scale16(const uint4 &v, int cw) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  // raw scale of chunk cw of a run of chunks whose fp16 group scales (one
+  // per two chunks) are packed in d
+  COLI_DEV static uint16_t scale_at(const uint32_t *d, int cw) {
     return (uint16_t)(d[cw >> 2] >> (16 * ((cw >> 1) & 1)));
   }
 };
@@ -225,8 +225,7 @@ struct CodecI8 {
       out[2 * i + 1] = bf16_pair((float)(int8_t)(v >> 16), (float)(int8_t)(v >> 24));
     }
   }
-  COLI_DEV static uint16_t scale16(const uint4 &v, int cw) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  COLI_DEV static uint16_t scale_at(const uint32_t *d, int cw) {
     return (uint16_t)(d[cw >> 2] >> (16 * ((cw >> 1) & 1)));
   }
 };
@@ -276,9 +275,8 @@ struct CodecF4 {
     out[2] = pair<2>(dw[0]);
     out[3] = pair<3>(dw[0]);
   }
-  // 16 E8M0 bytes, one per chunk
-  COLI_DEV static uint16_t scale16(const uint4 &v, int cw) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  // E8M0 bytes, one per chunk
+  COLI_DEV static uint16_t scale_at(const uint32_t *d, int cw) {
     return (uint16_t)((d[cw >> 2] >> (8 * (cw & 3))) & 0xffu);
   }
 };
@@ -731,9 +729,11 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
           if (cw % CPS == 0) d[t][a] = cin;
           d[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, as_bf16x8(bp), d[t][a], 0, 0, 0);
           if (cw % CPS == CPS - 1) {
-            const float sv = C::scale(C::scale16(sc[t], cw));
+            const uint32_t sd[4] = {sc[t].x, sc[t].y, sc[t].z, sc[t].w};
+            const float sv = C::scale(C::scale_at(sd, cw));
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[t][a][v] = fmaf(sv, d[t][a][v], acc[t][a][v]);
+            for (int v = 0; v < (ONE ? 2 : 4); ++v)  // one token: rows 0, 1 are used
+              acc[t][a][v] = fmaf(sv, d[t][a][v], acc[t][a][v]);
           }
         }
       }
@@ -750,7 +750,7 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
     for (int a = 0; a < NA; ++a) {
       float *dst = red + ((wv * TPW + t) * NA + a) * 128 + 2 * lane;
       dst[0] = acc[t][a][0] + acc[t][a][1];
-      dst[1] = acc[t][a][2] + acc[t][a][3];
+      if (!ONE) dst[1] = acc[t][a][2] + acc[t][a][3];  // one token: not read
     }
   __syncthreads();
   // the four wavefronts' sums, in wavefront order
