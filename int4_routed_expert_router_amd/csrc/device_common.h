@@ -69,8 +69,8 @@ COLI_DEV void x8_to_pairs(const uint32_t d[4], uint32_t out[4]) {
 }
 
 // -136 * (sum of a chunk's 32 activations), from its 16 paired dwords, in one
-// fixed order.  Every kernel that removes the nibble bias uses these, so a
-// token's result is the same whichever kernel handled it.
+// fixed order.  Every dot2 decode kernel that removes the nibble bias uses
+// these, so a token's result is the same whichever of them handled it.
 constexpr uint32_t kBf16Ones = 0x3f803f80u;  // bf16 (1.0, 1.0)
 COLI_DEV float chunk_bias(const uint32_t p[16]) {
   float s = 0.0f;
