@@ -58,6 +58,12 @@ COLI_DEV int value_index(int lane) {
   return idx;
 }
 
+// Which slots a launch computes: every slot of a one-token batch (kAll1);
+// in a larger batch, the slots holding exactly one token, with the same
+// single-token code (kSingles), or the others (kMulti).  A slot's tokens get
+// the same arithmetic whichever launch computes them.
+enum { kAll1 = 0, kSingles = 1, kMulti = 2 };
+
 // Union slot `slot`: slots 0 .. S-1 are the shared expert (all T tokens, rows
 // T*k + t), then one slot per routed expert of the union (counts[e] tokens,
 // rows offsets[e] + i).  Token i of a slot has pair-major row pos0 + i.
@@ -325,10 +331,11 @@ COLI_DEV void store_h_pair(float *row, int n, float h) {
 // the staging loop and its barriers are uniform over the workgroup.  Dynamic
 // LDS holds tg tokens: tg x 4 x NCH quads of paired bf16, then tg x NCH
 // chunk biases.
-template <int CPL, int RPW, bool ONE, class C>
+template <int CPL, int RPW, int MODE, class C>
 __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
     Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
     float *__restrict__ h_out) {
+  constexpr bool ONE = MODE != kMulti;  // one token in the slot
   constexpr int NCH = 64 * CPL;
   extern __shared__ uint4 smem[];
   float *xbias = reinterpret_cast<float *>(smem + tg * 4 * NCH);
@@ -339,8 +346,13 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
   const int waves_per_slot = I / RPW;
   const int slot = wave / waves_per_slot;
   // (one token always has exactly k distinct experts: every slot is live)
-  if (!ONE && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
-  const Slot sl = slot_of<ONE>(r, L, T, slot);
+  if (MODE != kAll1 && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
+  const Slot sl = slot_of<MODE == kAll1>(r, L, T, slot);
+  if (MODE == kSingles && sl.cnt != 1) return;
+  if (MODE == kMulti && sl.cnt == 1) return;
+  // the slot's one token (a larger batch's single-token slot is routed: the
+  // shared slot holds every token)
+  const int tok1 = MODE == kSingles ? r.pairs[sl.pos0] / L.k : 0;
   const int n0 = (wave % waves_per_slot) * RPW;
   const int64_t row_bytes = C::bytes(H);
   const uint8_t *qg = L.q4 + (int64_t)sl.e * L.expert_bytes + (int64_t)n0 * row_bytes +
@@ -354,7 +366,7 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
   // (the memory counter retires loads in issue order).
   uint4 xpre[4];
   if (ONE && threadIdx.x < NCH) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(x) + 4 * threadIdx.x;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)tok1 * H) + 4 * threadIdx.x;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) xpre[dw] = src[dw];
   }
@@ -593,10 +605,11 @@ COLI_DEV uint4 mfma_a_quad(const uint4 *hsm, const float *__restrict__ h_in, int
 template <class C>
 constexpr int mfma_tpw() { return C::Q == 1 ? 2 : 1; }  // 16-row tiles per wavefront
 
-template <int NA, bool ONE, class C>
+template <int NA, int MODE, class C>
 __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
     Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
     float *__restrict__ o_out) {
+  constexpr bool ONE = MODE != kMulti;  // one token in the slot
   constexpr int TPW = mfma_tpw<C>();
   constexpr int NCHK = 64;                     // chunks of an h row (I = 2048)
   constexpr int CPW = kMfmaKw / 32;            // chunks per wavefront (16)
@@ -617,8 +630,10 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
   const int H = L.H, I = L.I;
   const int wg_per_slot = H / (16 * TPW);
   const int slot = blockIdx.x / wg_per_slot;
-  if (!ONE && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
-  const Slot sl = slot_of<ONE>(r, L, T, slot);
+  if (MODE != kAll1 && slot >= L.S + r.n_union[0]) return;  // the whole workgroup
+  const Slot sl = slot_of<MODE == kAll1>(r, L, T, slot);
+  if (MODE == kSingles && sl.cnt != 1) return;
+  if (MODE == kMulti && sl.cnt == 1) return;
   const int cnt = ONE ? 1 : sl.cnt;
   const int m0 = (blockIdx.x % wg_per_slot) * (16 * TPW);
   const int k0 = wv * kMfmaKw;
@@ -784,12 +799,15 @@ hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t 
   while (tg > 1 && tg * per_token > 65536) --tg;
   const size_t lds = tg * per_token;
   const dim3 grid((waves + kWaves - 1) / kWaves);
-  if (T == 1)
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, true, C>, grid, dim3(kThreads),
-             lds, s, L, r, x, T, tg, h);
-  else
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, false, C>, grid,
+  if (T == 1) {
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kAll1, C>, grid,
              dim3(kThreads), lds, s, L, r, x, T, tg, h);
+  } else {  // the single-token slots with the one-token code, then the others
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kSingles, C>, grid,
+             dim3(kThreads), lds, s, L, r, x, T, tg, h);
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kMulti, C>, grid,
+             dim3(kThreads), lds, s, L, r, x, T, tg, h);
+  }
   return hipGetLastError();
 }
 
@@ -822,14 +840,19 @@ template <class C>
 hipError_t down_mfma(const Layer &L, const coli_moe_route_t &r, int T, const float *h, float *o,
                      int nslots, hipStream_t s) {
   const dim3 grid(nslots * (L.H / (16 * mfma_tpw<C>())));
-  if (T == 1)
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, true, C>, grid, dim3(kThreads), 0, s, L, r,
+  if (T == 1) {
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kAll1, C>, grid, dim3(kThreads), 0, s, L, r,
              T, h, o);
-  else if (T <= 8)
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, false, C>, grid, dim3(kThreads), 0, s, L,
+    return hipGetLastError();
+  }
+  // most slots of a small batch hold one token: those run the one-token code
+  launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kSingles, C>, grid, dim3(kThreads), 0, s, L,
+           r, T, h, o);
+  if (T <= 8)
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kMulti, C>, grid, dim3(kThreads), 0, s, L,
              r, T, h, o);
   else
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, false, C>, grid, dim3(kThreads), 0, s, L,
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, kMulti, C>, grid, dim3(kThreads), 0, s, L,
              r, T, h, o);
   return hipGetLastError();
 }
