@@ -60,9 +60,15 @@ COLI_DEV int value_index(int lane) {
 
 // Which slots a launch computes: every slot of a one-token batch (kAll1);
 // in a larger batch, the slots holding exactly one token, with the same
-// single-token code (kSingles), or the others (kMulti).  A slot's tokens get
-// the same arithmetic whichever launch computes them.
-enum { kAll1 = 0, kSingles = 1, kMulti = 2 };
+// single-token code (kSingles), or the others (kMulti), or every slot with
+// the general code (kAllN).  A slot's tokens get the same arithmetic
+// whichever launch computes them.
+enum { kAll1 = 0, kSingles = 1, kMulti = 2, kAllN = 3 };
+
+// Whether a batch of several tokens splits its single-token slots off into a
+// launch of their own: it pays where a slot's weights are large (measured on
+// H 6144, I 2048); on small layers (I 512) the extra launch costs more.
+inline bool split_singles(const Layer &L) { return L.I >= 2048; }
 
 // Union slot `slot`: slots 0 .. S-1 are the shared expert (all T tokens, rows
 // T*k + t), then one slot per routed expert of the union (counts[e] tokens,
@@ -335,7 +341,7 @@ template <int CPL, int RPW, int MODE, class C>
 __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
     Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
     float *__restrict__ h_out) {
-  constexpr bool ONE = MODE != kMulti;  // one token in the slot
+  constexpr bool ONE = MODE == kAll1 || MODE == kSingles;  // one token in the slot
   constexpr int NCH = 64 * CPL;
   extern __shared__ uint4 smem[];
   float *xbias = reinterpret_cast<float *>(smem + tg * 4 * NCH);
@@ -609,7 +615,7 @@ template <int NA, int MODE, class C>
 __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
     Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
     float *__restrict__ o_out) {
-  constexpr bool ONE = MODE != kMulti;  // one token in the slot
+  constexpr bool ONE = MODE == kAll1 || MODE == kSingles;  // one token in the slot
   constexpr int TPW = mfma_tpw<C>();
   constexpr int NCHK = 64;                     // chunks of an h row (I = 2048)
   constexpr int CPW = kMfmaKw / 32;            // chunks per wavefront (16)
@@ -802,10 +808,13 @@ hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t 
   if (T == 1) {
     launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kAll1, C>, grid,
              dim3(kThreads), lds, s, L, r, x, T, tg, h);
-  } else {  // the single-token slots with the one-token code, then the others
+  } else if (split_singles(L)) {  // single-token slots with the one-token code
     launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kSingles, C>, grid,
              dim3(kThreads), lds, s, L, r, x, T, tg, h);
     launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kMulti, C>, grid,
+             dim3(kThreads), lds, s, L, r, x, T, tg, h);
+  } else {
+    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kAllN, C>, grid,
              dim3(kThreads), lds, s, L, r, x, T, tg, h);
   }
   return hipGetLastError();
