@@ -214,7 +214,10 @@ int coli_moe_route_hidden(const coli_moe_layer_t *layer, const uint16_t *w_route
  *   y[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t]) + [S] FFN_E(x[t])
  *   FFN_e(x) = W_down * (silu(W_gate x) .* (W_up x)),  silu(g) = g/(1+e^-g)
  * Every distinct expert's weights are streamed from HBM once per call.
- * A token's result does not depend on which other tokens share the batch.
+ * A token's result does not depend on which other tokens share the batch,
+ * among batches of 1-16 tokens and among batches of 17-64 tokens; with
+ * I = 2048 the down projection of the two ranges runs on different units
+ * (matrix cores, vector dot products) and rounds differently.
  *  x [T*H] bf16;  y [T*H] bf16 (round-to-nearest-even) or fp32 (y_dtype).
  * Sources: tantan.ink post, sections "它的核心判断" and "几个关键工程动作". */
 int coli_moe_forward_decode(const coli_moe_layer_t *layer,
