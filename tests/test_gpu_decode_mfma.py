@@ -10,6 +10,8 @@ import dataclasses
 import pytest
 import torch
 
+import int4_routed_expert_router_amd as coli
+from int4_routed_expert_router_amd.binding import COLI_E_UNSUPPORTED
 import synth
 import test_gpu_decode as dec
 import test_gpu_int8_decode as dec8
@@ -50,3 +52,33 @@ def test_batch_invariant(fmt, T):
     for t in range(T):
         yt = forward(L, run_route(L, lg[t:t + 1].contiguous()), x[t:t + 1].contiguous(), "decode")
         assert torch.equal(yt[0], y[t]), "%s token %d of %d depends on its batch" % (fmt, t, T)
+
+
+# 17..64 tokens: the vector decode kernels, at the same width (int4; the
+# int8 and MXFP4 containers decode at most 16 tokens)
+@pytest.mark.parametrize("T", [17, 40, 64])
+def test_large_batch_parity(T):
+    dec._decode_case(SMALL, T, seed=11, zipf=0.5)
+
+
+def test_large_batch_invariant():
+    """Among batches of 17..64 tokens a token's result does not depend on the
+    rest of the batch: the first 17 tokens of a 40-token batch, alone."""
+    L = gpu_layer(SMALL, seed=13)
+    lg = synth.make_logits(SMALL, 40, seed=13, zipf_alpha=0.5).cuda()
+    x = synth.make_x(SMALL, 40, seed=13).cuda()
+    y40 = forward(L, run_route(L, lg), x, "decode")
+    y17 = forward(L, run_route(L, lg[:17].contiguous()), x[:17].contiguous(), "decode")
+    assert torch.equal(y17, y40[:17])
+
+
+@pytest.mark.parametrize("fmt", ["int8", "mxfp4"])
+def test_large_batch_unsupported_for_int8_mxfp4(fmt):
+    spec = dataclasses.replace(SMALL, int8=fmt == "int8", mxfp4=fmt == "mxfp4")
+    L = gpu_layer(spec, seed=1)
+    lg = synth.make_logits(spec, 17, seed=1).cuda()
+    x = synth.make_x(spec, 17, seed=1).cuda()
+    r = run_route(L, lg)
+    with pytest.raises(coli.ColiError) as e:
+        forward(L, r, x, "decode")
+    assert e.value.status == COLI_E_UNSUPPORTED
