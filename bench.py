@@ -557,7 +557,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "MoE-layer tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights, bf16 x bf16 dot products, f32 accumulation",
+        "dtype": "int4 weights, bf16 x bf16 products, f32 accumulation",
         "data": "synthetic (seeded; shapes of the GLM-5.2 MoE layer)",
         "config": {"workload": "glm52_decode_stack", "hidden": spec.hidden, "inter": spec.inter,
                    "routed_experts": spec.n_experts, "shared_experts": spec.n_shared,
