@@ -418,15 +418,20 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
     __syncthreads();
     #pragma unroll 1
     for (int ti = 0; ti < nt; ++ti) {
+      // (one token: a single pass, nothing to hoist; and pinning the weight
+      // registers there made the compiler copy them all, waiting for every
+      // load, before the first dot product)
+      if (!ONE) {
 #pragma unroll
-      for (int j = 0; j < RPW; ++j)
+        for (int j = 0; j < RPW; ++j)
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
+          for (int i = 0; i < CPL; ++i)
 #pragma unroll
-          for (int q = 0; q < C::Q; ++q) {
-            opaque(wg[j][i][q]);
-            opaque(wu[j][i][q]);
-          }
+            for (int q = 0; q < C::Q; ++q) {
+              opaque(wg[j][i][q]);
+              opaque(wu[j][i][q]);
+            }
+      }
       const uint4 *xs = smem + ti * 4 * NCH;
       float v[2 * RPW];
 #pragma unroll
