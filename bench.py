@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
+    python bench.py --prefill-only | --decode-t4-only | --convert-only
+    python bench.py --calibrate-copy | --summarize-rocprof DIR   (profiling helpers)
 
 Default workload: the GLM-5.2-shaped decode stack -- 12 resident layers of
 H=6144, 256 routed experts of I=2048 + 1 shared expert (int4, gs64 fp16
@@ -19,7 +21,8 @@ of each layer's batch union, plus the shared expert, read once), the
 roofline of the dominant kernel (decode gate/up GEMV: algorithmic bytes per
 launch over its average duration from HIP events), the CPU oracle on a
 bounded sample, and secondary workloads (decode at 4 tokens, the 2048-token
-GLM prefill on int8 matrix cores, OLMoE-like and 35B-A3B-class layers).
+GLM prefill on int8 matrix cores, the router GEMV, the weight quantisers,
+OLMoE-like and 35B-A3B-class layers, int8 and MXFP4 expert containers).
 
 Prints ONE JSON line.  Inputs are synthetic (seeded generator module
 `synth`); all inputs are resident in HBM before timing starts.
