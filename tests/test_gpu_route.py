@@ -46,6 +46,10 @@ def test_route_workloads(name, T):
     (8, 8, 3, 0), (5, 1, 17, 1), (300, 17, 33, 257), (1024, 32, 40, 1), (1024, 8, 4096, 256),
     (64, 8, 16, 257), (64, 8, 17, 257), (1, 1, 5, 0), (256, 8, 65536 // 8, 257),
     (64, 16, 65536, 257),  # the maximum batch: 65,536 tokens, 2^20 pairs
+    # one token (the single-wavefront kernel): E not a multiple of 64, the
+    # largest E and k, one expert, k = E
+    (300, 17, 1, 257), (1024, 32, 1, 1), (1024, 8, 1, 256), (5, 1, 1, 1), (1, 1, 1, 0),
+    (8, 8, 1, 0), (130, 3, 1, 257),
 ])
 def test_route_edges(E, k, T, flags):
     spec = synth.LayerSpec(64, 64, E, 0, k, sigmoid=bool(flags & 1), renorm=bool(flags & 256),
