@@ -3,7 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
     python bench.py --prefill-only | --decode-t4-only | --convert-only
-    python bench.py --calibrate-copy | --summarize-rocprof DIR   (profiling helpers)
+    python bench.py --ceilings | --calibrate-copy | --summarize-rocprof DIR
+                                      (measurement and profiling helpers)
 
 Default workload: the GLM-5.2-shaped decode stack -- 12 resident layers of
 H=6144, 256 routed experts of I=2048 + 1 shared expert (int4, gs64 fp16
@@ -236,6 +237,81 @@ def summarize_rocprof(path):
                 print("| `%s` | %d | %s | %.1f |" % (k, len(v), c, statistics.mean(v)))
 
 
+def read_ceiling(sizes_mb=(60, 120), buffers=8, reps=40):
+    """The plain streaming-read rate of this chip, for the roofline fractions:
+    coli_moe_read_probe (the decode GEMVs' access pattern without their
+    arithmetic) over `buffers` rotating buffers per size, so that successive
+    reads miss the 256 MB Infinity Cache, timed per dispatch."""
+    import torch
+
+    import int4_routed_expert_router_amd as coli
+
+    out = {}
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for mb in sizes_mb:
+        n = mb * 1000 * 1000
+        bufs = [torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+                for _ in range(buffers)]
+        state = {"i": 0}
+
+        def one():
+            coli.coli_moe_read_probe(bufs[state["i"] % buffers], n, sink)
+            state["i"] += 1
+
+        for _ in range(buffers):
+            one()
+        t = traced_kernels(one, reps)["read_probe"]
+        out["%d MB" % mb] = {"bytes": n, "launches": t["n"], "avg_us": round(t["avg_us"], 2),
+                             "GB_per_s": round(n / (t["avg_us"] * 1e3), 1)}
+        del bufs
+        torch.cuda.empty_cache()
+    return {"measurement": "plain streaming read, coli_moe_read_probe", "buffers": buffers,
+            "results": out, "spec_peak_GB_per_s": 8000.0}
+
+
+# dense peaks of the MI355X spec sheet, per instruction's data type
+MFMA_SPEC_PEAK_T = {"i8_16x16x32": 5000.0, "i8_16x16x64": 5000.0, "bf16_16x16x32": 2500.0}
+
+
+def mfma_ceiling(workgroups=2048, iters=2048, reps=10):
+    """The issue rate of the matrix-core instructions the kernels use, with no
+    memory traffic (coli_moe_mfma_probe): T(FL)OP/s per instruction, next to
+    the dense spec peak of its data type."""
+    import torch
+
+    import int4_routed_expert_router_amd as coli
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, kind in (("i8_16x16x32", coli.COLI_MFMA_I8_K32),
+                       ("i8_16x16x64", coli.COLI_MFMA_I8_K64),
+                       ("bf16_16x16x32", coli.COLI_MFMA_BF16_K32)):
+        ops = coli.coli_moe_mfma_probe(kind, iters, workgroups, sink)
+        t = traced_kernels(lambda: coli.coli_moe_mfma_probe(kind, iters, workgroups, sink),
+                           reps)["mfma_probe"]
+        rate = ops / (t["avg_us"] * 1e-6) / 1e12
+        out[name] = {"ops_per_launch": ops, "avg_us": round(t["avg_us"], 2),
+                     "T_per_s": round(rate, 1), "spec_peak_T_per_s": MFMA_SPEC_PEAK_T[name],
+                     "frac_of_spec": round(rate / MFMA_SPEC_PEAK_T[name], 4)}
+    return {"measurement": "register-only matrix-core loop, coli_moe_mfma_probe",
+            "workgroups": workgroups, "iters": iters, "results": out}
+
+
+def cpu_host():
+    """Host CPU model and thread count, recorded with the CPU baseline."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def cpu_baseline_decode(spec, layers_obj, x_list, logits_list, budget_s=12.0):
     """The CPU oracle on a bounded sample of the decode stack (T = 1)."""
     import numpy as np
@@ -264,7 +340,7 @@ def cpu_baseline_decode(spec, layers_obj, x_list, logits_list, budget_s=12.0):
     # the oracle parallelises over tokens (OpenMP), so it uses min(T, cores)
     cores = min(T, oracle.threads())
     return {"value": T * done / t_total, "unit": "MoE-layer tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "host": cpu_host(),
             "sample": "%d of the 12 layers, %d token(s) each, route + decode-mode layer in fp64 "
                       "(%.1f s)" % (done, T, t_total)}
 
@@ -434,6 +510,9 @@ def main():
                     help="only the GLM-shaped decode stack with 4 tokens (verify batch)")
     ap.add_argument("--convert-only", action="store_true",
                     help="only the float -> int4 quantiser on 32 GLM-shaped experts")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time a plain streaming read (60 and 120 MB) and the matrix-core "
+                         "issue rate, print them and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
@@ -455,6 +534,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.ceilings:
+        print(json.dumps({"read": read_ceiling(), "mfma": mfma_ceiling()}), flush=True)
         return
     if args.prefill_only:
         pw = synth.WORKLOADS["glm_prefill"]

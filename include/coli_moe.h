@@ -302,6 +302,31 @@ int coli_moe_quantize_int8_gs64(const void *src, int32_t src_dtype, int64_t rows
 int coli_moe_quantize_mxfp4(const void *src, int32_t src_dtype, int64_t rows, int64_t K,
                             uint8_t *q4, uint8_t *e8m0, void *stream);
 
+/* Measurement aid, not a step of the layer: reads `bytes` bytes of device
+ * memory once with the access pattern of the decode GEMVs and none of their
+ * arithmetic (256-thread workgroups, each lane four 16-byte loads, each load
+ * instruction of a wavefront 1 KiB contiguous), so that a caller can time
+ * the plain read rate a kernel gets from HBM on this chip.  The loaded words
+ * are combined, and sink[0] is written only if the result equals 0x12345678,
+ * which keeps the loads live without a write per workgroup.
+ *  src device, 16-byte aligned; bytes a positive multiple of 16, at most
+ *  2^40.  COLI_E_INVALID / COLI_E_ALIGN on bad arguments. */
+int coli_moe_read_probe(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
+/* Measurement aid, not a step of the layer: the matrix-core issue rate of
+ * one instruction on this chip, with no memory traffic.  `workgroups`
+ * workgroups of 4 wavefronts; each wavefront runs `iters` rounds of 4
+ * independent accumulations of the instruction `kind` on register operands.
+ * Operations per launch = workgroups x 4 x iters x 4 x ops(kind), where
+ * ops = 2 x 16 x 16 x K: K = 32 (COLI_MFMA_I8_K32, the instruction the
+ * prefill kernels issue), 64 (COLI_MFMA_I8_K64, the instruction the int8
+ * peak is quoted for) or 32 (COLI_MFMA_BF16_K32, the decode down kernel's).
+ * sink[0] is written only if the accumulators combine to 0x12345678.
+ *  iters and workgroups in [1, 2^20].  COLI_E_INVALID / COLI_E_ALIGN. */
+enum { COLI_MFMA_I8_K32 = 0, COLI_MFMA_I8_K64 = 1, COLI_MFMA_BF16_K32 = 2 };
+int coli_moe_mfma_probe(int32_t kind, int32_t iters, int32_t workgroups, uint32_t *sink,
+                        void *stream);
+
 /* The exact int32 block dot products of one weight matrix of one expert
  * with T rows of int8 activations:
  *   dots[t][n][b] = sum_{k in [32b, 32b+32)} qw[n][k] * q_act[t][k]
@@ -329,7 +354,8 @@ enum {
   COLI_K_DECODE_DOWN = 4, COLI_K_COMBINE = 5, COLI_K_QUANTIZE = 6, COLI_K_PLAN = 7,
   COLI_K_GEMM_GATEUP = 8, COLI_K_GEMM_DOWN = 9, COLI_K_BLOCK_DOTS = 10,
   COLI_K_ROUTER_LOGITS = 11, COLI_K_QUANTIZE_INT4 = 12, COLI_K_QUANTIZE_INT8 = 13,
-  COLI_K_QUANTIZE_MXFP4 = 14, COLI_K_COUNT = 15
+  COLI_K_QUANTIZE_MXFP4 = 14, COLI_K_READ_PROBE = 15,
+  COLI_K_MFMA_PROBE = 16, COLI_K_COUNT = 17
 };
 typedef struct coli_moe_trace {
   void **start;     /* hipEvent_t[capacity] */

@@ -43,7 +43,8 @@ class _TraceC(ctypes.Structure):
 
 KERNEL_NAMES = ["route_fused", "route_topk", "route_group", "decode_gateup", "decode_down",
                 "combine", "quantize_q8_0", "plan", "gemm_gateup", "gemm_down", "block_dots",
-                "router_logits", "quantize_int4", "quantize_int8", "quantize_mxfp4"]
+                "router_logits", "quantize_int4", "quantize_int8", "quantize_mxfp4", "read_probe",
+                "mfma_probe"]
 
 
 class _RouteC(ctypes.Structure):
@@ -79,6 +80,8 @@ def _load():
         lib.coli_moe_quantize_int4_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
         lib.coli_moe_quantize_int8_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
         lib.coli_moe_quantize_mxfp4.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+        lib.coli_moe_read_probe.argtypes = [vp, i64, vp, vp]
+        lib.coli_moe_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
         lib.coli_moe_block_dots.argtypes = [P(_LayerC), i32, i32, vp, i32, vp, vp]
         lib.coli_moe_strerror.argtypes = [ctypes.c_int]
         lib.coli_moe_strerror.restype = ctypes.c_char_p
@@ -89,7 +92,8 @@ def _load():
         for f in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
                   "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
                   "coli_moe_quantize_int4_gs64", "coli_moe_quantize_int8_gs64",
-                  "coli_moe_quantize_mxfp4"):
+                  "coli_moe_quantize_mxfp4", "coli_moe_read_probe",
+                  "coli_moe_mfma_probe"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -228,6 +232,23 @@ def coli_moe_quantize_int8_gs64(src, src_dtype: int, rows: int, K: int, q, scale
 def coli_moe_quantize_mxfp4(src, src_dtype: int, rows: int, K: int, q4, e8m0, stream=None):
     _check("coli_moe_quantize_mxfp4", _load().coli_moe_quantize_mxfp4(
         _ptr(src), src_dtype, rows, K, _ptr(q4), _ptr(e8m0), _stream(stream)))
+
+
+def coli_moe_read_probe(src, nbytes: int, sink, stream=None):
+    _check("coli_moe_read_probe", _load().coli_moe_read_probe(
+        _ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
+COLI_MFMA_I8_K32, COLI_MFMA_I8_K64, COLI_MFMA_BF16_K32 = 0, 1, 2
+MFMA_PROBE_OPS = {COLI_MFMA_I8_K32: 2 * 16 * 16 * 32, COLI_MFMA_I8_K64: 2 * 16 * 16 * 64,
+                  COLI_MFMA_BF16_K32: 2 * 16 * 16 * 32}
+
+
+def coli_moe_mfma_probe(kind: int, iters: int, workgroups: int, sink, stream=None):
+    """Returns the operations the launch performs."""
+    _check("coli_moe_mfma_probe", _load().coli_moe_mfma_probe(
+        kind, iters, workgroups, _ptr(sink), _stream(stream)))
+    return workgroups * 4 * iters * 4 * MFMA_PROBE_OPS[kind]
 
 
 def coli_moe_block_dots(layer: Layer, expert: int, matrix: int, q_act, T: int, dots,

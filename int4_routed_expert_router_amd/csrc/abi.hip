@@ -103,6 +103,9 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
 
 namespace coli {
 coli_moe_trace_t *g_trace = nullptr;
+// probe.hip: the plain streaming read behind coli_moe_read_probe
+int launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+int launch_mfma_probe(int kind, int iters, int workgroups, uint32_t *sink, hipStream_t s);
 }
 
 using namespace coli;
@@ -214,6 +217,22 @@ int coli_moe_quantize_mxfp4(const void *src, int32_t src_dtype, int64_t rows, in
   if (!aligned(src, 16) || !aligned(q4, 4)) return COLI_E_ALIGN;
   return launch_quantize_mxfp4(src, src_dtype, rows * K, q4, e8m0,
                                reinterpret_cast<hipStream_t>(stream));
+}
+
+int coli_moe_read_probe(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 || bytes > (int64_t(1) << 40))
+    return COLI_E_INVALID;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return COLI_E_ALIGN;
+  return launch_read_probe(src, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+}
+
+int coli_moe_mfma_probe(int32_t kind, int32_t iters, int32_t workgroups, uint32_t *sink,
+                        void *stream) {
+  if (kind < COLI_MFMA_I8_K32 || kind > COLI_MFMA_BF16_K32 || !sink || iters < 1 ||
+      iters > (1 << 20) || workgroups < 1 || workgroups > (1 << 20))
+    return COLI_E_INVALID;
+  if (!aligned(sink, 4)) return COLI_E_ALIGN;
+  return launch_mfma_probe(kind, iters, workgroups, sink, reinterpret_cast<hipStream_t>(stream));
 }
 
 int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t matrix,

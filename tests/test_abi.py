@@ -122,6 +122,21 @@ def test_route_quantize_dots_reject_bad_calls():
     assert q4(FAKE + 8, 0, 1, 64, FAKE, FAKE, None) == -4     # src align
     assert q4(FAKE, 1, 1, 64, FAKE + 2, FAKE, None) == -4     # q4 align
     assert q4(FAKE, 1, 1, 64, FAKE, FAKE + 1, None) == -4     # scales align
+    rp = lib.coli_moe_read_probe
+    assert rp(None, 16, FAKE, None) == -1         # src NULL
+    assert rp(FAKE, 24, FAKE, None) == -1         # bytes % 16
+    assert rp(FAKE, 0, FAKE, None) == -1          # bytes = 0
+    assert rp(FAKE, 16, None, None) == -1         # sink NULL
+    assert rp(FAKE + 8, 16, FAKE, None) == -4     # src align
+    assert rp(FAKE, 16, FAKE + 2, None) == -4     # sink align
+    mp = lib.coli_moe_mfma_probe
+    assert mp(3, 1, 1, FAKE, None) == -1          # kind
+    assert mp(-1, 1, 1, FAKE, None) == -1
+    assert mp(0, 0, 1, FAKE, None) == -1          # iters
+    assert mp(0, (1 << 20) + 1, 1, FAKE, None) == -1
+    assert mp(1, 1, 0, FAKE, None) == -1          # workgroups
+    assert mp(2, 1, 1, None, None) == -1          # sink NULL
+    assert mp(2, 1, 1, FAKE + 2, None) == -4      # sink align
     bd = lib.coli_moe_block_dots
     assert bd(ctypes.byref(L.c), 257, 0, FAKE, 4, FAKE, None) == -1   # expert out of range
     assert bd(ctypes.byref(L.c), 0, 3, FAKE, 4, FAKE, None) == -1     # matrix out of range
