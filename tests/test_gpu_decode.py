@@ -50,6 +50,12 @@ def test_decode_workloads(name, T):
     # the largest hidden size, and the largest decode intermediate size
     (synth.LayerSpec(16384, 128, 4, 1, 2, sigmoid=True, renorm=True), 3),
     (synth.LayerSpec(128, 15360, 3, 1, 1, sigmoid=False, renorm=False), 2),
+    # the most experts and the largest top-k: 1024 experts, k = 32, on the
+    # general kernels (T = 64: a union of up to 1024 slots) and on the
+    # streaming kernels (T = 1, and T = 16 with a union of up to 512 slots)
+    (synth.LayerSpec(256, 128, 1024, 1, 32, sigmoid=True, renorm=True), 64),
+    (synth.LayerSpec(2048, 512, 1024, 1, 32, sigmoid=False, renorm=True), 1),
+    (synth.LayerSpec(2048, 512, 1024, 1, 32, sigmoid=True, renorm=False), 16),
 ])
 def test_decode_edge_shapes(spec, T):
     _decode_case(spec, T, seed=7, zipf=0.5)

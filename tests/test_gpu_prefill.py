@@ -114,6 +114,8 @@ def test_prefill_glm_2048_sampled():
     (synth.LayerSpec(2048, 512, 256, 1, 8, sigmoid=True, renorm=True), 16),
     (synth.LayerSpec(64, 64, 1, 0, 1, sigmoid=False, renorm=False), 1),
     (synth.LayerSpec(1024, 448, 32, 0, 4, sigmoid=False, renorm=True), 129),
+    # the most experts and the largest top-k (1024 experts, k = 32)
+    (synth.LayerSpec(256, 256, 1024, 1, 32, sigmoid=True, renorm=True), 100),
 ])
 def test_prefill_edge_shapes(spec, T):
     _prefill_case(spec, T, seed=3, zipf=0.6)
