@@ -361,7 +361,8 @@ def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=N
             "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
 
 
-def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
+def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
+                      k32_ceiling=None):
     import torch
 
     import int4_routed_expert_router_amd as coli
@@ -404,6 +405,9 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1):
            "weight_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
+    if k32_ceiling:  # the measured rate of the instruction the GEMM issues
+        out["measured_k32_TOPS"] = k32_ceiling
+        out["frac_of_measured_k32"] = round(ops / (ms * 1e-3) / 1e12 / k32_ceiling, 4)
     return out
 
 
@@ -586,6 +590,11 @@ def main():
                 "kernel_source_digest": kernel_digest(),
                 "kernels_us": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
     log("kernels (us):", roofline["kernels_us"])
+    # the same kernel against what a plain read of 120 MB reaches on this chip
+    rc = read_ceiling(sizes_mb=(120,), reps=20)["results"]["120 MB"]["GB_per_s"]
+    roofline["measured_read_GBps"] = rc
+    roofline["frac_of_measured_read"] = round(gu_gbps / rc, 4)
+    log("plain read of 120 MB: %.0f GB/s; gate/up at %.1f%% of it" % (rc, 100 * gu_gbps / rc))
 
     cpu = None
     if not args.no_cpu:
@@ -598,8 +607,9 @@ def main():
         secondary.append(secondary_decode("glm_decode_stack_T4", spec, 4, w.zipf_alpha, layers,
                                           max(10, args.steps // 2), 3, layer_weights=stack.layers))
         pw = synth.WORKLOADS["glm_prefill"]
+        k32 = mfma_ceiling(reps=3)["results"]["i8_16x16x32"]["T_per_s"]
         secondary.append(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
-                                           10, 2, layer=stack.layers[0]))
+                                           10, 2, layer=stack.layers[0], k32_ceiling=k32))
         del stack
         torch.cuda.empty_cache()
         secondary.append(secondary_router("glm_router_T1", w.spec, 1, 200, 10))
