@@ -20,8 +20,8 @@ value = MoE-layer tokens/s = tokens x layers / step time.  Also reported:
 int4 weight GB/s of the whole step (algorithmic bytes: every distinct expert
 of each layer's batch union, plus the shared expert, read once), the
 roofline of the dominant kernel (decode gate/up GEMV: algorithmic bytes per
-launch over its average duration from HIP events), the CPU oracle on a
-bounded sample, and secondary workloads (decode at 4 tokens, the 2048-token
+launch over its average duration from HIP events; also against a plain read
+of 120 MB timed in the same run), the CPU oracle on a bounded sample, and secondary workloads (decode at 4 tokens, the 2048-token
 GLM prefill on int8 matrix cores, the router GEMV, the weight quantisers,
 OLMoE-like and 35B-A3B-class layers, int8 and MXFP4 expert containers).
 
