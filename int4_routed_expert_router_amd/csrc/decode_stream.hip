@@ -73,6 +73,15 @@ inline bool split_singles(const Layer &L) { return L.I >= 2048; }
 // Union slot `slot`: slots 0 .. S-1 are the shared expert (all T tokens, rows
 // T*k + t), then one slot per routed expert of the union (counts[e] tokens,
 // rows offsets[e] + i).  Token i of a slot has pair-major row pos0 + i.
+// A gate/up weight quad, read once per call: a non-temporal load, so the
+// stream does not displace cached lines.  (The same hint on the down
+// weights made the down kernel slower, so it loads them plainly.)
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+COLI_DEV uint4 load_stream(const uint8_t *p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 struct Slot {
   int e, cnt, pos0;
   bool shared;
@@ -385,8 +394,8 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
       const int64_t ob = (int64_t)j * row_bytes + 1024 * C::Q * i;
 #pragma unroll
       for (int q = 0; q < C::Q; ++q) {
-        wg[j][i][q] = *reinterpret_cast<const uint4 *>(qg + ob + 16 * q);
-        wu[j][i][q] = *reinterpret_cast<const uint4 *>(qu + ob + 16 * q);
+        wg[j][i][q] = load_stream(qg + ob + 16 * q);
+        wu[j][i][q] = load_stream(qu + ob + 16 * q);
       }
       sg[j][i] = C::scale_raw(sgb, n0 + j, H, lane + 64 * i);
       su[j][i] = C::scale_raw(sub, n0 + j, H, lane + 64 * i);
