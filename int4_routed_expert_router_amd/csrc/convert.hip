@@ -159,9 +159,15 @@ COLI_DEV void quantize_chunk_fp4(const float v[8], uint32_t &packed, uint8_t &e_
   e_out = (uint8_t)E;
 }
 
+// Every source byte is read once and every code byte written once: both go
+// through non-temporal accesses.
+typedef unsigned int cv_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int cv_u32x2 __attribute__((ext_vector_type(2)));
+typedef float cv_f32x4 __attribute__((ext_vector_type(4)));
+
 COLI_DEV void load_chunk(const void *src, int src_dtype, int64_t t, float v[8]) {
   if (src_dtype == COLI_SRC_BF16) {
-    const uint4 u = reinterpret_cast<const uint4 *>(src)[t];
+    const cv_u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const cv_u32x4 *>(src) + t);
     const uint32_t d[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -169,8 +175,8 @@ COLI_DEV void load_chunk(const void *src, int src_dtype, int64_t t, float v[8]) 
       v[2 * j + 1] = bf16_to_f32(d[j] >> 16);
     }
   } else {
-    const float4 *p = reinterpret_cast<const float4 *>(src) + 2 * t;
-    const float4 f0 = p[0], f1 = p[1];
+    const cv_f32x4 *p = reinterpret_cast<const cv_f32x4 *>(src) + 2 * t;
+    const cv_f32x4 f0 = __builtin_nontemporal_load(p), f1 = __builtin_nontemporal_load(p + 1);
     v[0] = f0.x, v[1] = f0.y, v[2] = f0.z, v[3] = f0.w;
     v[4] = f1.x, v[5] = f1.y, v[6] = f1.z, v[7] = f1.w;
   }
@@ -188,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) quantize_int4_kernel(const void *__r
   uint32_t packed;
   uint16_t s16;
   quantize_chunk(v, packed, s16);
-  q4[t] = packed;
+  __builtin_nontemporal_store(packed, q4 + t);
   if ((t & 7) == 0) scales[t >> 3] = s16;
 }
 
@@ -204,7 +210,7 @@ __global__ void __launch_bounds__(kThreads) quantize_int8_kernel(const void *__r
   uint32_t lo, hi;
   uint16_t s16;
   quantize_chunk8(v, lo, hi, s16);
-  q[t] = make_uint2(lo, hi);
+  __builtin_nontemporal_store(cv_u32x2{lo, hi}, reinterpret_cast<cv_u32x2 *>(q) + t);
   if ((t & 7) == 0) scales[t >> 3] = s16;
 }
 
@@ -220,7 +226,7 @@ __global__ void __launch_bounds__(kThreads) quantize_mxfp4_kernel(const void *__
   uint32_t packed;
   uint8_t E;
   quantize_chunk_fp4(v, packed, E);
-  q4[t] = packed;
+  __builtin_nontemporal_store(packed, q4 + t);
   if ((t & 3) == 0) e8[t >> 2] = E;
 }
 
