@@ -172,7 +172,12 @@ typedef struct coli_moe_route {
 } coli_moe_route_t;
 
 /* Bytes of device workspace an entry point needs for T tokens (entry is a
- * COLI_ENTRY_*).  Returns 0 for invalid arguments.  Host-only, no HIP call. */
+ * COLI_ENTRY_*).  Returns 0 for invalid arguments.  Host-only, no HIP call.
+ * The workspace holds what the layer definition makes between its steps:
+ * the SwiGLU output h and the down outputs o of every (token, expert) row of
+ * the batch union, and on the integer path the Q8_0 codes and scales of x
+ * and h (alphamatch.ai blog, section "優化整數核心"; batch union: tantan.ink
+ * post, section "几个关键工程动作"). */
 size_t coli_moe_workspace_bytes(const coli_moe_layer_t *layer, int32_t T,
                                 int32_t entry);
 
@@ -271,7 +276,8 @@ int coli_moe_quantize_q8_0(const void *src, int32_t src_dtype, int64_t n,
  *  scales [rows*K/64] fp16 bits, device, 2-byte aligned.
  * Groups are independent and flat, so matrices stored back to back (gate,
  * up and down of an expert, or a whole container in container order) can be
- * quantised in one call with rows*K their total size; rows*K <= 2^36.
+ * quantised in one call with rows*K their total size; rows*K <= 2^34 (one
+ * work-item per 8 values keeps the grid within a dispatch's 2^32 items).
  * Returns COLI_E_INVALID for a bad size, dtype or null pointer and
  * COLI_E_ALIGN for misaligned buffers; the outputs are then untouched. */
 int coli_moe_quantize_int4_gs64(const void *src, int32_t src_dtype, int64_t rows,
@@ -285,7 +291,7 @@ int coli_moe_quantize_int4_gs64(const void *src, int32_t src_dtype, int64_t rows
  *  src [rows*K] bf16 or fp32, 16-byte aligned, finite, max|w| <= 127 * 65504;
  *  q [rows*K] int8, 8-byte aligned (byte k of row n at n*K + k);
  *  scales [rows*K/64] fp16 bits, 2-byte aligned.  K % 64 == 0,
- *  rows*K <= 2^36.  Errors as for coli_moe_quantize_int4_gs64. */
+ *  rows*K <= 2^34.  Errors as for coli_moe_quantize_int4_gs64. */
 int coli_moe_quantize_int8_gs64(const void *src, int32_t src_dtype, int64_t rows,
                                 int64_t K, int8_t *q, uint16_t *scales, void *stream);
 
@@ -298,7 +304,7 @@ int coli_moe_quantize_int8_gs64(const void *src, int32_t src_dtype, int64_t rows
  * table); this is the published MX conversion.
  *  src [rows*K] bf16 or fp32, 16-byte aligned, finite;  q4 [rows*K/2]
  *  nibbles (even k low), 4-byte aligned;  e8m0 [rows*K/32] bytes.
- *  K % 32 == 0, rows*K <= 2^36.  Errors as for coli_moe_quantize_int4_gs64. */
+ *  K % 32 == 0, rows*K <= 2^34.  Errors as for coli_moe_quantize_int4_gs64. */
 int coli_moe_quantize_mxfp4(const void *src, int32_t src_dtype, int64_t rows, int64_t K,
                             uint8_t *q4, uint8_t *e8m0, void *stream);
 
@@ -310,7 +316,7 @@ int coli_moe_quantize_mxfp4(const void *src, int32_t src_dtype, int64_t rows, in
  * are combined, and sink[0] is written only if the result equals 0x12345678,
  * which keeps the loads live without a write per workgroup.
  *  src device, 16-byte aligned; bytes a positive multiple of 16, at most
- *  2^40.  COLI_E_INVALID / COLI_E_ALIGN on bad arguments. */
+ *  2^36.  COLI_E_INVALID / COLI_E_ALIGN on bad arguments. */
 int coli_moe_read_probe(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
 /* Measurement aid, not a step of the layer: the matrix-core issue rate of
@@ -328,7 +334,11 @@ int coli_moe_mfma_probe(int32_t kind, int32_t iters, int32_t workgroups, uint32_
                         void *stream);
 
 /* The exact int32 block dot products of one weight matrix of one expert
- * with T rows of int8 activations:
+ * with T rows of int8 activations -- the integer unit of the pages' kernel,
+ * which multiplies Q8_0-style int8 activations with the integer weight codes
+ * (alphamatch.ai blog, section "優化整數核心").  Weight scales cover 64
+ * codes and activation scales 32 values, so the 32-wide block is the unit
+ * both scales are constant over:
  *   dots[t][n][b] = sum_{k in [32b, 32b+32)} qw[n][k] * q_act[t][k]
  *  matrix 0 = gate, 1 = up (K = H, rows = I), 2 = down (K = I, rows = H).
  *  q_act [T*K] int8, T in [1, 4096];  dots [T*rows*(K/32)] int32.

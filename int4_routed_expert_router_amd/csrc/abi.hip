@@ -193,7 +193,7 @@ int coli_moe_quantize_int4_gs64(const void *src, int32_t src_dtype, int64_t rows
                                 uint8_t *q4, uint16_t *scales, void *stream) {
   if (!src || !q4 || !scales) return COLI_E_INVALID;
   if (src_dtype != COLI_SRC_BF16 && src_dtype != COLI_SRC_F32) return COLI_E_INVALID;
-  if (rows < 1 || K < 64 || K % 64 || rows > (int64_t(1) << 36) / K) return COLI_E_INVALID;
+  if (rows < 1 || K < 64 || K % 64 || rows > (int64_t(1) << 34) / K) return COLI_E_INVALID;
   if (!aligned(src, 16) || !aligned(q4, 4) || !aligned(scales, 2)) return COLI_E_ALIGN;
   return launch_quantize_int4(src, src_dtype, rows * K, q4, scales,
                               reinterpret_cast<hipStream_t>(stream));
@@ -203,7 +203,7 @@ int coli_moe_quantize_int8_gs64(const void *src, int32_t src_dtype, int64_t rows
                                 int8_t *q, uint16_t *scales, void *stream) {
   if (!src || !q || !scales) return COLI_E_INVALID;
   if (src_dtype != COLI_SRC_BF16 && src_dtype != COLI_SRC_F32) return COLI_E_INVALID;
-  if (rows < 1 || K < 64 || K % 64 || rows > (int64_t(1) << 36) / K) return COLI_E_INVALID;
+  if (rows < 1 || K < 64 || K % 64 || rows > (int64_t(1) << 34) / K) return COLI_E_INVALID;
   if (!aligned(src, 16) || !aligned(q, 8) || !aligned(scales, 2)) return COLI_E_ALIGN;
   return launch_quantize_int8(src, src_dtype, rows * K, q, scales,
                               reinterpret_cast<hipStream_t>(stream));
@@ -213,14 +213,14 @@ int coli_moe_quantize_mxfp4(const void *src, int32_t src_dtype, int64_t rows, in
                             uint8_t *q4, uint8_t *e8m0, void *stream) {
   if (!src || !q4 || !e8m0) return COLI_E_INVALID;
   if (src_dtype != COLI_SRC_BF16 && src_dtype != COLI_SRC_F32) return COLI_E_INVALID;
-  if (rows < 1 || K < 32 || K % 32 || rows > (int64_t(1) << 36) / K) return COLI_E_INVALID;
+  if (rows < 1 || K < 32 || K % 32 || rows > (int64_t(1) << 34) / K) return COLI_E_INVALID;
   if (!aligned(src, 16) || !aligned(q4, 4)) return COLI_E_ALIGN;
   return launch_quantize_mxfp4(src, src_dtype, rows * K, q4, e8m0,
                                reinterpret_cast<hipStream_t>(stream));
 }
 
 int coli_moe_read_probe(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
-  if (!src || !sink || bytes < 16 || bytes % 16 || bytes > (int64_t(1) << 40))
+  if (!src || !sink || bytes < 16 || bytes % 16 || bytes > (int64_t(1) << 36))
     return COLI_E_INVALID;
   if (!aligned(src, 16) || !aligned(sink, 4)) return COLI_E_ALIGN;
   return launch_read_probe(src, bytes, sink, reinterpret_cast<hipStream_t>(stream));

@@ -9,7 +9,10 @@
  *
  * Everything is straight loops in the order the definitions read, with fp64
  * accumulation (built with -ffp-contract=off).  OpenMP splits only
- * independent output rows / tokens; every sum runs sequentially.
+ * independent output rows / tokens; every sum runs sequentially.  Tokens
+ * are split across threads when there are at least as many tokens as
+ * threads; otherwise each token's output rows are (OR_ROWS_PARALLEL), so a
+ * single token also uses every core.
  *
  * Definitions followed (web pages about the colibri engine):
  *  - int4, one fp16 scale per 64 weights ("gs64"): tantan.ink post
@@ -38,12 +41,20 @@
  * implemented (the RENORM flag) and each is pinned to its own definition.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define OR_OK 0
 #define OR_EINVAL -1
+
+/* Split a loop over independent output rows across threads, unless the
+ * caller's token loop already runs in parallel. */
+#define OR_ROWS_PARALLEL _Pragma("omp parallel for schedule(static) if(!omp_in_parallel())")
+
+/* Whether a token loop of T iterations should itself run in parallel. */
+static int or_tokens_parallel(int64_t T) { return T >= omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- numbers */
 
@@ -278,6 +289,7 @@ static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
   const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
   const uint8_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
   const int f = L->fmt;
+  OR_ROWS_PARALLEL
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t k = 0; k < H; ++k) {
@@ -286,6 +298,7 @@ static void or_ffn_f64(const or_layer *L, int64_t e, const double *x, double *h,
     }
     h[n] = or_silu(g) * u;
   }
+  OR_ROWS_PARALLEL
   for (int64_t m = 0; m < H; ++m) {
     double acc = 0.0;
     for (int64_t n = 0; n < I; ++n)
@@ -307,7 +320,7 @@ int oracle_forward_decode(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
     return OR_EINVAL;
   or_layer L = {H, I, E, S, q4, (const uint8_t *)scales, fmt};
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad) if(or_tokens_parallel(T))
   for (int64_t t = 0; t < T; ++t) {
     double *x = (double *)malloc(sizeof(double) * (size_t)H);
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
@@ -528,6 +541,7 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
   const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
   const uint8_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
   const int f = L->fmt;
+  OR_ROWS_PARALLEL
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t b = 0; b < H / 32; ++b) {
@@ -538,6 +552,7 @@ static int or_ffn_q8(const or_layer *L, int64_t e, const int8_t *qx,
     hf[n] = (float)(or_silu(g) * u);
   }
   if (oracle_quantize_q8_0(hf, I, qh, dh) != OR_OK) return OR_EINVAL;
+  OR_ROWS_PARALLEL
   for (int64_t m = 0; m < H; ++m) {
     double acc = 0.0;
     for (int64_t b = 0; b < I / 32; ++b)
@@ -562,7 +577,7 @@ int oracle_forward_prefill(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k
     return OR_EINVAL;
   or_layer L = {H, I, E, S, q4, (const uint8_t *)scales, fmt};
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad) if(or_tokens_parallel(T))
   for (int64_t t = 0; t < T; ++t) {
     float *xf = (float *)malloc(sizeof(float) * (size_t)H);
     int8_t *qx = (int8_t *)malloc((size_t)H);

@@ -35,6 +35,46 @@ def route_host(r: coli.Route, T: int, k: int):
         "topk_idx", "topk_w", "counts", "offsets", "pairs", "pair_pos", "union_ids", "n_union")}
 
 
+def checked_route(spec: synth.LayerSpec, r: coli.Route, logits: torch.Tensor, sel_bias=None):
+    """The oracle's route of the same logits, after checking the device route
+    against it: top-k indices, counts, offsets and pair lists bit for bit,
+    routing weights within 3e-6 relative.  End-to-end comparisons feed the
+    oracle's own routing to the oracle layer, so a device routing mistake
+    cannot hide behind both sides using the same wrong experts."""
+    T = logits.shape[0]
+    k = spec.top_k
+    g = route_host(r, T, k)
+    sb = None if sel_bias is None else sel_bias.float().cpu().numpy()
+    o = oracle.route(logits.float().cpu().numpy(), k, spec.flags, spec.routed_scale, sel_bias=sb)
+    assert np.array_equal(g["topk_idx"].reshape(T, k), o["topk_idx"]), "device top-k differs"
+    assert np.array_equal(g["counts"], o["counts"]), "device counts differ"
+    assert np.array_equal(g["offsets"], o["offsets"]), "device offsets differ"
+    assert np.array_equal(g["pairs"], o["pairs"]), "device pair lists differ"
+    np.testing.assert_allclose(g["topk_w"].reshape(T, k), o["topk_w"], rtol=3e-6, atol=1e-7)
+    return o
+
+
+def cover_tokens(g, T: int, k: int, tile: int = 64, hottest: int = 0, shared: bool = True):
+    """Tokens that touch every (expert, token tile) work item of a batched
+    union: for each expert, the first and the last row of each run of `tile`
+    rows of its token list (so every partial last tile's last row too), the
+    shared expert's tile boundaries (tokens 0, tile-1, tile, ...), and every
+    token of the `hottest` most-loaded experts.  g is a route dict
+    (counts, offsets, pairs)."""
+    counts, offsets, pairs = g["counts"], g["offsets"], np.asarray(g["pairs"]).ravel()
+    toks = set()
+    for e in range(len(counts)):
+        n = int(counts[e])
+        for pos in range(n):
+            if pos % tile in (0, tile - 1) or pos == n - 1:
+                toks.add(int(pairs[offsets[e] + pos]) // k)
+    if shared:
+        toks.update(t for t in range(T) if t % tile in (0, tile - 1) or t == T - 1)
+    for e in np.argsort(-np.asarray(counts), kind="stable")[:hottest]:
+        toks.update(int(p) // k for p in pairs[offsets[e]:offsets[e + 1]])
+    return sorted(toks)
+
+
 def forward(L: coli.Layer, r: coli.Route, x: torch.Tensor, entry: str, y_dtype=coli.COLI_OUT_F32):
     T = x.shape[0]
     ent = coli.COLI_ENTRY_DECODE if entry == "decode" else coli.COLI_ENTRY_PREFILL

@@ -118,7 +118,11 @@ def test_route_quantize_dots_reject_bad_calls():
     assert q4(FAKE, 2, 1, 64, FAKE, FAKE, None) == -1         # dtype
     assert q4(FAKE, 0, 0, 64, FAKE, FAKE, None) == -1         # rows = 0
     assert q4(FAKE, 0, 1, 96, FAKE, FAKE, None) == -1         # K % 64
-    assert q4(FAKE, 0, 1 << 30, 128, FAKE, FAKE, None) == -1  # rows * K > 2^36
+    assert q4(FAKE, 0, 1 << 30, 128, FAKE, FAKE, None) == -1  # rows * K > 2^34
+    # rows * K just past 2^34: one work-item per 8 values would pass 2^31
+    assert q4(FAKE, 0, (1 << 28) + 1, 64, FAKE, FAKE, None) == -1
+    assert lib.coli_moe_quantize_int8_gs64(FAKE, 0, (1 << 28) + 1, 64, FAKE, FAKE, None) == -1
+    assert lib.coli_moe_quantize_mxfp4(FAKE, 0, (1 << 29) + 1, 32, FAKE, FAKE, None) == -1
     assert q4(FAKE + 8, 0, 1, 64, FAKE, FAKE, None) == -4     # src align
     assert q4(FAKE, 1, 1, 64, FAKE + 2, FAKE, None) == -4     # q4 align
     assert q4(FAKE, 1, 1, 64, FAKE, FAKE + 1, None) == -4     # scales align
@@ -126,6 +130,7 @@ def test_route_quantize_dots_reject_bad_calls():
     assert rp(None, 16, FAKE, None) == -1         # src NULL
     assert rp(FAKE, 24, FAKE, None) == -1         # bytes % 16
     assert rp(FAKE, 0, FAKE, None) == -1          # bytes = 0
+    assert rp(FAKE, (1 << 36) + 16, FAKE, None) == -1   # past 2^36 bytes
     assert rp(FAKE, 16, None, None) == -1         # sink NULL
     assert rp(FAKE + 8, 16, FAKE, None) == -4     # src align
     assert rp(FAKE, 16, FAKE + 2, None) == -4     # sink align

@@ -6,7 +6,7 @@ import torch
 import int4_routed_expert_router_amd as coli
 import synth
 from gpu_util import (BF16_HALF_ULP, REL_TOL, bf16_ulp_distance, forward, gpu_layer, oracle_layer, rel_err,
-                      route_host, run_route)
+                      checked_route, run_route)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ def _decode_case(spec, T, seed=0, zipf=0.0, layer=0, tokens=None):
     x = synth.make_x(spec, T, seed=seed, layer=layer).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "decode")
-    g = route_host(r, T, spec.top_k)
+    g = checked_route(spec, r, lg)
     toks = range(T) if tokens is None else tokens
     ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, toks, "decode")
     err = rel_err(y.cpu().numpy()[list(toks)], ref)

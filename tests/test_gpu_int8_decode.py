@@ -10,7 +10,7 @@ import torch
 
 import int4_routed_expert_router_amd as coli
 import synth
-from gpu_util import REL_TOL, forward, gpu_layer, oracle_layer, rel_err, route_host, run_route
+from gpu_util import REL_TOL, forward, gpu_layer, oracle_layer, rel_err, checked_route, run_route
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def _case(spec, T, seed=0, zipf=0.0, tokens=None):
     x = synth.make_x(spec, T, seed=seed).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "decode")
-    g = route_host(r, T, spec.top_k)
+    g = checked_route(spec, r, lg)
     toks = list(range(T)) if tokens is None else tokens
     ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, toks, "decode")
     err = rel_err(y.cpu().numpy()[toks], ref)
@@ -77,7 +77,7 @@ def test_int8_extreme_codes():
         x = synth.make_x(spec, 2, seed=1).cuda()
         r = run_route(L, lg)
         y = forward(L, r, x, "decode")
-        g = route_host(r, 2, spec.top_k)
+        g = checked_route(spec, r, lg)
         ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, [0, 1], "decode")
         assert rel_err(y.cpu().numpy(), ref) < REL_TOL, hex(byte)
 

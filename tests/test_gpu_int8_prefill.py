@@ -13,7 +13,7 @@ import torch
 import int4_routed_expert_router_amd as coli
 import oracle
 import synth
-from gpu_util import check_prefill_output, forward, gpu_layer, route_host, run_route
+from gpu_util import check_prefill_output, forward, gpu_layer, checked_route, cover_tokens, run_route
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def test_int8_block_dots_extremes():
         assert np.all(d[0] == 32 * q * 127) and np.all(d[1] == -32 * q * 127)
 
 
-def _case(spec, T, seed=0, zipf=0.0, tokens=None):
+def _case(spec, T, seed=0, zipf=0.0, tokens=None, cover=None):
     print("int8 prefill case: H=%d I=%d E=%d S=%d k=%d T=%d" % (
         spec.hidden, spec.inter, spec.n_experts, spec.n_shared, spec.top_k, T), flush=True)
     L = gpu_layer(spec, seed=seed)
@@ -74,8 +74,11 @@ def _case(spec, T, seed=0, zipf=0.0, tokens=None):
     x = synth.make_x(spec, T, seed=seed).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "prefill")
-    g = route_host(r, T, spec.top_k)
+    g = checked_route(spec, r, lg)
     toks = list(range(T)) if tokens is None else list(tokens)
+    if cover is not None:
+        toks = sorted(set(toks) | set(cover_tokens(g, T, spec.top_k, **cover)))
+    print("  comparing %d tokens" % len(toks), flush=True)
     # int8 weights make a Q8_0 boundary decision of h weigh more than int4
     # codes do, so the comparison allows for those decisions explicitly
     err, n_budget = check_prefill_output(spec, L, g, x, y, toks)
@@ -87,9 +90,13 @@ def test_int8_prefill_olmoe_512_sampled():
     _case(_i8(synth.WORKLOADS["olmoe"].spec), 512, tokens=[0, 1, 63, 64, 200, 511])
 
 
-def test_int8_prefill_glm_sampled():
+@pytest.mark.timeout(600)
+def test_int8_prefill_glm_every_tile():
+    """GLM-shaped int8 layer at 700 tokens: every (expert, 64-token tile)
+    item's first and last row, the shared expert's tile boundaries and all
+    tokens of the hottest expert (about 300 tokens)."""
     w = synth.WORKLOADS["glm_prefill"]
-    _case(_i8(w.spec), 700, zipf=w.zipf_alpha, tokens=[0, 350, 699])
+    _case(_i8(w.spec), 700, zipf=w.zipf_alpha, tokens=[350], cover=dict(tile=64, hottest=1))
 
 
 @pytest.mark.parametrize("spec,T", [

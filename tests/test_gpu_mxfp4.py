@@ -13,7 +13,7 @@ import int4_routed_expert_router_amd as coli
 import oracle
 import synth
 from gpu_util import (REL_TOL, check_prefill_output, forward, gpu_layer, oracle_layer, rel_err,
-                      route_host, run_route)
+                      checked_route, cover_tokens, run_route)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _decode(spec, T, seed=0, zipf=0.0, tokens=None):
     x = synth.make_x(spec, T, seed=seed).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "decode")
-    g = route_host(r, T, spec.top_k)
+    g = checked_route(spec, r, lg)
     toks = list(range(T)) if tokens is None else tokens
     ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, toks, "decode")
     err = rel_err(y.cpu().numpy()[toks], ref)
@@ -61,7 +61,7 @@ def test_mxfp4_decode_every_code_and_scale_extremes():
     x = synth.make_x(spec, 3, seed=2).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "decode")
-    gh = route_host(r, 3, spec.top_k)
+    gh = checked_route(spec, r, lg)
     ref = oracle_layer(spec, L, gh["topk_idx"], gh["topk_w"], x, [0, 1, 2], "decode")
     assert rel_err(y.cpu().numpy(), ref) < REL_TOL
 
@@ -97,7 +97,7 @@ def test_mxfp4_block_dots_bit_exact(spec, T, experts):
             assert np.array_equal(dots.cpu().numpy(), want), (e, m)
 
 
-def _prefill(spec, T, seed=0, zipf=0.0, tokens=None):
+def _prefill(spec, T, seed=0, zipf=0.0, tokens=None, cover=None):
     print("mxfp4 prefill case: H=%d I=%d E=%d T=%d" % (spec.hidden, spec.inter, spec.n_experts, T),
           flush=True)
     L = gpu_layer(spec, seed=seed)
@@ -105,8 +105,11 @@ def _prefill(spec, T, seed=0, zipf=0.0, tokens=None):
     x = synth.make_x(spec, T, seed=seed).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "prefill")
-    g = route_host(r, T, spec.top_k)
+    g = checked_route(spec, r, lg)
     toks = list(range(T)) if tokens is None else list(tokens)
+    if cover is not None:
+        toks = sorted(set(toks) | set(cover_tokens(g, T, spec.top_k, **cover)))
+    print("  comparing %d tokens" % len(toks), flush=True)
     err, n_budget = check_prefill_output(spec, L, g, x, y, toks)
     print("  rel err %.3g, %d elements within the boundary budget" % (err, n_budget), flush=True)
     return L, r, x, y
@@ -116,9 +119,13 @@ def test_mxfp4_prefill_olmoe_sampled():
     _prefill(_f4(synth.WORKLOADS["olmoe"].spec), 512, tokens=[0, 1, 63, 64, 511])
 
 
-def test_mxfp4_prefill_glm_sampled():
+@pytest.mark.timeout(600)
+def test_mxfp4_prefill_glm_every_tile():
+    """GLM-shaped MXFP4 layer at 600 tokens: every (expert, 64-token tile)
+    item's first and last row, the shared expert's tile boundaries and all
+    tokens of the hottest expert (about 270 tokens)."""
     w = synth.WORKLOADS["glm_prefill"]
-    _prefill(_f4(w.spec), 600, zipf=w.zipf_alpha, tokens=[0, 599])
+    _prefill(_f4(w.spec), 600, zipf=w.zipf_alpha, tokens=[300], cover=dict(tile=64, hottest=1))
 
 
 @pytest.mark.parametrize("spec,T", [

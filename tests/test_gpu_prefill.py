@@ -7,7 +7,7 @@ import int4_routed_expert_router_amd as coli
 import oracle
 import synth
 from gpu_util import (REL_TOL, bf16_ulp_distance, forward, gpu_layer, oracle_layer, rel_err,
-                      route_host, run_route)
+                      checked_route, cover_tokens, run_route)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_block_dots_bit_exact(spec, T, experts):
 
 # ---------------------------------------------------------- layer output
 
-def _prefill_case(spec, T, seed=0, zipf=0.0, tokens=None):
+def _prefill_case(spec, T, seed=0, zipf=0.0, tokens=None, cover=None):
     print("prefill case: H=%d I=%d E=%d S=%d k=%d T=%d" % (
         spec.hidden, spec.inter, spec.n_experts, spec.n_shared, spec.top_k, T), flush=True)
     L = gpu_layer(spec, seed=seed)
@@ -85,8 +85,11 @@ def _prefill_case(spec, T, seed=0, zipf=0.0, tokens=None):
     x = synth.make_x(spec, T, seed=seed).cuda()
     r = run_route(L, lg)
     y = forward(L, r, x, "prefill")
-    g = route_host(r, T, spec.top_k)
+    g = checked_route(spec, r, lg)
     toks = list(range(T)) if tokens is None else list(tokens)
+    if cover is not None:
+        toks = sorted(set(toks) | set(cover_tokens(g, T, spec.top_k, **cover)))
+    print("  comparing %d tokens" % len(toks), flush=True)
     ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, toks, "prefill")
     err = rel_err(y.cpu().numpy()[toks], ref)
     print("  rel err %.3g" % err, flush=True)
@@ -101,12 +104,18 @@ def test_prefill_tiny():
 
 def test_prefill_olmoe_512_sampled():
     w = synth.WORKLOADS["olmoe"]
-    _prefill_case(w.spec, 512, tokens=[0, 1, 63, 64, 200, 333, 510, 511])
+    _prefill_case(w.spec, 512, tokens=[200, 333], cover=dict(tile=64, hottest=1))
 
 
-def test_prefill_glm_2048_sampled():
+@pytest.mark.timeout(600)
+def test_prefill_glm_2048_every_tile():
+    """The GLM-shaped prefill at 2,048 tokens: every (expert, 64-token tile)
+    item's first and last row, every partial last tile, the shared expert's
+    tile boundaries and all tokens of the three hottest experts, element by
+    element (about 1,100 of the 2,048 tokens)."""
     w = synth.WORKLOADS["glm_prefill"]
-    _prefill_case(w.spec, 2048, zipf=w.zipf_alpha, tokens=[0, 777, 2047])
+    _prefill_case(w.spec, 2048, zipf=w.zipf_alpha, tokens=[777],
+                  cover=dict(tile=64, hottest=3))
 
 
 @pytest.mark.parametrize("spec,T", [

@@ -52,8 +52,8 @@ MUTANTS = [
      "return ldexp(1.0, (int)sc[n * (K / 32) + k / 64] - 128);"),
     ("fp4 nibbles high first", "or_e2m1((k & 1) ? byte >> 4 : byte & 15)",
      "or_e2m1((k & 1) ? byte & 15 : byte >> 4)"),
-    ("up uses gate scales", "*su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);\n  const int f = L->fmt;\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {",
-     "*su = or_sc(L, e, 0), *sd = or_sc(L, e, 2);\n  const int f = L->fmt;\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {"),
+    ("up uses gate scales", "*su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);\n  const int f = L->fmt;\n  OR_ROWS_PARALLEL\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {",
+     "*su = or_sc(L, e, 0), *sd = or_sc(L, e, 2);\n  const int f = L->fmt;\n  OR_ROWS_PARALLEL\n  for (int64_t n = 0; n < I; ++n) {\n    double g = 0.0, u = 0.0;\n    for (int64_t k = 0; k < H; ++k) {"),
     ("silu sign flipped", "return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
     ("gate and up swapped in swiglu", "h[n] = or_silu(g) * u;", "h[n] = or_silu(u) * g;"),
     ("down transposed", "acc += (double)or_q(qd, I, m, n, f) * or_s(sd, I, m, n, f) * h[n];",
