@@ -210,5 +210,10 @@ def check_prefill_output(spec, L, g, x, y, tokens, tol=REL_TOL):
     rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
     denom = np.maximum(np.abs(ref), rms)
     err = np.abs(yv - ref)
-    assert np.all(err <= tol * denom + budget), float(np.max((err - budget) / denom))
+    over = (err - budget) / denom
+    worst = np.unravel_index(int(np.argmax(over)), over.shape)
+    print("  worst element: token %d, column %d: |err| / scale %.3g, budget / scale %.3g"
+          % (tokens[worst[0]], worst[1], err[worst] / denom[worst], budget[worst] / denom[worst]),
+          flush=True)
+    assert np.all(err <= tol * denom + budget), float(np.max(over))
     return rel_err(yv, ref), int(np.count_nonzero(err > tol * denom))

@@ -6,8 +6,8 @@ import torch
 import int4_routed_expert_router_amd as coli
 import oracle
 import synth
-from gpu_util import (REL_TOL, bf16_ulp_distance, forward, gpu_layer, oracle_layer, rel_err,
-                      checked_route, cover_tokens, run_route)
+from gpu_util import (check_prefill_output, checked_route, cover_tokens, forward, gpu_layer,
+                      run_route)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,11 +90,12 @@ def _prefill_case(spec, T, seed=0, zipf=0.0, tokens=None, cover=None):
     if cover is not None:
         toks = sorted(set(toks) | set(cover_tokens(g, T, spec.top_k, **cover)))
     print("  comparing %d tokens" % len(toks), flush=True)
-    ref = oracle_layer(spec, L, g["topk_idx"], g["topk_w"], x, toks, "prefill")
-    err = rel_err(y.cpu().numpy()[toks], ref)
-    print("  rel err %.3g" % err, flush=True)
-    assert err < REL_TOL
-    return L, r, x, y, ref, toks
+    # h is quantised to Q8_0 on both sides from fp32 values that differ by
+    # rounding order, so a code on a rounding boundary may differ; the
+    # comparison allows exactly those decisions (gpu_util.prefill_flip_budget)
+    err, n_budget = check_prefill_output(spec, L, g, x, y, toks)
+    print("  rel err %.3g, %d elements within the boundary budget" % (err, n_budget), flush=True)
+    return L, r, x, y, toks
 
 
 def test_prefill_tiny():
@@ -143,7 +144,7 @@ def test_prefill_largest_hidden_sampled():
 
 def test_prefill_deterministic_bf16_and_zero_scales():
     spec = synth.WORKLOADS["a3b"].spec
-    L, r, x, y, ref, toks = _prefill_case(spec, 96, zipf=synth.ZIPF_ALPHA)
+    L, r, x, y, toks = _prefill_case(spec, 96, zipf=synth.ZIPF_ALPHA)
     y2 = forward(L, r, x, "prefill")
     assert torch.equal(y, y2)
     yb = forward(L, r, x, "prefill", y_dtype=coli.COLI_OUT_BF16)
