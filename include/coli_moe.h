@@ -230,6 +230,25 @@ int coli_moe_forward_decode(const coli_moe_layer_t *layer,
                             int32_t T, void *y, int32_t y_dtype, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* coli_moe_forward_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The h and o rows live in a
+ * library-owned device array of 32 MiB (COLI_NOALLOC_SCRATCH_BYTES), one
+ * per GPU, held until the process ends; the call allocates and frees
+ * nothing.  Same arguments, kernels and results as coli_moe_forward_decode.
+ * Returns COLI_E_WORKSPACE, before any launch, when coli_moe_workspace_bytes
+ * (layer, T, COLI_ENTRY_DECODE) -- T*(k+S) rows of H + I fp32 values --
+ * exceeds the array; every GLM-shaped call (H + I = 8192, k + S = 9,
+ * T <= 64) fits, 64 tokens at k = 32 and H = 16384 do not.  The first call on a device
+ * looks up that device's copy (hipGetSymbolAddress) with it current; make
+ * it outside graph capture.  Every call on one GPU uses the same array, so
+ * calls that overlap on one GPU (several streams, several host threads) race
+ * and must be serialised by the caller.  No memory has to start at zero. */
+#define COLI_NOALLOC_SCRATCH_BYTES (32u << 20)
+int coli_moe_forward_decode_noalloc(const coli_moe_layer_t *layer,
+                                    const coli_moe_route_t *route, const uint16_t *x,
+                                    int32_t T, void *y, int32_t y_dtype, void *stream);
+
 /* Prefill-shaped forward, T in [1, 65536] tokens, on the integer path:
  *  1. x[t] (bf16 -> fp32) is quantised Q8_0 per 32 values (see below).
  *  2. g, u = sum over 32-blocks b of s[n][b/2] * d_x[t][b] * dot_b, where

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8, COLI_WEIGHTS_MXFP4,
     COLI_MFMA_BF16_K32, COLI_MFMA_I8_K32, COLI_MFMA_I8_K64,
     ColiError, KernelTimer, Layer, Route, coli_moe_block_dots, coli_moe_forward_decode,
+    coli_moe_forward_decode_noalloc,
     coli_moe_forward_prefill, coli_moe_quantize_int4_gs64, coli_moe_quantize_int8_gs64,
     coli_moe_quantize_mxfp4, coli_moe_quantize_q8_0, coli_moe_read_probe, coli_moe_mfma_probe,
     coli_moe_route, coli_moe_route_hidden,

@@ -76,6 +76,7 @@ def _load():
                                               sz, vp]
         lib.coli_moe_forward_decode.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
         lib.coli_moe_forward_prefill.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp, sz, vp]
+        lib.coli_moe_forward_decode_noalloc.argtypes = [P(_LayerC), P(_RouteC), vp, i32, vp, i32, vp]
         lib.coli_moe_quantize_q8_0.argtypes = [vp, i32, i64, vp, vp, vp]
         lib.coli_moe_quantize_int4_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
         lib.coli_moe_quantize_int8_gs64.argtypes = [vp, i32, i64, i64, vp, vp, vp]
@@ -90,7 +91,7 @@ def _load():
         lib.coli_moe_version.argtypes = []
         lib.coli_moe_version.restype = ctypes.c_char_p
         for f in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
-                  "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
+                  "coli_moe_forward_decode_noalloc", "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
                   "coli_moe_quantize_int4_gs64", "coli_moe_quantize_int8_gs64",
                   "coli_moe_quantize_mxfp4", "coli_moe_read_probe",
                   "coli_moe_mfma_probe"):
@@ -203,6 +204,13 @@ def coli_moe_forward_decode(layer: Layer, route: Route, x, T: int, y, y_dtype: i
     _check("coli_moe_forward_decode", _load().coli_moe_forward_decode(
         ctypes.byref(layer.c), ctypes.byref(route.c), _ptr(x), T, _ptr(y), y_dtype,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def coli_moe_forward_decode_noalloc(layer: Layer, route: Route, x, T: int, y, y_dtype: int,
+                                    stream=None):
+    _check("coli_moe_forward_decode_noalloc", _load().coli_moe_forward_decode_noalloc(
+        ctypes.byref(layer.c), ctypes.byref(route.c), _ptr(x), T, _ptr(y), y_dtype,
+        _stream(stream)))
 
 
 def coli_moe_forward_prefill(layer: Layer, route: Route, x, T: int, y, y_dtype: int, ws,

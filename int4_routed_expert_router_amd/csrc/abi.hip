@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace coli {
@@ -108,6 +110,40 @@ int launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_
 int launch_mfma_probe(int kind, int iters, int workgroups, uint32_t *sink, hipStream_t s);
 }
 
+namespace coli {
+namespace {
+
+// Library-owned decode workspace for coli_moe_forward_decode_noalloc: one
+// copy per GPU, held until the process ends.  Host code never uses this
+// name as an address (on the host it is only a stand-in for the symbol);
+// the device address of each GPU's copy comes from hipGetSymbolAddress and
+// is cached per device below.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static_assert(kScratchBytes == COLI_NOALLOC_SCRATCH_BYTES, "scratch size and header disagree");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch array, looked up on the
+// first call on that device (with that device current) and cached.
+int scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return COLI_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return COLI_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return COLI_OK;
+}
+
+}  // namespace
+}  // namespace coli
+
 using namespace coli;
 
 extern "C" {
@@ -168,6 +204,22 @@ int coli_moe_forward_decode(const coli_moe_layer_t *layer, const coli_moe_route_
   Layer L;
   const int rc = check_forward(layer, route, x, T, y, y_dtype, ws, ws_bytes, COLI_ENTRY_DECODE, &L);
   if (rc) return rc;
+  return launch_decode(L, *route, x, T, y, y_dtype, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+int coli_moe_forward_decode_noalloc(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
+                                    const uint16_t *x, int32_t T, void *y, int32_t y_dtype,
+                                    void *stream) {
+  Layer L;
+  // validated against the scratch size with a stand-in address (256-aligned,
+  // never dereferenced); the real address is only taken once the call is valid
+  void *const stand_in = reinterpret_cast<void *>(uintptr_t(256));
+  const int rc = check_forward(layer, route, x, T, y, y_dtype, stand_in, kScratchBytes,
+                               COLI_ENTRY_DECODE, &L);
+  if (rc) return rc;
+  void *ws = nullptr;
+  const int prc = scratch_ptr(&ws);
+  if (prc) return prc;
   return launch_decode(L, *route, x, T, y, y_dtype, ws, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("coli_moe_route", "coli_moe_route_hidden", "coli_moe_forward_decode",
               "coli_moe_forward_prefill", "coli_moe_workspace_bytes", "coli_moe_quantize_q8_0",
-              "coli_moe_quantize_int4_gs64", "coli_moe_block_dots", "coli_moe_strerror", "coli_moe_version"):
+              "coli_moe_quantize_int4_gs64", "coli_moe_block_dots", "coli_moe_strerror", "coli_moe_version",
+              "coli_moe_forward_decode_noalloc"):
         assert n in names
 
 
@@ -98,6 +99,22 @@ def test_forward_rejects_bad_calls():
     assert dec(ctypes.byref(L.c), r, FAKE, 4, FAKE, 0, FAKE + 16, need, None) == -4
     need = coli.coli_moe_workspace_bytes(L, 300, coli.COLI_ENTRY_PREFILL)
     assert pre(ctypes.byref(L.c), r, FAKE, 300, FAKE, 0, FAKE, need - 1, None) == -3
+
+
+def test_noalloc_decode_validates_before_any_hip_call():
+    lib = binding.raw_library()
+    na = lib.coli_moe_forward_decode_noalloc
+    r = ctypes.byref(_FakeRoute().c)
+    assert na(ctypes.byref(_layer(hidden=100).c), r, FAKE, 1, FAKE, 0, None) == -1  # layer
+    assert na(ctypes.byref(_layer().c), r, FAKE, 65, FAKE, 0, None) == -1           # T > 64
+    assert na(ctypes.byref(_layer().c), r, FAKE + 2, 1, FAKE, 0, None) == -4        # x align
+    # past the 32 MiB scratch: 64 tokens x 33 rows of H + I = 16384 + 512 fp32 values
+    big = _layer(hidden=16384, n_experts=64, top_k=32)
+    assert coli.coli_moe_workspace_bytes(big, 64, coli.COLI_ENTRY_DECODE) > 32 << 20
+    assert na(ctypes.byref(big.c), r, FAKE, 64, FAKE, 0, None) == -3
+    # the largest GLM-shaped call fits
+    glm = _layer(hidden=6144, inter=2048)
+    assert coli.coli_moe_workspace_bytes(glm, 64, coli.COLI_ENTRY_DECODE) <= 32 << 20
 
 
 def test_route_quantize_dots_reject_bad_calls():
