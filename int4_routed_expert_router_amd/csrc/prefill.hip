@@ -65,10 +65,15 @@ COLI_DEV void q8_0_block(const float v[32], uint32_t qw[8], uint16_t &d16) {
   }
 }
 
+// PR (the int4 path of the DMA GEMM): the codes of every 8 values are
+// stored as [k0 k2 k4 k6 k1 k3 k5 k7], the order of unpacked nibbles, and
+// the block's record {-M*d16, d16} (fp32) replaces the fp16 scale.
+template <bool PR>
 __global__ void __launch_bounds__(kThreads) quantize_kernel(const void *__restrict__ src,
                                                             int src_dtype, int64_t nblocks,
                                                             int8_t *__restrict__ q,
-                                                            uint16_t *__restrict__ d) {
+                                                            uint16_t *__restrict__ d,
+                                                            float2 *__restrict__ rec) {
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (b >= nblocks) return;
   float v[32];
@@ -98,10 +103,23 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const void *__restri
   uint32_t qw[8];
   uint16_t d16;
   q8_0_block(v, qw, d16);
+  if (PR) {
+#pragma unroll
+    for (int w = 0; w < 8; w += 2) {
+      const uint32_t lo = qw[w], hi = qw[w + 1];
+      qw[w] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);
+      qw[w + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);
+    }
+  }
   uint4 *qo = reinterpret_cast<uint4 *>(q) + 2 * b;
   qo[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
   qo[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
-  d[b] = d16;
+  if (PR) {
+    const float df = f16_to_f32(d16);
+    rec[b] = make_float2(-kMagicF * df, df);
+  } else {
+    d[b] = d16;
+  }
 }
 
 // ---------------------------------------------------------------- plan
@@ -906,16 +924,410 @@ gemm4_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
   }
 }
 
+// ------------------------------------ GEMM from DMA-filled stages (int4)
+//
+// The same work items and arithmetic as gemm4_kernel, arranged for the
+// vector ALUs, which bound this contraction: every output needs two fp32
+// FMAs per 32-block (activation scale with the offset removed, then the
+// weight scale), against 1/16 of a matrix-core instruction.
+//  * Stages of 256 k are copied global -> LDS with global_load_lds (the
+//    data never passes through registers): 128 weight rows of nibbles
+//    (16 KB), the tile's 64 token rows of int8 activations (16 KB), the
+//    rows' fp16 group scales and the tokens' block records {-M*d, d}.  Two
+//    stages alternate, so one is loading while the other is computed.
+//  * Wave w computes weight rows [16w, 16w+16) and [64+16w, 64+16w+16) (for
+//    gate/up: gate and up of the same 16 channels) against each 16-token
+//    subtile that holds a token; empty subtiles are skipped (templated on
+//    their count), so a tile of n tokens costs ceil(n/16) subtiles.
+//  * The nibbles are unpacked as each wave reads its operand: a dword of 8
+//    codes gives (w << 4) & 0xf0f0f0f0 (k 0,2,4,6 times 16) and w &
+//    0xf0f0f0f0 (k 1,3,5,7 times 16).  The activations are stored in that
+//    order within every 8 values ([x0 x2 x4 x6 x1 x3 x5 x7]) by whoever
+//    writes them (the Q8_0 kernel for x, the gate/up epilogue for h), so
+//    the pairing of weights and activations, and every block dot, is exact.
+//  * LDS layouts are XOR-swizzled at 16-byte granularity so that each DMA
+//    instruction moves whole 128-byte lines and each operand read is free
+//    of bank conflicts: weight row r keeps block c at chunk c ^ ((r>>1)&7),
+//    token t keeps its 16-byte piece j at j ^ (t & 15).
+constexpr int kSK = 256;            // k per stage
+constexpr int kSB = kSK / 32;       // 32-blocks per stage
+#define COLI_LDS __attribute__((address_space(3)))
+
+struct DStage {
+  uint4 w[BR * 8];   // [row][chunk]: 16 B of nibbles = one 32-block of one row
+  uint4 a[BM * 16];  // [token][chunk]: 16 B of int8 = half a 32-block
+  uint2 sw[BR];      // [row]: fp16 scales of the stage's four 64-groups
+  uint4 sa[BM * 4];  // [token][pair]: records {c, d} of blocks 2p and 2p+1
+};
+
+// global -> LDS, 16 (or 4) bytes per lane; lane i lands at lds + 16*i (4*i).
+COLI_DEV void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (COLI_LDS void *)lds, 16, 0, 0);
+}
+COLI_DEV void dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (COLI_LDS void *)lds, 4, 0, 0);
+}
+COLI_DEV void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Per-lane DMA sources of a work item; a stage adds a fixed byte step.
+struct DSrc {
+  const uint8_t *w[4];  // weight chunk of instruction 4*wave + j (step 128 B)
+  const int8_t *a[4];   // activation chunk of instruction 4*wave + j (step 256 B)
+  const uint8_t *sw;    // 4 bytes of scales (step 8 B)
+  const uint8_t *sa;    // 16 bytes of records (step 64 B)
+};
+
+// Natural-order 8 int8 values (lo = k0..3, hi = k4..7) -> the even/odd
+// order of the unpacked nibbles: [k0 k2 k4 k6], [k1 k3 k5 k7].
+COLI_DEV uint2 even_odd8(uint32_t lo, uint32_t hi) {
+  return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x06040200u),
+                    __builtin_amdgcn_perm(hi, lo, 0x07050301u));
+}
+
+template <int MODE, int NTS>
+COLI_DEV void dgemm_item(const GemmArgs &g, const Item &it, const int *rowid, const int *outrow,
+                         const uint8_t *wq, const uint16_t *ws, const float2 *rec,
+                         DStage &B0, DStage &B1, float (*xch)[4][16], int8_t *qh_out,
+                         float2 *rech_out, float *o_out, int32_t *dots_out) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kq = lane >> 4, lr = lane & 15;
+  const int nst = g.K / kSK;
+
+  // ---- DMA sources of this lane
+  DSrc src;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // weights: instruction q = 4*wave + j covers item rows 8q..8q+7
+    const int row = 32 * wv + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    const uint8_t *q;
+    const uint16_t *unused;
+    weight_row<MODE == kDots ? kDown : MODE>(g, it.n0, row, q, unused);
+    src.w[j] = q + 16 * chunk;
+    // activations: instruction q covers tokens 4q..4q+3
+    const int t = 16 * wv + 4 * j + (lane >> 4);
+    src.a[j] = g.act + (int64_t)rowid[t] * g.K + 16 * ((lane & 15) ^ (t & 15));
+  }
+  {
+    const int row = 32 * wv + (lane >> 1);
+    const uint8_t *unused;
+    const uint16_t *s;
+    weight_row<MODE == kDots ? kDown : MODE>(g, it.n0, row, unused, s);
+    src.sw = reinterpret_cast<const uint8_t *>(s) + 4 * (lane & 1);
+    // record pairs are stored at position pair ^ ((t >> 2) & 3): the 16
+    // tokens a read covers then fall on distinct 16-byte bank groups
+    const int t = 16 * wv + (lane >> 2);
+    src.sa = reinterpret_cast<const uint8_t *>(rec + (int64_t)rowid[t] * (g.K / 32)) +
+             16 * ((lane & 3) ^ ((t >> 2) & 3));
+  }
+  (void)wq;
+  (void)ws;
+  // DMA instruction p (0..9) of a stage: 4 of weights, 4 of activations,
+  // the scales and the records.  A stage's ten are spread over the blocks
+  // of the previous stage's compute, so no wavefront stalls behind a burst
+  // of them on the memory pipeline while it has arithmetic to issue.
+  // Wave wv moves the activations and records of tokens 16wv..16wv+15, so
+  // the waves past the tile's last 16-token subtile move none.
+  const bool tok_live = wv < NTS;
+  auto issue_part = [&](DStage &B, int st, int p) {
+    if (p < 4) {
+      dma16(src.w[p] + st * (kSK / 2), &B.w[(4 * wv + p) * 64]);
+    } else if (p < 8) {
+      if (tok_live) dma16(src.a[p - 4] + st * kSK, &B.a[(4 * wv + p - 4) * 64]);
+    } else if (MODE != kDots) {
+      if (p == 8) dma4(src.sw + st * 8, reinterpret_cast<uint8_t *>(B.sw) + 256 * wv);
+      else if (tok_live) dma16(src.sa + st * 64, &B.sa[64 * wv]);
+    }
+  };
+  auto issue = [&](DStage &B, int st) {
+#pragma unroll
+    for (int p = 0; p < 10; ++p) issue_part(B, st, p);
+  };
+
+  float acc[2][NTS][4];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rs][ts][i] = 0.0f;
+  coli_i32x4 magic = {(int)kMagic, (int)kMagic, (int)kMagic, (int)kMagic};
+  asm volatile("" : "+v"(magic));
+
+  // per-lane LDS byte offsets of the operand reads (before the block XOR)
+  const int rA = 16 * wv + lr;                               // row of subtile 0
+  const uint32_t offA = rA * 128 + 16 * ((rA >> 1) & 7) + 4 * kq;  // ^ 16*b
+  const uint32_t offB = lr * 256 + 16 * ((kq >> 1) ^ lr) + 8 * (kq & 1);  // ^ 32*b
+  const int rS = 16 * wv + 4 * kq;                            // first row of the lane's scales
+
+  struct Ops {
+    long a[2], b[NTS];
+  };
+  auto read_ops = [&](const DStage &B, int b, Ops &o) {
+    const char *wb = reinterpret_cast<const char *>(B.w) + (offA ^ (16 * b));
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const uint32_t x = *reinterpret_cast<const uint32_t *>(wb + rs * 64 * 128);
+      const uint32_t ev = (x << 4) & 0xf0f0f0f0u, od = x & 0xf0f0f0f0u;
+      o.a[rs] = (long)(((uint64_t)od << 32) | ev);
+    }
+    const char *ab = reinterpret_cast<const char *>(B.a) + (offB ^ (32 * b));
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      uint2 v = *reinterpret_cast<const uint2 *>(ab + ts * 16 * 256);
+      if (MODE == kDots) v = even_odd8(v.x, v.y);  // caller's codes are in natural order
+      o.b[ts] = (long)(((uint64_t)v.y << 32) | v.x);
+    }
+  };
+  auto mfmas = [&](const Ops &o, coli_i32x4 (&d)[2][NTS]) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int ts = 0; ts < NTS; ++ts)
+        d[rs][ts] = __builtin_amdgcn_mfma_i32_16x16x32_i8(o.a[rs], o.b[ts], magic, 0, 0, 0);
+  };
+  // weight scales of group gq for the lane's 8 rows (from the stage's fp16
+  // scales, read once per stage), and the token records of the group
+  struct Scl {
+    float w[2][4];
+    float4 r[NTS];  // {c, d} of the group's two blocks
+  };
+  uint4 swh[2][2];  // [rs][rows 4kq+{0,1} | 4kq+{2,3}]: 4 fp16 each
+  auto read_sw = [&](const DStage &B) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        swh[rs][h] = *reinterpret_cast<const uint4 *>(&B.sw[rS + 64 * rs + 2 * h]);
+  };
+  const int fsa = (lr >> 2) & 3;
+  auto read_scl = [&](const DStage &B, int gq, Scl &c) {
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 q = swh[rs][i >> 1];
+        const uint32_t hw = (i & 1) ? ((gq & 2) ? q.w : q.z) : ((gq & 2) ? q.y : q.x);
+        c.w[rs][i] = f16_to_f32((uint16_t)((gq & 1) ? hw >> 16 : hw));
+      }
+    const uint4 *sa = &B.sa[lr * 4 + (gq ^ fsa)];
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      const uint4 v = sa[ts * 64];
+      c.r[ts] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                            __uint_as_float(v.w));
+    }
+  };
+  auto finish = [&](int st, int b, const Scl &c, const coli_i32x4 (&d)[2][NTS]) {
+    if (MODE == kDots) {
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int ts = 0; ts < NTS; ++ts) {
+          const int m = 16 * ts + lr;
+          if (m >= it.ntok) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = it.n0 + 16 * wv + 64 * rs + 4 * kq + i;
+            if (n >= g.rows) continue;
+            dots_out[((int64_t)(it.row0 + m) * g.rows + n) * (g.K / 32) + kSB * st + b] =
+                (d[rs][ts][i] - (int)kMagic) >> 4;
+          }
+        }
+      return;
+    }
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      const float cc = (b & 1) ? c.r[ts].z : c.r[ts].x;
+      const float dd = (b & 1) ? c.r[ts].w : c.r[ts].y;
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[rs][ts][i] =
+              fmaf(c.w[rs][i], fmaf(__int_as_float(d[rs][ts][i]), dd, cc), acc[rs][ts][i]);
+    }
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int ts = 0; ts < NTS; ++ts)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[rs][ts][i]));
+  };
+  // one stage: block b's MFMAs run while block b-1's epilogue runs; the
+  // next stage's DMA (into `N`, if `nxt` >= 0) is issued along the way
+  auto compute = [&](const DStage &B, int st, DStage &N, int nxt) {
+    Ops o;
+    Scl c0, c1;
+    coli_i32x4 d0[2][NTS], d1[2][NTS];
+    read_ops(B, 0, o);
+    if (MODE != kDots) {
+      read_sw(B);
+      read_scl(B, 0, c0);
+    }
+    mfmas(o, d0);
+#pragma unroll
+    for (int b = 0; b < kSB; ++b) {
+      if (nxt >= 0) {
+        issue_part(N, nxt, b);
+        if (b < 2) issue_part(N, nxt, 8 + b);
+      }
+      if (b + 1 < kSB) {
+        read_ops(B, b + 1, o);
+        if (MODE != kDots && ((b + 1) & 1) == 0) read_scl(B, (b + 1) >> 1, ((b >> 1) & 1) ? c0 : c1);
+        mfmas(o, (b & 1) ? d0 : d1);
+      }
+      finish(st, b, ((b >> 1) & 1) ? c1 : c0, (b & 1) ? d1 : d0);
+    }
+  };
+
+  issue(B0, 0);
+  wait_dma();
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    compute(B0, st, B1, st + 1 < nst ? st + 1 : -1);
+    wait_dma();
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    compute(B1, st + 1, B0, st + 2 < nst ? st + 2 : -1);
+    wait_dma();
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  if (MODE == kGateUp) {
+    // h = silu(g) * u for channels n0 + 16*wv + 4*kq + i; the codes are in
+    // units of 16 (x16 nibbles), removed here exactly.  Q8_0 of h per 32
+    // channels: waves 2p and 2p+1 hold the two halves of block p.
+    float hv[NTS][4];
+    float am[NTS];
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hv[ts][i] = silu_mul(acc[0][ts][i] * 0.0625f, acc[1][ts][i] * 0.0625f);
+        a = fmaxf(a, fabsf(hv[ts][i]));
+      }
+      a = fmaxf(a, __shfl_xor(a, 16, 64));
+      a = fmaxf(a, __shfl_xor(a, 32, 64));
+      am[ts] = a;
+      if (kq == 0) xch[wv][ts][lr] = a;
+    }
+    __syncthreads();
+    const int I = g.rows;
+    const int ch0 = it.n0 + 16 * wv;  // first channel of this wave
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      const float amax = fmaxf(am[ts], xch[wv ^ 1][ts][lr]);
+      const float dq = __fdiv_rn(amax, 127.0f);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int q = 0;
+        if (amax != 0.0f) {
+          q = (int)roundf(__fdiv_rn(hv[ts][i], dq));
+          q = max(-127, min(127, q));
+        }
+        packed |= (uint32_t)(q & 0xff) << (8 * i);
+      }
+      // lanes kq = 2m, 2m+1 hold channels 8m..8m+3 and 8m+4..8m+7; write
+      // them as [c0 c2 c4 c6] and [c1 c3 c5 c7]
+      const uint32_t e = __builtin_amdgcn_perm(packed, packed, 0x03010200u);  // q0 q2 q1 q3
+      const uint32_t p = (uint32_t)__shfl_xor((int)e, 16, 64);
+      const uint32_t out = (kq & 1) ? ((p >> 16) | (e & 0xffff0000u)) : ((e & 0xffffu) | (p << 16));
+      const int m = 16 * ts + lr;
+      if (m < it.ntok && ch0 < I) {
+        const int64_t orow = outrow[m];
+        *reinterpret_cast<uint32_t *>(qh_out + orow * I + ch0 + 4 * kq) = out;
+        if ((wv & 1) == 0 && kq == 0) {
+          const float d16 = f16_to_f32(f32_to_f16_bits(dq));
+          rech_out[orow * (I / 32) + ch0 / 32] = make_float2(-kMagicF * d16, d16);
+        }
+      }
+    }
+  } else if (MODE == kDown) {
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      const int m = 16 * ts + lr;
+      if (m >= it.ntok) continue;
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const int n = it.n0 + 16 * wv + 64 * rs + 4 * kq;
+        if (n < g.rows)
+          *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
+              make_float4(acc[rs][ts][0] * 0.0625f, acc[rs][ts][1] * 0.0625f,
+                          acc[rs][ts][2] * 0.0625f, acc[rs][ts][3] * 0.0625f);
+      }
+    }
+  }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dgemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
+             const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
+             int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
+             const float2 *__restrict__ rec, int8_t *__restrict__ qh_out,
+             float2 *__restrict__ rech_out, float *__restrict__ o_out,
+             int32_t *__restrict__ dots_out) {
+  __shared__ DStage B0;
+  __shared__ DStage B1;
+  __shared__ int rowid[BM];
+  __shared__ int outrow[BM];
+  __shared__ float xch[4][4][16];
+  const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
+  const int items = band_items(ntiles, n_ntiles);
+  const int G = gridDim.x;
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int item = vid; item < items; item += G) {
+    int tile, ntile;
+    item_coords(item, n_ntiles, tile, ntile);
+    if (tile >= ntiles) continue;
+    const Item it = setup_item<MODE>(tile, ntile, tiles, fixed_ntok, fixed_expert, r, T, k,
+                                     rowid, outrow);
+    GemmArgs ge = g;
+    ge.wq = g.wq + (int64_t)it.expert * expert_stride_q;
+    ge.ws = g.ws + (int64_t)it.expert * expert_stride_s;
+    const int nts = (it.ntok + 15) >> 4;
+    switch (nts) {
+      case 1:
+        dgemm_item<MODE, 1>(ge, it, rowid, outrow, ge.wq, ge.ws, rec, B0, B1, xch, qh_out,
+                            rech_out, o_out, dots_out);
+        break;
+      case 2:
+        dgemm_item<MODE, 2>(ge, it, rowid, outrow, ge.wq, ge.ws, rec, B0, B1, xch, qh_out,
+                            rech_out, o_out, dots_out);
+        break;
+      case 3:
+        dgemm_item<MODE, 3>(ge, it, rowid, outrow, ge.wq, ge.ws, rec, B0, B1, xch, qh_out,
+                            rech_out, o_out, dots_out);
+        break;
+      default:
+        dgemm_item<MODE, 4>(ge, it, rowid, outrow, ge.wq, ge.ws, rec, B0, B1, xch, qh_out,
+                            rech_out, o_out, dots_out);
+        break;
+    }
+  }
+}
+
 struct PrefillWs {
   int8_t *qx;
   uint16_t *dx;
   int8_t *qh;
   uint16_t *dh;
+  float2 *rx;  // DMA GEMM: block records of x and of h
+  float2 *rh;
   float *o;
   int4 *tiles;
   int *ntiles;
   size_t total;
 };
+
+// Layers the DMA GEMM serves: int4 codes, both reduction lengths whole
+// 256-k stages.
+bool dgemm_layer(const Layer &L) { return !L.w8 && !L.f4 && L.H % kSK == 0 && L.I % kSK == 0; }
 
 int max_tiles(const Layer &L, int T) {
   const int64_t P = (int64_t)T * L.k;
@@ -935,6 +1347,8 @@ PrefillWs carve(const Layer &L, int T, void *base) {
   w.dx = reinterpret_cast<uint16_t *>(take((size_t)T * (L.H / 32) * 2));
   w.qh = reinterpret_cast<int8_t *>(take((size_t)rows * L.I));
   w.dh = reinterpret_cast<uint16_t *>(take((size_t)rows * (L.I / 32) * 2));
+  w.rx = reinterpret_cast<float2 *>(take((size_t)T * (L.H / 32) * 8));
+  w.rh = reinterpret_cast<float2 *>(take((size_t)rows * (L.I / 32) * 8));
   w.o = reinterpret_cast<float *>(take((size_t)rows * L.H * 4));
   w.tiles = reinterpret_cast<int4 *>(take((size_t)max_tiles(L, T) * sizeof(int4)));
   w.ntiles = reinterpret_cast<int *>(take(sizeof(int)));
@@ -961,14 +1375,68 @@ int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, u
                          hipStream_t s) {
   const int64_t nb = n / 32;
   const int64_t grid = (nb + kThreads - 1) / kThreads;
-  launch_k(COLI_K_QUANTIZE, quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, src,
-           src_dtype, nb, q, d);
+  launch_k(COLI_K_QUANTIZE, quantize_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+           src, src_dtype, nb, q, d, nullptr);
   return hip_status(hipGetLastError());
 }
+
+namespace {
+
+// The int4 forward on the DMA GEMM (dgemm_layer).
+int launch_prefill_dgemm(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                         void *y, int y_dtype, const PrefillWs &w, hipStream_t s) {
+  {
+    const int64_t nb = (int64_t)T * L.H / 32;
+    launch_k(COLI_K_QUANTIZE, quantize_kernel<true>, dim3((unsigned)((nb + kThreads - 1) / kThreads)),
+             dim3(kThreads), 0, s, (const void *)x, (int)COLI_SRC_BF16, nb, w.qx,
+             (uint16_t *)nullptr, w.rx);
+  }
+  launch_k(COLI_K_PLAN, plan_kernel, dim3(1), dim3(1024), 0, s, r, T, L.k, L.E, L.S, w.tiles,
+           w.ntiles);
+  if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  const int mt = max_tiles(L, T);
+  {  // gate / up + SwiGLU + Q8_0(h)
+    GemmArgs g{};
+    g.wq = L.q4;
+    g.ws = L.scales;
+    g.rows = L.I;
+    g.K = L.H;
+    g.rs = 1;
+    g.act = w.qx;
+    g.up_offset_q = (int64_t)L.I * L.H / 2;
+    g.up_offset_s = (int64_t)L.I * L.H / 64;
+    const int nn = L.I / 64;
+    launch_k(COLI_K_GEMM_GATEUP, dgemm_kernel<kGateUp>,
+             dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles,
+             w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes, L.expert_scales,
+             (const float2 *)w.rx, w.qh, w.rh, (float *)nullptr, (int32_t *)nullptr);
+    if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  }
+  {  // down
+    GemmArgs g{};
+    g.rs = 1;
+    g.wq = L.q4 + (int64_t)L.I * L.H;
+    g.ws = L.scales + (int64_t)2 * L.I * L.H / 64;
+    g.rows = L.H;
+    g.K = L.I;
+    g.act = w.qh;
+    const int nn = (L.H + BR - 1) / BR;
+    launch_k(COLI_K_GEMM_DOWN, dgemm_kernel<kDown>, dim3(grid_for(band_items_host(mt, nn))),
+             dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0, 0, T, L.k, nn, L.expert_bytes,
+             L.expert_scales, (const float2 *)w.rh, (int8_t *)nullptr, (float2 *)nullptr, w.o,
+             (int32_t *)nullptr);
+    if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  }
+  launch_combine(w.o, r, T, L.H, L.k, L.S, y, y_dtype, s);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace
 
 int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T, void *y,
                    int y_dtype, void *ws, hipStream_t s) {
   const PrefillWs w = carve(L, T, ws);
+  if (dgemm_layer(L)) return launch_prefill_dgemm(L, r, x, T, y, y_dtype, w, s);
   int rc = launch_quantize_q8_0(x, COLI_SRC_BF16, (int64_t)T * L.H, w.qx, w.dx, s);
   if (rc) return rc;
   launch_k(COLI_K_PLAN, plan_kernel, dim3(1), dim3(1024), 0, s, r, T, L.k, L.E, L.S, w.tiles,
@@ -1034,6 +1502,13 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
   const int nn = (g.rows + BR - 1) / BR;
   const int ntile = (T + BM - 1) / BM;
   coli_moe_route_t none{};
+  if (dgemm_layer(L)) {
+    launch_k(COLI_K_BLOCK_DOTS, dgemm_kernel<kDots>, dim3(grid_for(band_items_host(ntile, nn))),
+             dim3(kThreads), 0, s, g, none, (const int4 *)nullptr, (const int *)nullptr, T, expert,
+             T, 1, nn, L.expert_bytes, L.expert_scales, (const float2 *)nullptr, (int8_t *)nullptr,
+             (float2 *)nullptr, (float *)nullptr, dots);
+    return hip_status(hipGetLastError());
+  }
   launch_k(COLI_K_BLOCK_DOTS,
            wf == kFmtF4 ? gemm4_kernel<kDots, kFmtF4>
            : wf == kFmtI8 ? gemm4_kernel<kDots, kFmtI8>
