@@ -323,26 +323,59 @@ def cpu_baseline_decode(spec, layers_obj, x_list, logits_list, budget_s=12.0):
     T = x_list[0].shape[0]
     for l in range(len(layers_obj)):
         lg = logits_list[l].cpu().numpy()
-        r = oracle.route(lg, spec.top_k, spec.flags, spec.routed_scale)
-        used = sorted(set(int(e) for e in r["topk_idx"].ravel()))
+        # only the experts the token uses are copied to the host (not timed)
+        r0 = oracle.route(lg, spec.top_k, spec.flags, spec.routed_scale)
+        used = sorted(set(int(e) for e in r0["topk_idx"].ravel()))
         experts = used + ([spec.n_experts] if spec.n_shared else [])
         q4h, sch = synth.expert_slice(spec, layers_obj[l].q4, layers_obj[l].scales, experts)
         remap = np.zeros(spec.n_experts, np.int32)
         remap[used] = np.arange(len(used), dtype=np.int32)
         xb = synth.bf16_bits(x_list[l])
         t0 = time.perf_counter()
+        r = oracle.route(lg, spec.top_k, spec.flags, spec.routed_scale)
         oracle.forward_decode(spec.hidden, spec.inter, len(used), spec.n_shared, spec.top_k,
                               q4h, sch, remap[r["topk_idx"]], r["topk_w"], xb)
         t_total += time.perf_counter() - t0
         done += 1
         if t_total >= budget_s:
             break
-    # the oracle parallelises over tokens (OpenMP), so it uses min(T, cores)
-    cores = min(T, oracle.threads())
+    # with fewer tokens than threads the oracle splits each token's output
+    # rows across its OpenMP threads, so every thread works
+    cores = oracle.threads()
     return {"value": T * done / t_total, "unit": "MoE-layer tokens/s", "cores": cores,
             "kind": "oracle", "host": cpu_host(),
             "sample": "%d of the 12 layers, %d token(s) each, route + decode-mode layer in fp64 "
                       "(%.1f s)" % (done, T, t_total)}
+
+
+def cpu_baseline_prefill(spec, layer, lg, x, T, budget_s=12.0, chunk=32):
+    """The CPU oracle on a bounded token sample of a prefill workload: the
+    integer-path layer (Q8_0, exact block dots, fp64 sums) for the first
+    tokens of the batch, in chunks of `chunk` tokens until about `budget_s`
+    seconds have run."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    lgh = lg.cpu().numpy()
+    q4h, sch = synth.expert_slice(spec, layer.q4, layer.scales, list(range(spec.n_total)))
+    xb = synth.bf16_bits(x)
+    done, t_total = 0, 0.0
+    while done < T and t_total < budget_s:
+        n = min(chunk, T - done)
+        t0 = time.perf_counter()
+        r = oracle.route(lgh[done:done + n], spec.top_k, spec.flags, spec.routed_scale)
+        oracle.forward_prefill(spec.hidden, spec.inter, spec.n_experts, spec.n_shared,
+                               spec.top_k, q4h, sch, r["topk_idx"], r["topk_w"],
+                               xb[done:done + n], weights=spec.weights)
+        t_total += time.perf_counter() - t0
+        done += n
+    ops = 2.0 * 3 * spec.hidden * spec.inter * done * (spec.top_k + spec.n_shared)
+    return {"value": done / t_total, "unit": "prefill tokens/s", "cores": oracle.threads(),
+            "kind": "oracle", "int8_ops_per_s": round(ops / t_total, 1),
+            "sample": "the first %d of %d tokens, route + integer-path layer in fp64 (%.1f s)"
+                      % (done, T, t_total)}
 
 
 def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=None):
@@ -362,7 +395,7 @@ def secondary_decode(name, spec, T, zipf, layers, steps, warmup, layer_weights=N
 
 
 def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
-                      k32_ceiling=None):
+                      k32_ceiling=None, cpu=False):
     import torch
 
     import int4_routed_expert_router_amd as coli
@@ -408,6 +441,8 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
     if k32_ceiling:  # the measured rate of the instruction the GEMM issues
         out["measured_k32_TOPS"] = k32_ceiling
         out["frac_of_measured_k32"] = round(ops / (ms * 1e-3) / 1e12 / k32_ceiling, 4)
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline_prefill(spec, Ls[0], lg, x, T)
     return out
 
 
@@ -589,7 +624,16 @@ def main():
                 "avg_us": round(gu["avg_us"], 3), "launches_timed": gu["n"],
                 "kernel_source_digest": kernel_digest(),
                 "kernels_us": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
+    # the decode GEMV as a whole: gate/up and down bytes over their summed time
+    dn = kern["decode_down"]
+    dn_bytes = (spec.top_k + spec.n_shared) * spec.inter * spec.hidden * (0.5 + 2 / 64)
+    gemv_gbps = (gu_bytes + dn_bytes) / ((gu["avg_us"] + dn["avg_us"]) * 1e-6) / 1e9
+    roofline["decode_gemv_combined"] = {
+        "kernels": "decode_gateup + decode_down", "bytes_per_layer": int(gu_bytes + dn_bytes),
+        "avg_us": round(gu["avg_us"] + dn["avg_us"], 3), "achieved": round(gemv_gbps, 1),
+        "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4)}
     log("kernels (us):", roofline["kernels_us"])
+    log("decode GEMV (gate/up + down): %.0f GB/s, %.1f%% of 8 TB/s" % (gemv_gbps, 100 * gemv_gbps / HBM_PEAK_GBPS))
     # the same kernel against what a plain read of 120 MB reaches on this chip
     rc = read_ceiling(sizes_mb=(120,), reps=20)["results"]["120 MB"]["GB_per_s"]
     roofline["measured_read_GBps"] = rc
@@ -609,7 +653,8 @@ def main():
         pw = synth.WORKLOADS["glm_prefill"]
         k32 = mfma_ceiling(reps=3)["results"]["i8_16x16x32"]["T_per_s"]
         secondary.append(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
-                                           10, 2, layer=stack.layers[0], k32_ceiling=k32))
+                                           10, 2, layer=stack.layers[0], k32_ceiling=k32,
+                                           cpu=not args.no_cpu))
         del stack
         torch.cuda.empty_cache()
         secondary.append(secondary_router("glm_router_T1", w.spec, 1, 200, 10))

@@ -608,7 +608,9 @@ COLI_DEV coli_bf16x8 as_bf16x8(const uint32_t p[4]) {
   return __builtin_bit_cast(coli_bf16x8, v);
 }
 
-constexpr int kMfmaKw = 512;  // k per wavefront (I / 4)
+// k per wavefront: I / 4 (I = 512, 1024 or 2048)
+template <int KW>
+constexpr bool mfma_kw_ok() { return KW == 128 || KW == 256 || KW == 512; }
 
 // Activation quad q (0..3 high half, 4..7 low half) of chunk c of A row a:
 // from the LDS copy of the token's h row (one token) or from h itself (A row
@@ -622,17 +624,20 @@ COLI_DEV uint4 mfma_a_quad(const uint4 *hsm, const float *__restrict__ h_in, int
   return reinterpret_cast<const uint4 *>(h_in + (int64_t)(pos0 + tok) * I + 32 * c)[q];
 }
 
-template <class C>
-constexpr int mfma_tpw() { return C::Q == 1 ? 2 : 1; }  // 16-row tiles per wavefront
+// 16-row tiles per wavefront: about eight 16-byte weight loads per lane
+// (two tiles of 512 k with int4 codes, four of 256 or 128 k; half with int8)
+template <class C, int KW>
+constexpr int mfma_tpw() { return (KW == 512 ? 2 : 4) / C::Q; }
 
-template <int NA, int MODE, class C>
+template <int NA, int MODE, class C, int KW>
 __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
     Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
     float *__restrict__ o_out) {
+  static_assert(mfma_kw_ok<KW>(), "k per wavefront");
   constexpr bool ONE = MODE == kAll1 || MODE == kSingles;  // one token in the slot
-  constexpr int TPW = mfma_tpw<C>();
-  constexpr int NCHK = 64;                     // chunks of an h row (I = 2048)
-  constexpr int CPW = kMfmaKw / 32;            // chunks per wavefront (16)
+  constexpr int TPW = mfma_tpw<C, KW>();
+  constexpr int NCHK = KW / 8;                 // chunks of an h row (I / 32)
+  constexpr int CPW = KW / 32;                 // chunks per wavefront
   constexpr int LPT = CPW * C::Q / 4;          // 16-byte loads per tile (int8: 8, else 4)
   constexpr int CPL = 4 / C::Q;                // chunks per load
   constexpr int CPS = C::kChunksPerScale;      // chunks sharing one scale
@@ -656,13 +661,19 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
   if (MODE == kMulti && sl.cnt == 1) return;
   const int cnt = ONE ? 1 : sl.cnt;
   const int m0 = (blockIdx.x % wg_per_slot) * (16 * TPW);
-  const int k0 = wv * kMfmaKw;
-  // one token: the h row (8 KB), requested before the weights
-  uint4 hp0 = make_uint4(0u, 0u, 0u, 0u), hp1 = hp0;
+  const int k0 = wv * KW;
+  // one token: the h row (I / 4 quads: 2 per thread at I = 2048), requested
+  // before the weights
+  constexpr int HQ = KW;  // 16-byte quads of an h row (hi + lo bf16 pairs)
+  constexpr int HPT = (HQ + kThreads - 1) / kThreads;
+  uint4 hp[HPT];
   if (ONE) {
     const uint4 *src = reinterpret_cast<const uint4 *>(h_in + (int64_t)sl.pos0 * I);
-    hp0 = src[threadIdx.x];
-    hp1 = src[threadIdx.x + kThreads];
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      hp[i] = q < HQ ? src[q] : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   // weights: tile t, load j holds bytes 64 j + 16 g of row m0 + 16 t + rr
   // within the wavefront's k range
@@ -675,7 +686,8 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < LPT; ++j)
       w[t][j] = *reinterpret_cast<const uint4 *>(qd + (int64_t)16 * t * row_bytes + 64 * j);
-  // the scales of those 16 chunks of the row: 16 bytes (8 fp16, or 16 E8M0)
+  // the scales of the wavefront's CPW chunks of the row: KW / 32 bytes (one
+  // fp16 per two chunks, or one E8M0 per chunk), exactly what is needed
   const uint8_t *sdb = reinterpret_cast<const uint8_t *>(
       L.scales + (int64_t)sl.e * L.expert_scales + (int64_t)2 * I * H / 64);
   uint4 sc[TPW];
@@ -683,12 +695,21 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
   for (int t = 0; t < TPW; ++t) {
     const int64_t row = m0 + 16 * t + rr;
     const int64_t off = CPS == 2 ? 2 * (row * (I / 64) + k0 / 64) : row * (I / 32) + k0 / 32;
-    sc[t] = *reinterpret_cast<const uint4 *>(sdb + off);
+    if (KW == 512) {
+      sc[t] = *reinterpret_cast<const uint4 *>(sdb + off);
+    } else if (KW == 256) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(sdb + off);
+      sc[t] = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+      sc[t] = make_uint4(*reinterpret_cast<const uint32_t *>(sdb + off), 0u, 0u, 0u);
+    }
   }
   if (ONE) {
-    const int q0 = threadIdx.x, q1 = threadIdx.x + kThreads;
-    hsm[(q0 & 7) * NCHK + (q0 >> 3)] = hp0;
-    hsm[(q1 & 7) * NCHK + (q1 >> 3)] = hp1;
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      if (q < HQ) hsm[(q & 7) * NCHK + (q >> 3)] = hp[i];
+    }
     __syncthreads();
   }
   if (kHasBias) {
@@ -858,25 +879,35 @@ hipError_t down_shape(const Layer &L, const coli_moe_route_t &r, int T, const fl
   return hipGetLastError();
 }
 
-// I = 2048: the down GEMV on the matrix cores, NA operand tiles of 8 tokens
-template <class C>
+// I = 4 * KW (512, 1024, 2048): the down GEMV on the matrix cores, NA
+// operand tiles of 8 tokens
+template <class C, int KW>
 hipError_t down_mfma(const Layer &L, const coli_moe_route_t &r, int T, const float *h, float *o,
                      int nslots, hipStream_t s) {
-  const dim3 grid(nslots * (L.H / (16 * mfma_tpw<C>())));
+  const dim3 grid(nslots * (L.H / (16 * mfma_tpw<C, KW>())));
   if (T == 1) {
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kAll1, C>, grid, dim3(kThreads), 0, s, L, r,
-             T, h, o);
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kAll1, C, KW>, grid, dim3(kThreads), 0, s,
+             L, r, T, h, o);
+    return hipGetLastError();
+  }
+  if (!split_singles(L)) {  // small layers: one launch over every slot
+    if (T <= 8)
+      launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kAllN, C, KW>, grid, dim3(kThreads), 0, s,
+               L, r, T, h, o);
+    else
+      launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, kAllN, C, KW>, grid, dim3(kThreads), 0, s,
+               L, r, T, h, o);
     return hipGetLastError();
   }
   // most slots of a small batch hold one token: those run the one-token code
-  launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kSingles, C>, grid, dim3(kThreads), 0, s, L,
-           r, T, h, o);
+  launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kSingles, C, KW>, grid, dim3(kThreads), 0, s,
+           L, r, T, h, o);
   if (T <= 8)
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kMulti, C>, grid, dim3(kThreads), 0, s, L,
-             r, T, h, o);
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kMulti, C, KW>, grid, dim3(kThreads), 0, s,
+             L, r, T, h, o);
   else
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, kMulti, C>, grid, dim3(kThreads), 0, s, L,
-             r, T, h, o);
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, kMulti, C, KW>, grid, dim3(kThreads), 0, s,
+             L, r, T, h, o);
   return hipGetLastError();
 }
 
@@ -914,9 +945,9 @@ bool launch_stream(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     default: e = gateup_cpl<4, C>(L, r, x, T, h, nslots, s); break;
   }
   if (e == hipSuccess) {
-    if (lpr == 16) e = down_shape<16, 1, C>(L, r, T, h, o, nslots, s);
-    else if (lpr == 32) e = down_shape<32, 1, C>(L, r, T, h, o, nslots, s);
-    else if (cpl == 1) e = down_mfma<C>(L, r, T, h, o, nslots, s);
+    if (lpr == 16) e = down_mfma<C, 128>(L, r, T, h, o, nslots, s);
+    else if (lpr == 32) e = down_mfma<C, 256>(L, r, T, h, o, nslots, s);
+    else if (cpl == 1) e = down_mfma<C, 512>(L, r, T, h, o, nslots, s);
     else if (cpl == 2) e = down_shape<64, 2, C>(L, r, T, h, o, nslots, s);
     else if (cpl == 3) e = down_shape<64, 3, C>(L, r, T, h, o, nslots, s);
     else e = down_shape<64, 4, C>(L, r, T, h, o, nslots, s);
