@@ -161,6 +161,7 @@ def traced_kernels(fn, reps):
 
 TRAFFIC_PROFILE = os.path.join(_ROOT, "profiles", "decode_gateup_glm52_stack_traffic.md")
 KERNEL_SOURCES = ("int4_routed_expert_router_amd/csrc/decode_stream.hip",
+                  "int4_routed_expert_router_amd/csrc/codec.h",
                   "int4_routed_expert_router_amd/csrc/device_common.h",
                   "int4_routed_expert_router_amd/csrc/internal.h")
 
@@ -425,7 +426,7 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    kern = traced_kernels(lambda: step(0), reps=2)
+    kern = traced_kernels(lambda: step(0), reps=3)
     nbytes = union_bytes(spec, [lg], spec.top_k)
     ops = 2.0 * 3 * spec.hidden * spec.inter * T * (spec.top_k + spec.n_shared)
     gemm_us = sum(kern.get(k, {"avg_us": 0})["avg_us"] for k in ("gemm_gateup", "gemm_down"))
@@ -437,12 +438,26 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
            "gemm_int8_TOPS": round(ops / (gemm_us * 1e-6) / 1e12, 2) if gemm_us else None,
            "weight_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-           "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()}}
+           "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+           "kernels_us_from": "3 eager steps after the timed ones, each kernel's dispatch events"}
     if k32_ceiling:  # the measured rate of the instruction the GEMM issues
         out["measured_k32_TOPS"] = k32_ceiling
         out["frac_of_measured_k32"] = round(ops / (ms * 1e-3) / 1e12 / k32_ceiling, 4)
     if cpu:
         out["cpu_baseline"] = cpu_baseline_prefill(spec, Ls[0], lg, x, T)
+    return out
+
+
+def prefill_dense(steps, warmup):
+    """The prefill GEMMs above the ridge: a GLM-shaped layer (H 6144, I 2048)
+    with one routed expert (top-1) and the shared expert, so that both see
+    all 2048 tokens: 32 full 64-token tiles per expert, the shape of the
+    shared expert's GEMM in every prefill batch."""
+    import synth
+
+    spec = synth.LayerSpec(6144, 2048, 1, 1, 1, sigmoid=True, renorm=True)
+    out = secondary_prefill("glm_shape_dense_2experts_T2048", spec, 2048, 0.0, steps, warmup)
+    out["note"] = "routed expert 0 and the shared expert each take all 2048 tokens"
     return out
 
 
@@ -545,6 +560,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="main workload only")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the 2048-token GLM prefill workload (for profiling it)")
+    ap.add_argument("--prefill-dense-only", action="store_true",
+                    help="the GLM-shaped GEMMs with every one of 2048 tokens on each expert")
     ap.add_argument("--decode-t4-only", action="store_true",
                     help="only the GLM-shaped decode stack with 4 tokens (verify batch)")
     ap.add_argument("--convert-only", action="store_true",
@@ -581,6 +598,9 @@ def main():
         pw = synth.WORKLOADS["glm_prefill"]
         print(json.dumps(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
                                            args.steps, args.warmup, copies=1)), flush=True)
+        return
+    if args.prefill_dense_only:
+        print(json.dumps(prefill_dense(args.steps, args.warmup)), flush=True)
         return
     if args.decode_t4_only:
         w = synth.WORKLOADS["glm"]
@@ -656,6 +676,8 @@ def main():
                                            10, 2, layer=stack.layers[0], k32_ceiling=k32,
                                            cpu=not args.no_cpu))
         del stack
+        torch.cuda.empty_cache()
+        secondary.append(prefill_dense(10, 2))
         torch.cuda.empty_cache()
         secondary.append(secondary_router("glm_router_T1", w.spec, 1, 200, 10))
         secondary.append(secondary_router("glm_router_T2048", w.spec, 2048, 20, 3))

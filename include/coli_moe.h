@@ -112,11 +112,7 @@ enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
  * draft acceptance; tantan.ink post, section "我看到的几个坑") and list the
  * OLMoE container as int8 (ai-tools-nav review, model family table); they do
  * not give its scale granularity, read here as the same gs64.  int8 layers
- * run in coli_moe_forward_decode when the shape has the streaming path
- * (H a multiple of 2048 up to 8192; I in {512, 1024} or a multiple of 2048
- * up to 8192) and T <= 16, and in coli_moe_forward_prefill and
- * coli_moe_block_dots when H and I (the reduction length) are multiples of
- * 256; other calls return COLI_E_UNSUPPORTED.
+ * take every call and shape that int4 layers take.
  *
  * MXFP4 codes (weight_format = COLI_WEIGHTS_MXFP4): the pages list fp4
  * experts for Kimi K3 and DeepSeek V4 (ai-tools-nav review, model family
@@ -128,7 +124,7 @@ enum { COLI_ENTRY_ROUTE = 0, COLI_ENTRY_DECODE = 1, COLI_ENTRY_PREFILL = 2 };
  * One E8M0 byte per 32 weights takes the bytes of one fp16 per 64, so the
  * scale layout per expert and matrix is the same (gate at byte 0, up at
  * I*H/32, down at 2*I*H/32; expert e at byte e * 3*I*H/32).  Same calls and
- * shape limits as int8 codes.  On the integer path the codes enter the
+ * shapes as int4 codes.  On the integer path the codes enter the
  * int8 matrix cores as 2 * E2M1 (integers in [-12, 12], exact) with the
  * scale halved; coli_moe_block_dots returns the dots of those doubled codes.
  */

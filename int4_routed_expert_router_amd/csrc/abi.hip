@@ -87,11 +87,6 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
   if ((rc = check_route(route))) return rc;
   if ((rc = check_tokens(*L, T, entry == COLI_ENTRY_DECODE ? kMaxDecodeT : kMaxT))) return rc;
   if (entry == COLI_ENTRY_DECODE && L->I > kMaxDecodeInter) return COLI_E_UNSUPPORTED;
-  // int8 and MXFP4 codes: decode on the streaming path; prefill with H, I
-  // multiples of 256 (the four-step matrix-core kernel)
-  if ((L->w8 || L->f4) && (entry == COLI_ENTRY_DECODE ? !decode_stream_supported(*L, T)
-                                                      : (L->H % 256 || L->I % 256)))
-    return COLI_E_UNSUPPORTED;
   if (!x || !y) return COLI_E_INVALID;
   if (y_dtype != COLI_OUT_BF16 && y_dtype != COLI_OUT_F32) return COLI_E_INVALID;
   if (!aligned(x, 16) || !aligned(y, 16)) return COLI_E_ALIGN;
@@ -296,7 +291,6 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t m
   if (expert < 0 || expert >= L.E + L.S || matrix < 0 || matrix > 2) return COLI_E_INVALID;
   if (T < 1 || T > 4096 || !q_act || !dots) return COLI_E_INVALID;
   if (!aligned(q_act, 16) || !aligned(dots, 16)) return COLI_E_ALIGN;
-  if ((L.w8 || L.f4) && (matrix == 2 ? L.I : L.H) % 256) return COLI_E_UNSUPPORTED;
   return launch_block_dots(L, expert, matrix, q_act, T, dots, reinterpret_cast<hipStream_t>(stream));
 }
 

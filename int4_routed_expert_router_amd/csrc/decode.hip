@@ -21,6 +21,7 @@
 // A token's output depends only on its own rows, so results are independent
 // of the other tokens in the batch, and there are no atomics.
 #include "device_common.h"
+#include "codec.h"
 #include "internal.h"
 
 namespace coli {
@@ -72,7 +73,7 @@ __device__ bool load_slot(const coli_moe_route_t &r, int slot, int T, int k, int
 
 // LPR lanes share one row; CPL = chunks per lane (0: runtime loop);
 // TG tokens per pass.  Rows per work item: 4 waves * 2 * (64/LPR) * 2.
-template <int LPR, int CPL, int TG>
+template <int LPR, int CPL, int TG, class C>
 __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_route_t r,
                                                           const uint16_t *__restrict__ x,
                                                           int T, float *__restrict__ h_out,
@@ -97,9 +98,11 @@ __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_rout
     __syncthreads();
     const int e = si.expert, ntok = si.ntok;
     const uint8_t *qg = L.q4 + (int64_t)e * L.expert_bytes;
-    const uint8_t *qu = qg + (int64_t)I * H / 2;
-    const uint16_t *sg = L.scales + (int64_t)e * L.expert_scales;
-    const uint16_t *su = sg + (int64_t)I * H / 64;
+    const uint8_t *qu = qg + C::bytes((int64_t)I * H);
+    const uint8_t *sg = reinterpret_cast<const uint8_t *>(L.scales + (int64_t)e * L.expert_scales);
+    const uint8_t *su =
+        reinterpret_cast<const uint8_t *>(L.scales + (int64_t)e * L.expert_scales + (int64_t)I * H / 64);
+    const int64_t rowb = C::bytes(H);  // bytes per weight row
     const int row_base = rb * ROWS_ITEM + wid * ROWS_WAVE;
 
     for (int t0 = 0; t0 < ntok; t0 += TG) {
@@ -116,10 +119,10 @@ __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_rout
           for (int dw = 0; dw < 4; ++dw) {
             const uint4 v = src[dw];
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-            x8_to_pairs(d, &p[4 * dw]);
+            C::pairs(d, &p[4 * dw]);
             xs[(tt * 4 + dw) * NCH + c] = make_uint4(p[4 * dw], p[4 * dw + 1], p[4 * dw + 2], p[4 * dw + 3]);
           }
-          nb = chunk_bias(p);
+          nb = codec_bias<C>(p);
         }
         corr[tt * NCH + c] = -nb;
       }
@@ -137,19 +140,28 @@ __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_rout
           for (int ii = i; ii < cpl; ii += (CPL ? CPL : 1)) {
             const int c = lc + LPR * ii;
             if (c >= NCH) break;
-            uint4 wga = make_uint4(0, 0, 0, 0), wua = wga, wgb = wga, wub = wga;
+            uint4 wga[C::Q], wua[C::Q], wgb[C::Q], wub[C::Q];
+#pragma unroll
+            for (int q = 0; q < C::Q; ++q)
+              wga[q] = wua[q] = wgb[q] = wub[q] = make_uint4(0, 0, 0, 0);
             float sga = 0.f, sua = 0.f, sgb = 0.f, sub = 0.f;
             if (va) {
-              wga = *reinterpret_cast<const uint4 *>(qg + (int64_t)ra * (H / 2) + 16 * c);
-              wua = *reinterpret_cast<const uint4 *>(qu + (int64_t)ra * (H / 2) + 16 * c);
-              sga = f16_to_f32(sg[(int64_t)ra * (H / 64) + c / 2]);
-              sua = f16_to_f32(su[(int64_t)ra * (H / 64) + c / 2]);
+#pragma unroll
+              for (int q = 0; q < C::Q; ++q) {
+                wga[q] = *reinterpret_cast<const uint4 *>(qg + ra * rowb + 16 * (C::Q * c + q));
+                wua[q] = *reinterpret_cast<const uint4 *>(qu + ra * rowb + 16 * (C::Q * c + q));
+              }
+              sga = C::scale(C::scale_raw(sg, ra, H, c));
+              sua = C::scale(C::scale_raw(su, ra, H, c));
             }
             if (vb) {
-              wgb = *reinterpret_cast<const uint4 *>(qg + (int64_t)rb2 * (H / 2) + 16 * c);
-              wub = *reinterpret_cast<const uint4 *>(qu + (int64_t)rb2 * (H / 2) + 16 * c);
-              sgb = f16_to_f32(sg[(int64_t)rb2 * (H / 64) + c / 2]);
-              sub = f16_to_f32(su[(int64_t)rb2 * (H / 64) + c / 2]);
+#pragma unroll
+              for (int q = 0; q < C::Q; ++q) {
+                wgb[q] = *reinterpret_cast<const uint4 *>(qg + rb2 * rowb + 16 * (C::Q * c + q));
+                wub[q] = *reinterpret_cast<const uint4 *>(qu + rb2 * rowb + 16 * (C::Q * c + q));
+              }
+              sgb = C::scale(C::scale_raw(sg, rb2, H, c));
+              sub = C::scale(C::scale_raw(su, rb2, H, c));
             }
             float aga[TG], aua[TG], agb[TG], aub[TG];
 #pragma unroll
@@ -157,30 +169,22 @@ __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_rout
               const float cr = -corr[tt * NCH + c];
               aga[tt] = aua[tt] = agb[tt] = aub[tt] = cr;
             }
-            const uint32_t wgav[4] = {wga.x, wga.y, wga.z, wga.w};
-            const uint32_t wuav[4] = {wua.x, wua.y, wua.z, wua.w};
-            const uint32_t wgbv[4] = {wgb.x, wgb.y, wgb.z, wgb.w};
-            const uint32_t wubv[4] = {wub.x, wub.y, wub.z, wub.w};
 #pragma unroll
-            for (int dw = 0; dw < 4; ++dw) {
-              uint32_t pg[4], pu[4], qgb[4], qub[4];
-              nib8_to_bf16x4(wgav[dw], pg[0], pg[1], pg[2], pg[3]);
-              nib8_to_bf16x4(wuav[dw], pu[0], pu[1], pu[2], pu[3]);
-              nib8_to_bf16x4(wgbv[dw], qgb[0], qgb[1], qgb[2], qgb[3]);
-              nib8_to_bf16x4(wubv[dw], qub[0], qub[1], qub[2], qub[3]);
+            for (int tt = 0; tt < TG; ++tt) {
+              if (TG > 1 && tt >= nt) break;
+              uint32_t xp[16];
 #pragma unroll
-              for (int tt = 0; tt < TG; ++tt) {
-                if (TG > 1 && tt >= nt) break;
+              for (int dw = 0; dw < 4; ++dw) {
                 const uint4 xv = xs[(tt * 4 + dw) * NCH + c];
-                const uint32_t xp[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  aga[tt] = dot2_bf16(pg[q], xp[q], aga[tt]);
-                  aua[tt] = dot2_bf16(pu[q], xp[q], aua[tt]);
-                  agb[tt] = dot2_bf16(qgb[q], xp[q], agb[tt]);
-                  aub[tt] = dot2_bf16(qub[q], xp[q], aub[tt]);
-                }
+                xp[4 * dw] = xv.x;
+                xp[4 * dw + 1] = xv.y;
+                xp[4 * dw + 2] = xv.z;
+                xp[4 * dw + 3] = xv.w;
               }
+              aga[tt] = C::template dot<false>(wga, xp, nullptr, aga[tt]);
+              aua[tt] = C::template dot<false>(wua, xp, nullptr, aua[tt]);
+              agb[tt] = C::template dot<false>(wgb, xp, nullptr, agb[tt]);
+              aub[tt] = C::template dot<false>(wub, xp, nullptr, aub[tt]);
             }
 #pragma unroll
             for (int tt = 0; tt < TG; ++tt) {
@@ -209,7 +213,7 @@ __global__ void __launch_bounds__(kThreads) gateup_kernel(Layer L, coli_moe_rout
 
 // ------------------------------------------------------------------ down
 
-template <int LPR, int CPL, int TG>
+template <int LPR, int CPL, int TG, class C>
 __global__ void __launch_bounds__(kThreads) down_kernel(Layer L, coli_moe_route_t r, int T,
                                                         const float *__restrict__ h_in,
                                                         float *__restrict__ o_out, int nrb,
@@ -233,8 +237,10 @@ __global__ void __launch_bounds__(kThreads) down_kernel(Layer L, coli_moe_route_
     if (!load_slot(r, slot, T, L.k, L.E, L.S, si)) continue;
     __syncthreads();
     const int e = si.expert, ntok = si.ntok;
-    const uint8_t *qd = L.q4 + (int64_t)e * L.expert_bytes + (int64_t)I * H;
-    const uint16_t *sd = L.scales + (int64_t)e * L.expert_scales + (int64_t)2 * I * H / 64;
+    const uint8_t *qd = L.q4 + (int64_t)e * L.expert_bytes + C::bytes((int64_t)2 * I * H);
+    const uint8_t *sd = reinterpret_cast<const uint8_t *>(L.scales + (int64_t)e * L.expert_scales +
+                                                          (int64_t)2 * I * H / 64);
+    const int64_t rowb = C::bytes(I);
     const int row_base = rb * ROWS_ITEM + wid * ROWS_WAVE;
 
     for (int t0 = 0; t0 < ntok; t0 += TG) {
@@ -259,12 +265,12 @@ __global__ void __launch_bounds__(kThreads) down_kernel(Layer L, coli_moe_route_
               hi[q] = h0 | (h1 << 16);
               lo[q] = l0 | (l1 << 16);
             }
-            x8_to_pairs(hi, &ph[4 * dw]);
-            x8_to_pairs(lo, &pl[4 * dw]);
+            C::pairs(hi, &ph[4 * dw]);
+            C::pairs(lo, &pl[4 * dw]);
             xs[(tt * 8 + dw) * NCH + c] = make_uint4(ph[4 * dw], ph[4 * dw + 1], ph[4 * dw + 2], ph[4 * dw + 3]);
             xs[(tt * 8 + 4 + dw) * NCH + c] = make_uint4(pl[4 * dw], pl[4 * dw + 1], pl[4 * dw + 2], pl[4 * dw + 3]);
           }
-          nb = chunk_bias2(ph, pl);
+          nb = codec_bias2<C>(ph, pl);
         }
         corr[tt * NCH + c] = -nb;
       }
@@ -282,41 +288,44 @@ __global__ void __launch_bounds__(kThreads) down_kernel(Layer L, coli_moe_route_
           for (int ii = i; ii < cpl; ii += (CPL ? CPL : 1)) {
             const int c = lc + LPR * ii;
             if (c >= NCH) break;
-            uint4 wa = make_uint4(0, 0, 0, 0), wb = wa;
+            uint4 wa[C::Q], wb[C::Q];
+#pragma unroll
+            for (int q = 0; q < C::Q; ++q) wa[q] = wb[q] = make_uint4(0, 0, 0, 0);
             float sa = 0.f, sb = 0.f;
             if (va) {
-              wa = *reinterpret_cast<const uint4 *>(qd + (int64_t)ma * (I / 2) + 16 * c);
-              sa = f16_to_f32(sd[(int64_t)ma * (I / 64) + c / 2]);
+#pragma unroll
+              for (int q = 0; q < C::Q; ++q)
+                wa[q] = *reinterpret_cast<const uint4 *>(qd + ma * rowb + 16 * (C::Q * c + q));
+              sa = C::scale(C::scale_raw(sd, ma, I, c));
             }
             if (vb) {
-              wb = *reinterpret_cast<const uint4 *>(qd + (int64_t)mb * (I / 2) + 16 * c);
-              sb = f16_to_f32(sd[(int64_t)mb * (I / 64) + c / 2]);
+#pragma unroll
+              for (int q = 0; q < C::Q; ++q)
+                wb[q] = *reinterpret_cast<const uint4 *>(qd + mb * rowb + 16 * (C::Q * c + q));
+              sb = C::scale(C::scale_raw(sd, mb, I, c));
             }
             float aa[TG], ab[TG];
 #pragma unroll
             for (int tt = 0; tt < TG; ++tt) aa[tt] = ab[tt] = -corr[tt * NCH + c];
-            const uint32_t wav[4] = {wa.x, wa.y, wa.z, wa.w};
-            const uint32_t wbv[4] = {wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-            for (int dw = 0; dw < 4; ++dw) {
-              uint32_t pa[4], pb[4];
-              nib8_to_bf16x4(wav[dw], pa[0], pa[1], pa[2], pa[3]);
-              nib8_to_bf16x4(wbv[dw], pb[0], pb[1], pb[2], pb[3]);
+            for (int tt = 0; tt < TG; ++tt) {
+              if (TG > 1 && tt >= nt) break;
+              uint32_t hp[16], lp[16];
 #pragma unroll
-              for (int tt = 0; tt < TG; ++tt) {
-                if (TG > 1 && tt >= nt) break;
+              for (int dw = 0; dw < 4; ++dw) {
                 const uint4 xh = xs[(tt * 8 + dw) * NCH + c];
                 const uint4 xl = xs[(tt * 8 + 4 + dw) * NCH + c];
-                const uint32_t hp[4] = {xh.x, xh.y, xh.z, xh.w};
-                const uint32_t lp[4] = {xl.x, xl.y, xl.z, xl.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  aa[tt] = dot2_bf16(pa[q], hp[q], aa[tt]);
-                  aa[tt] = dot2_bf16(pa[q], lp[q], aa[tt]);
-                  ab[tt] = dot2_bf16(pb[q], hp[q], ab[tt]);
-                  ab[tt] = dot2_bf16(pb[q], lp[q], ab[tt]);
-                }
+                hp[4 * dw] = xh.x;
+                hp[4 * dw + 1] = xh.y;
+                hp[4 * dw + 2] = xh.z;
+                hp[4 * dw + 3] = xh.w;
+                lp[4 * dw] = xl.x;
+                lp[4 * dw + 1] = xl.y;
+                lp[4 * dw + 2] = xl.z;
+                lp[4 * dw + 3] = xl.w;
               }
+              aa[tt] = C::template dot<true>(wa, hp, lp, aa[tt]);
+              ab[tt] = C::template dot<true>(wb, hp, lp, ab[tt]);
             }
 #pragma unroll
             for (int tt = 0; tt < TG; ++tt) {
@@ -415,12 +424,12 @@ Shape pick_shape(int K) {
 
 int rows_per_item(int lpr) { return 4 * 2 * (64 / lpr) * 2; }
 
-template <int TG>
+template <int TG, class C>
 hipError_t launch_gateup(Shape sh, dim3 grid, size_t lds, hipStream_t s, const Layer &L,
                          const coli_moe_route_t &r, const uint16_t *x, int T, float *h,
                          int nrb, int items) {
 #define COLI_GU(LPR, CPL)                                                                \
-  launch_k(COLI_K_DECODE_GATEUP, gateup_kernel<LPR, CPL, TG>, grid, dim3(kThreads), lds, s, L, \
+  launch_k(COLI_K_DECODE_GATEUP, gateup_kernel<LPR, CPL, TG, C>, grid, dim3(kThreads), lds, s, L, \
            r, x, T, h, nrb, items)
   switch (sh.lpr * 10 + sh.cpl) {
     case 81: COLI_GU(8, 1); break;
@@ -436,12 +445,12 @@ hipError_t launch_gateup(Shape sh, dim3 grid, size_t lds, hipStream_t s, const L
   return hipGetLastError();
 }
 
-template <int TG>
+template <int TG, class C>
 hipError_t launch_down(Shape sh, dim3 grid, size_t lds, hipStream_t s, const Layer &L,
                        const coli_moe_route_t &r, int T, const float *h, float *o, int nrb,
                        int items) {
 #define COLI_DN(LPR, CPL)                                                                 \
-  launch_k(COLI_K_DECODE_DOWN, down_kernel<LPR, CPL, TG>, grid, dim3(kThreads), lds, s, L, r, \
+  launch_k(COLI_K_DECODE_DOWN, down_kernel<LPR, CPL, TG, C>, grid, dim3(kThreads), lds, s, L, r, \
            T, h, o, nrb, items)
   switch (sh.lpr * 10 + sh.cpl) {
     case 81: COLI_DN(8, 1); break;
@@ -462,6 +471,36 @@ int pick_tg(int T, int K, int bytes_per_value) {
   if (T == 1) return 1;
   const size_t per_tok = (size_t)K * bytes_per_value + (size_t)(K / 32) * 4;
   return per_tok * 4 <= 60 * 1024 ? 4 : 1;
+}
+
+// Gate/up and down over (union slot, row block) work items, any shape and
+// up to 64 tokens, for weight codec C.
+template <class C>
+hipError_t decode_general(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                          float *h, float *o, int nslots, hipStream_t s) {
+  hipError_t err;
+  {  // gate / up
+    const Shape sh = pick_shape(L.H);
+    const int nrb = (L.I + rows_per_item(sh.lpr) - 1) / rows_per_item(sh.lpr);
+    const int items = nslots * nrb;
+    const dim3 grid(items < 8192 ? items : 8192);
+    const int tg = pick_tg(T, L.H, 2);
+    const size_t lds = (size_t)tg * (L.H / 32) * (64 + 4);
+    err = tg == 1 ? launch_gateup<1, C>(sh, grid, lds, s, L, r, x, T, h, nrb, items)
+                  : launch_gateup<4, C>(sh, grid, lds, s, L, r, x, T, h, nrb, items);
+    if (err != hipSuccess) return err;
+  }
+  {  // down
+    const Shape sh = pick_shape(L.I);
+    const int nrb = (L.H + rows_per_item(sh.lpr) - 1) / rows_per_item(sh.lpr);
+    const int items = nslots * nrb;
+    const dim3 grid(items < 8192 ? items : 8192);
+    const int tg = pick_tg(T, L.I, 4);
+    const size_t lds = (size_t)tg * (L.I / 32) * (128 + 4);
+    err = tg == 1 ? launch_down<1, C>(sh, grid, lds, s, L, r, T, h, o, nrb, items)
+                  : launch_down<4, C>(sh, grid, lds, s, L, r, T, h, o, nrb, items);
+  }
+  return err;
 }
 
 }  // namespace
@@ -492,28 +531,10 @@ int launch_decode(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, 
     return hip_status(hipGetLastError());
   }
 
-  {  // gate / up
-    const Shape sh = pick_shape(L.H);
-    const int nrb = (L.I + rows_per_item(sh.lpr) - 1) / rows_per_item(sh.lpr);
-    const int items = nslots * nrb;
-    const dim3 grid(items < 8192 ? items : 8192);
-    const int tg = pick_tg(T, L.H, 2);
-    const size_t lds = (size_t)tg * (L.H / 32) * (64 + 4);
-    err = tg == 1 ? launch_gateup<1>(sh, grid, lds, s, L, r, x, T, h, nrb, items)
-                  : launch_gateup<4>(sh, grid, lds, s, L, r, x, T, h, nrb, items);
-    if (err != hipSuccess) return COLI_E_HIP;
-  }
-  {  // down
-    const Shape sh = pick_shape(L.I);
-    const int nrb = (L.H + rows_per_item(sh.lpr) - 1) / rows_per_item(sh.lpr);
-    const int items = nslots * nrb;
-    const dim3 grid(items < 8192 ? items : 8192);
-    const int tg = pick_tg(T, L.I, 4);
-    const size_t lds = (size_t)tg * (L.I / 32) * (128 + 4);
-    err = tg == 1 ? launch_down<1>(sh, grid, lds, s, L, r, T, h, o, nrb, items)
-                  : launch_down<4>(sh, grid, lds, s, L, r, T, h, o, nrb, items);
-    if (err != hipSuccess) return COLI_E_HIP;
-  }
+  err = L.f4 ? decode_general<CodecF4>(L, r, x, T, h, o, nslots, s)
+      : L.w8  ? decode_general<CodecI8>(L, r, x, T, h, o, nslots, s)
+              : decode_general<CodecI4>(L, r, x, T, h, o, nslots, s);
+  if (err != hipSuccess) return COLI_E_HIP;
   launch_combine(o, r, T, L.H, L.k, L.S, y, y_dtype, s);
   err = hipGetLastError();
   return hip_status(err);

@@ -180,17 +180,48 @@ __global__ void __launch_bounds__(1024) plan_kernel(coli_moe_route_t r, int T, i
 
 // ---------------------------------------------------------------- GEMM
 
+// weight code formats: int4 nibbles, int8 bytes, MXFP4 E2M1 nibbles
+constexpr int kFmtI4 = 0, kFmtI8 = 1, kFmtF4 = 2;
+
+// MXFP4: 8 E2M1 codes (a dword, low nibble first) -> 8 int8 2 * E2M1 in k
+// order, as two dwords.  Magnitudes index byte tables of 2|v| and -2|v|
+// (v_perm), and each byte takes the negative entry where its code's sign bit
+// is set: v_perm selectors 8-11 replicate bits 15 / 31 of its operands, so
+// shifted copies of the codes give 0xff per negative code.
+constexpr uint32_t kF4PosLo = 0x03020100u, kF4PosHi = 0x0C080604u;  // 0 1 2 3 | 4 6 8 12
+constexpr uint32_t kF4NegLo = 0xFDFEFF00u, kF4NegHi = 0xF4F8FAFCu;  // negated
+COLI_DEV void fp4x8_to_i8(uint32_t w, uint32_t &k0123, uint32_t &k4567) {
+  const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;  // even / odd k
+  // sign masks: even codes' sign bits 3, 11, 19, 27; odd codes' 7, 15, 23, 31
+  const uint32_t se = __builtin_amdgcn_perm(w << 4, w << 12, 0x0B090A08u);
+  const uint32_t so = __builtin_amdgcn_perm(w, w << 8, 0x0B090A08u);
+  // v_bitop3 truth table 0xCA is a ? b : c, bit by bit
+  const uint32_t ve = __builtin_amdgcn_bitop3_b32(
+      se, __builtin_amdgcn_perm(kF4NegHi, kF4NegLo, me), __builtin_amdgcn_perm(kF4PosHi, kF4PosLo, me),
+      0xCAu);  // se ? neg : pos
+  const uint32_t vo = __builtin_amdgcn_bitop3_b32(
+      so, __builtin_amdgcn_perm(kF4NegHi, kF4NegLo, mo), __builtin_amdgcn_perm(kF4PosHi, kF4PosLo, mo),
+      0xCAu);
+  // interleave: k0 k1 k2 k3 = ve.b0 vo.b0 ve.b1 vo.b1, k4..k7 = bytes 2, 3
+  k0123 = __builtin_amdgcn_perm(vo, ve, 0x05010400u);
+  k4567 = __builtin_amdgcn_perm(vo, ve, 0x07030602u);
+}
+
+
 // LDS stage: operands already in matrix-core lane order.  Each 16-row x
 // 32-deep operand tile is 64 lanes x 8 bytes; consecutive tiles are kPad
 // entries apart (64 + 16), which puts the two 32-blocks of a row tile (and
 // of a token tile) in opposite halves of the 256-byte bank window, so the
 // unpacking writes below hit distinct banks within each half-wavefront.
 constexpr int kPad = 80;
+// NB weight scales per row and step: 1 (a 64-weight group) or 2 (MXFP4,
+// one per 32-block).
+template <int NB>
 struct Stage {
-  uint2 w[BR / 16][2][kPad];  // [row tile][32-block][lane] 8 int8 (x16) weights
+  uint2 w[BR / 16][2][kPad];  // [row tile][32-block][lane] 8 int8 weights (int4: x16)
   uint2 a[BM / 16][2][kPad];  // [token tile][32-block][lane] 8 int8 activations
-  float sw[BR];               // weight group scale of each row (0 on padding steps)
-  float4 sa[BM];              // per token: d0/16, -M*d0/16, d1/16, -M*d1/16
+  float sw[NB][BR];           // weight scales of each row (0 on padding steps)
+  float4 sa[BM];              // per token: d0*f, -M*d0*f, d1*f, -M*d1*f (f: 1/16 for int4)
 };
 
 struct GemmArgs {
@@ -240,14 +271,18 @@ struct Src {
   int s_next;  // offset of the second scale
 };
 
+template <int WF>
 struct Prefetch {
-  uint4 w;      // 16 bytes of nibbles (32 values, one 32-block)
-  uint4 a;      // 16 bytes of int8 activations
-  uint32_t s;   // two fp16 scales, first in the low half
+  uint4 w[WF == kFmtI8 ? 2 : 1];  // one 32-block of codes: 16 bytes of nibbles, or 32 of int8
+  uint4 a;                        // 16 bytes of int8 activations
+  uint32_t s;  // two 16-bit scale units, first in the low half (MXFP4: two E8M0 bytes in one)
 };
 
-COLI_DEV void load_step(const Src &src, int ks, Prefetch &p) {
-  p.w = *reinterpret_cast<const uint4 *>(src.w + ks * (BK / 2));
+template <int WF>
+COLI_DEV void load_step(const Src &src, int ks, Prefetch<WF> &p) {
+#pragma unroll
+  for (int h = 0; h < (WF == kFmtI8 ? 2 : 1); ++h)
+    p.w[h] = *reinterpret_cast<const uint4 *>(src.w + ks * (WF == kFmtI8 ? BK : BK / 2) + 16 * h);
   p.a = *reinterpret_cast<const uint4 *>(src.a + ks * BK);
   const uint16_t *s = src.s + ks * src.s_step;
   p.s = (uint32_t)s[0] | ((uint32_t)s[src.s_next] << 16);
@@ -255,19 +290,38 @@ COLI_DEV void load_step(const Src &src, int ks, Prefetch &p) {
 
 // Registers -> LDS for one step.  `live` is false on the padding steps past
 // the end of K: their weight scales become 0, so they add exactly nothing.
-template <int MODE>
-COLI_DEV void store_step(const Prefetch &p, Stage &st, int wid, bool live) {
+// 2^(E - 128) of an E8M0 byte: the MXFP4 scale halved for the doubled codes
+COLI_DEV float e8m0_half(uint32_t E) {
+  return __uint_as_float(E > 1 ? (E - 1) << 23 : (0x00400000u >> (1 - E)));
+}
+
+template <int MODE, int WF>
+COLI_DEV void store_step(const Prefetch<WF> &p, Stage<WF == kFmtF4 ? 2 : 1> &st, int wid,
+                         bool live) {
   const int t = threadIdx.x;
-  {  // 32 nibbles -> 32 int8 (x16), natural k order, into 4 lanes' slots
+  {  // 32 codes -> 32 int8, natural k order, into 4 lanes' slots
     const int rt = t >> 5, blk = (t >> 4) & 1, rr = t & 15;
-    const uint32_t w[4] = {p.w.x, p.w.y, p.w.z, p.w.w};
+    if (WF == kFmtI8) {  // as they are: 8 bytes per lane
+      const uint4 v0 = p.w[0], v1 = p.w[WF == kFmtI8 ? 1 : 0];
+      st.w[rt][blk][rr] = make_uint2(v0.x, v0.y);
+      st.w[rt][blk][rr + 16] = make_uint2(v0.z, v0.w);
+      st.w[rt][blk][rr + 32] = make_uint2(v1.x, v1.y);
+      st.w[rt][blk][rr + 48] = make_uint2(v1.z, v1.w);
+    } else {
+      const uint32_t w[4] = {p.w[0].x, p.w[0].y, p.w[0].z, p.w[0].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t even = (w[i] << 4) & 0xf0f0f0f0u;  // k 0,2,4,6 (x16)
-      const uint32_t odd = w[i] & 0xf0f0f0f0u;          // k 1,3,5,7 (x16)
-      const uint32_t lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);
-      const uint32_t hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);
-      st.w[rt][blk][rr + 16 * i] = make_uint2(lo, hi);
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo, hi;
+        if (WF == kFmtF4) {
+          fp4x8_to_i8(w[i], lo, hi);  // 2 * E2M1
+        } else {
+          const uint32_t even = (w[i] << 4) & 0xf0f0f0f0u;  // k 0,2,4,6 (x16)
+          const uint32_t odd = w[i] & 0xf0f0f0f0u;          // k 1,3,5,7 (x16)
+          lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);
+          hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);
+        }
+        st.w[rt][blk][rr + 16 * i] = make_uint2(lo, hi);
+      }
     }
   }
   {  // activations: token tile wid, k [16*qq, 16*qq+16) of the step
@@ -277,10 +331,17 @@ COLI_DEV void store_step(const Prefetch &p, Stage &st, int wid, bool live) {
   }
   if (MODE == kDots) return;
   if (wid < 2) {
-    st.sw[t] = live ? f16_to_f32((uint16_t)p.s) : 0.0f;
+    if (WF == kFmtF4) {  // the step's two E8M0 bytes, block 0 in the low byte
+      st.sw[0][t] = live ? e8m0_half(p.s & 0xffu) : 0.0f;
+      st.sw[WF == kFmtF4 ? 1 : 0][t] = live ? e8m0_half((p.s >> 8) & 0xffu) : 0.0f;
+    } else {
+      st.sw[0][t] = live ? f16_to_f32((uint16_t)p.s) : 0.0f;
+    }
   } else if (wid == 2) {
-    const float d0 = f16_to_f32((uint16_t)p.s) * 0.0625f;
-    const float d1 = f16_to_f32((uint16_t)(p.s >> 16)) * 0.0625f;
+    // int4 codes sit in the stage x16: their activation scales carry 1/16
+    constexpr float f = WF == kFmtI4 ? 0.0625f : 1.0f;
+    const float d0 = f16_to_f32((uint16_t)p.s) * f;
+    const float d1 = f16_to_f32((uint16_t)(p.s >> 16)) * f;
     st.sa[t - BR] = make_float4(d0, -kMagicF * d0, d1, -kMagicF * d1);
   }
 }
@@ -427,14 +488,15 @@ COLI_DEV void epilogue(const float (&acc)[8][4], const GemmArgs &g, const Item &
   }
 }
 
-template <int MODE>
+template <int MODE, int WF>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
             const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
             int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
             int8_t *__restrict__ qh_out, uint16_t *__restrict__ dh_out,
             float *__restrict__ o_out, int32_t *__restrict__ dots_out) {
-  __shared__ Stage st[2];
+  constexpr int NB = WF == kFmtF4 ? 2 : 1;
+  __shared__ Stage<NB> st[2];
   __shared__ int rowid[BM];
   __shared__ int outrow[BM];
   const int lane = threadIdx.x & 63;
@@ -465,7 +527,7 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
       const int t = threadIdx.x;
       const uint16_t *s_row;
       weight_row<MODE>(ge, n0, 16 * (t >> 5) + (t & 15), src.w, s_row);
-      src.w += 16 * ((t >> 4) & 1);
+      src.w += (WF == kFmtI8 ? 32 : 16) * ((t >> 4) & 1);
       const int m = 16 * wid + (t & 15);
       const int qq = 2 * ((t >> 4) & 1) + ((t >> 5) & 1);
       src.a = ge.act + (int64_t)rowid[m] * ge.K + 16 * qq;
@@ -493,7 +555,7 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
     // product, one rounding) and acc += s_w * that.  Folding both blocks'
     // offsets into one constant would save an FMA but leaves the sum
     // rounded at the offset's magnitude (~1.3e7 * d), about 500x coarser.
-    auto step = [&](const Stage &cur, int ks) {
+    auto step = [&](const Stage<NB> &cur, int ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         coli_i32x4 d[8];
@@ -520,7 +582,7 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
                 const int n = n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4) + i;
                 if (n >= g.rows) continue;
                 dots_out[((int64_t)(row0 + m) * g.rows + n) * (g.K / 32) + 2 * ks + blk] =
-                    (d[a * 2 + ms][i] - (int)kMagic) >> 4;
+                    (d[a * 2 + ms][i] - (int)kMagic) >> (WF == kFmtI4 ? 4 : 0);
               }
             }
         } else {
@@ -531,7 +593,7 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
               const float4 sw = *reinterpret_cast<const float4 *>(
-                  &cur.sw[16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
+                  &cur.sw[NB == 2 ? blk : 0][16 * wave_row_tile<MODE>(wn, a) + 4 * (lane >> 4)]);
               const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
 #pragma unroll
               for (int i = 0; i < 4; ++i)
@@ -555,18 +617,18 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
     // ks computes on stage ks & 1, refills the ring slot it freed with step
     // ks + kDepth (clamped to the last step, so every load is in bounds and
     // unconditional), and unpacks step ks + 1 into the other stage.
-    Prefetch pf[kDepth];
+    Prefetch<WF> pf[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) load_step(src, min(i, nsteps - 1), pf[i]);
-    store_step<MODE>(pf[0], st[0], wid, true);
+    for (int i = 0; i < kDepth; ++i) load_step<WF>(src, min(i, nsteps - 1), pf[i]);
+    store_step<MODE, WF>(pf[0], st[0], wid, true);
     __syncthreads();
     for (int ks0 = 0; ks0 < nsteps_pad; ks0 += kDepth) {
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
         const int ks = ks0 + u;
-        load_step(src, min(ks + kDepth, nsteps - 1), pf[u]);
+        load_step<WF>(src, min(ks + kDepth, nsteps - 1), pf[u]);
         step(st[u & 1], ks);
-        store_step<MODE>(pf[(u + 1) % kDepth], st[(u + 1) & 1], wid, ks + 1 < nsteps);
+        store_step<MODE, WF>(pf[(u + 1) % kDepth], st[(u + 1) & 1], wid, ks + 1 < nsteps);
         __syncthreads();
       }
     }
@@ -587,8 +649,6 @@ gemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
 // loads is in flight while the previous group is computed; two barriers per
 // group.
 constexpr int kGroup = 4;   // K steps per LDS stage
-// weight code formats of the four-step kernel
-constexpr int kFmtI4 = 0, kFmtI8 = 1, kFmtF4 = 2;
 // NB: weight scales per step, 1 (a 64-weight group) or 2 (one per 32-block)
 template <int NB>
 struct Stage4 {
@@ -644,30 +704,6 @@ COLI_DEV void load_group(const Src4 &src, int gi, Group4<W8> &G) {
 // Registers -> LDS.  Within each half-wavefront the 8-byte writes land on
 // distinct banks: lane bits 0-1 pick consecutive entries and the (step,
 // block) pair moves the address by a multiple of 4 entries (mod 32).
-// MXFP4: 8 E2M1 codes (a dword, low nibble first) -> 8 int8 2 * E2M1 in k
-// order, as two dwords.  Magnitudes index byte tables of 2|v| and -2|v|
-// (v_perm), and each byte takes the negative entry where its code's sign bit
-// is set: v_perm selectors 8-11 replicate bits 15 / 31 of its operands, so
-// shifted copies of the codes give 0xff per negative code.
-constexpr uint32_t kF4PosLo = 0x03020100u, kF4PosHi = 0x0C080604u;  // 0 1 2 3 | 4 6 8 12
-constexpr uint32_t kF4NegLo = 0xFDFEFF00u, kF4NegHi = 0xF4F8FAFCu;  // negated
-COLI_DEV void fp4x8_to_i8(uint32_t w, uint32_t &k0123, uint32_t &k4567) {
-  const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;  // even / odd k
-  // sign masks: even codes' sign bits 3, 11, 19, 27; odd codes' 7, 15, 23, 31
-  const uint32_t se = __builtin_amdgcn_perm(w << 4, w << 12, 0x0B090A08u);
-  const uint32_t so = __builtin_amdgcn_perm(w, w << 8, 0x0B090A08u);
-  // v_bitop3 truth table 0xCA is a ? b : c, bit by bit
-  const uint32_t ve = __builtin_amdgcn_bitop3_b32(
-      se, __builtin_amdgcn_perm(kF4NegHi, kF4NegLo, me), __builtin_amdgcn_perm(kF4PosHi, kF4PosLo, me),
-      0xCAu);  // se ? neg : pos
-  const uint32_t vo = __builtin_amdgcn_bitop3_b32(
-      so, __builtin_amdgcn_perm(kF4NegHi, kF4NegLo, mo), __builtin_amdgcn_perm(kF4PosHi, kF4PosLo, mo),
-      0xCAu);
-  // interleave: k0 k1 k2 k3 = ve.b0 vo.b0 ve.b1 vo.b1, k4..k7 = bytes 2, 3
-  k0123 = __builtin_amdgcn_perm(vo, ve, 0x05010400u);
-  k4567 = __builtin_amdgcn_perm(vo, ve, 0x07030602u);
-}
-
 template <int MODE, int WF, int NB>
 COLI_DEV void store_group(const Group4<WF == kFmtI8> &G, Stage4<NB> &st, int wid) {
   constexpr bool W8 = WF == kFmtI8;
@@ -1457,9 +1493,12 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.up_offset_s = (int64_t)L.I * L.H / 64;
     const int nn = (L.I + 63) / 64;
     launch_k(COLI_K_GEMM_GATEUP,
-             wf == kFmtF4 ? gemm4_kernel<kGateUp, kFmtF4>
+             L.H % 256 ? (wf == kFmtF4   ? gemm_kernel<kGateUp, kFmtF4>
+                          : wf == kFmtI8 ? gemm_kernel<kGateUp, kFmtI8>
+                                         : gemm_kernel<kGateUp, kFmtI4>)
+             : wf == kFmtF4 ? gemm4_kernel<kGateUp, kFmtF4>
              : wf == kFmtI8 ? gemm4_kernel<kGateUp, kFmtI8>
-             : (L.H % 256 ? gemm_kernel<kGateUp> : gemm4_kernel<kGateUp, kFmtI4>),
+                            : gemm4_kernel<kGateUp, kFmtI4>,
              dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, w.qh, w.dh, nullptr, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
@@ -1476,9 +1515,12 @@ int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x,
     g.act_d = w.dh;
     const int nn = (L.H + BR - 1) / BR;
     launch_k(COLI_K_GEMM_DOWN,
-             wf == kFmtF4 ? gemm4_kernel<kDown, kFmtF4>
+             L.I % 256 ? (wf == kFmtF4   ? gemm_kernel<kDown, kFmtF4>
+                          : wf == kFmtI8 ? gemm_kernel<kDown, kFmtI8>
+                                         : gemm_kernel<kDown, kFmtI4>)
+             : wf == kFmtF4 ? gemm4_kernel<kDown, kFmtF4>
              : wf == kFmtI8 ? gemm4_kernel<kDown, kFmtI8>
-             : (L.I % 256 ? gemm_kernel<kDown> : gemm4_kernel<kDown, kFmtI4>),
+                            : gemm4_kernel<kDown, kFmtI4>,
              dim3(grid_for(band_items_host(mt, nn))), dim3(kThreads), 0, s, g, r, w.tiles, w.ntiles, 0,
              0, T, L.k, nn, L.expert_bytes, L.expert_scales, nullptr, nullptr, w.o, nullptr);
     if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
@@ -1510,9 +1552,12 @@ int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_ac
     return hip_status(hipGetLastError());
   }
   launch_k(COLI_K_BLOCK_DOTS,
-           wf == kFmtF4 ? gemm4_kernel<kDots, kFmtF4>
+           g.K % 256 ? (wf == kFmtF4   ? gemm_kernel<kDots, kFmtF4>
+                        : wf == kFmtI8 ? gemm_kernel<kDots, kFmtI8>
+                                       : gemm_kernel<kDots, kFmtI4>)
+           : wf == kFmtF4 ? gemm4_kernel<kDots, kFmtF4>
            : wf == kFmtI8 ? gemm4_kernel<kDots, kFmtI8>
-           : (g.K % 256 ? gemm_kernel<kDots> : gemm4_kernel<kDots, kFmtI4>),
+                          : gemm4_kernel<kDots, kFmtI4>,
            dim3(grid_for(band_items_host(ntile, nn))),
            dim3(kThreads), 0, s, g, none, nullptr, nullptr, T, expert, T, 1, nn, L.expert_bytes,
            L.expert_scales, nullptr, nullptr, nullptr, dots);

@@ -11,7 +11,6 @@ import pytest
 import torch
 
 import int4_routed_expert_router_amd as coli
-from int4_routed_expert_router_amd.binding import COLI_E_UNSUPPORTED
 import synth
 import test_gpu_decode as dec
 import test_gpu_int8_decode as dec8
@@ -73,12 +72,8 @@ def test_large_batch_invariant():
 
 
 @pytest.mark.parametrize("fmt", ["int8", "mxfp4"])
-def test_large_batch_unsupported_for_int8_mxfp4(fmt):
-    spec = dataclasses.replace(SMALL, int8=fmt == "int8", mxfp4=fmt == "mxfp4")
-    L = gpu_layer(spec, seed=1)
-    lg = synth.make_logits(spec, 17, seed=1).cuda()
-    x = synth.make_x(spec, 17, seed=1).cuda()
-    r = run_route(L, lg)
-    with pytest.raises(coli.ColiError) as e:
-        forward(L, r, x, "decode")
-    assert e.value.status == COLI_E_UNSUPPORTED
+def test_large_batch_int8_mxfp4(fmt):
+    """17 tokens on the matrix-core shape run the general kernels with the
+    int8 or MXFP4 codec."""
+    dec._decode_case(dataclasses.replace(SMALL, int8=fmt == "int8", mxfp4=fmt == "mxfp4"), 17,
+                     seed=1, zipf=0.5)

@@ -1,7 +1,8 @@
 """GPU parity of int8-weight experts in the decode / verify forward against
 the fp64 oracle: the container with one int8 code per weight (the MTP layer
-and OLMoE-style containers), on every streaming shape, plus batch invariance
-and the calls that return COLI_E_UNSUPPORTED."""
+and OLMoE-style containers), on every streaming shape, on shapes and batch
+sizes (17..64 tokens) served by the general decode kernels, plus batch
+invariance."""
 import dataclasses
 
 import numpy as np
@@ -82,18 +83,26 @@ def test_int8_extreme_codes():
         assert rel_err(y.cpu().numpy(), ref) < REL_TOL, hex(byte)
 
 
-def test_int8_unsupported_calls():
-    spec = _i8(synth.WORKLOADS["olmoe"].spec)
-    L = gpu_layer(spec)
-    lg = synth.make_logits(spec, 17).cuda()
-    x = synth.make_x(spec, 17).cuda()
-    r = run_route(L, lg)
-    with pytest.raises(coli.ColiError) as e:   # 17 tokens: past the streaming path
-        forward(L, r, x, "decode")
-    assert e.value.status == -2
-    odd = synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, int8=True)
-    Lo = gpu_layer(odd)
-    ro = run_route(Lo, synth.make_logits(odd, 1).cuda())
-    with pytest.raises(coli.ColiError) as e:   # a shape without the streaming path
-        forward(Lo, ro, synth.make_x(odd, 1).cuda(), "decode")
-    assert e.value.status == -2
+@pytest.mark.parametrize("spec,T", [
+    (synth.LayerSpec(2048, 1024, 64, 1, 8, sigmoid=False, renorm=True, int8=True), 17),
+    (synth.LayerSpec(2048, 1024, 64, 1, 8, sigmoid=False, renorm=True, int8=True), 64),
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, int8=True), 1),  # no stream shape
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, int8=True), 9),
+    (synth.LayerSpec(2112, 1088, 5, 0, 2, sigmoid=False, renorm=False, int8=True), 33),
+])
+def test_int8_decode_general_path(spec, T):
+    """Shapes without the streaming kernels and batches of 17..64 tokens run
+    the general (slot, row block) kernels with the int8 codec."""
+    _case(spec, T, seed=6, zipf=0.5)
+
+
+def test_int8_decode_large_batch_invariant():
+    """Among batches of 17..64 tokens a token's result does not depend on the
+    rest of the batch: the first 17 tokens of a 40-token batch, alone."""
+    spec = synth.LayerSpec(2048, 1024, 64, 1, 8, sigmoid=False, renorm=True, int8=True)
+    L = gpu_layer(spec, seed=8)
+    lg = synth.make_logits(spec, 40, seed=8, zipf_alpha=0.5).cuda()
+    x = synth.make_x(spec, 40, seed=8).cuda()
+    y40 = forward(L, run_route(L, lg), x, "decode")
+    y17 = forward(L, run_route(L, lg[:17].contiguous()), x[:17].contiguous(), "decode")
+    assert torch.equal(y17, y40[:17])

@@ -26,6 +26,8 @@ def _i8(spec):
     (synth.LayerSpec(256, 256, 4, 0, 2, False, False, int8=True), 5, (0, 3)),
     (synth.LayerSpec(2048, 1024, 4, 1, 2, True, True, int8=True), 100, (1, 4)),
     (synth.LayerSpec(6144, 2048, 2, 1, 2, True, True, int8=True), 64, (2,)),
+    # reduction lengths that are not multiples of 256 (the per-step kernel)
+    (synth.LayerSpec(192, 320, 3, 1, 2, True, True, int8=True), 37, (0, 3)),
 ])
 def test_int8_block_dots_bit_exact(spec, T, experts):
     print("int8 block dots case: H=%d I=%d T=%d" % (spec.hidden, spec.inter, T), flush=True)
@@ -103,18 +105,15 @@ def test_int8_prefill_glm_every_tile():
     (synth.LayerSpec(256, 256, 6, 1, 2, sigmoid=True, renorm=True, int8=True), 70),
     (synth.LayerSpec(1024, 768, 32, 0, 4, sigmoid=False, renorm=True, int8=True), 129),
     (synth.LayerSpec(512, 256, 1, 0, 1, sigmoid=False, renorm=False, int8=True), 1),
+    # H, I not multiples of 256: the per-step kernel
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, int8=True), 70),
+    (synth.LayerSpec(2112, 1088, 8, 1, 3, sigmoid=False, renorm=True, int8=True), 150),
 ])
 def test_int8_prefill_edge_shapes(spec, T):
     _case(spec, T, seed=3, zipf=0.6)
 
 
-def test_int8_prefill_deterministic_and_unsupported():
+def test_int8_prefill_deterministic():
     spec = _i8(synth.WORKLOADS["a3b"].spec)
     L, r, x, y = _case(spec, 96, zipf=synth.ZIPF_ALPHA, tokens=[0, 95])
     assert torch.equal(forward(L, r, x, "prefill"), y)
-    odd = synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, int8=True)
-    Lo = gpu_layer(odd)
-    ro = run_route(Lo, synth.make_logits(odd, 4).cuda())
-    with pytest.raises(coli.ColiError) as e:   # H, I not multiples of 256
-        forward(Lo, ro, synth.make_x(odd, 4).cuda(), "prefill")
-    assert e.value.status == -2

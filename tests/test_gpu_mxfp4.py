@@ -74,9 +74,35 @@ def test_mxfp4_decode_batch_invariant():
         assert torch.equal(forward(L, rt, x[t:t + 1].contiguous(), "decode")[0], y[t])
 
 
+@pytest.mark.parametrize("spec,T", [
+    (synth.LayerSpec(2048, 1024, 64, 1, 8, sigmoid=False, renorm=True, mxfp4=True), 17),
+    (synth.LayerSpec(2048, 1024, 64, 1, 8, sigmoid=False, renorm=True, mxfp4=True), 64),
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, mxfp4=True), 1),  # no stream shape
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, mxfp4=True), 9),
+    (synth.LayerSpec(2112, 1088, 5, 0, 2, sigmoid=False, renorm=False, mxfp4=True), 33),
+])
+def test_mxfp4_decode_general_path(spec, T):
+    """Shapes without the streaming kernels and batches of 17..64 tokens run
+    the general (slot, row block) kernels with the MXFP4 codec."""
+    _decode(spec, T, seed=6, zipf=0.5)
+
+
+def test_mxfp4_decode_large_batch_invariant():
+    """The first 17 tokens of a 40-token batch, alone, give the same bits."""
+    spec = synth.LayerSpec(2048, 1024, 64, 1, 8, sigmoid=False, renorm=True, mxfp4=True)
+    L = gpu_layer(spec, seed=8)
+    lg = synth.make_logits(spec, 40, seed=8, zipf_alpha=0.5).cuda()
+    x = synth.make_x(spec, 40, seed=8).cuda()
+    y40 = forward(L, run_route(L, lg), x, "decode")
+    y17 = forward(L, run_route(L, lg[:17].contiguous()), x[:17].contiguous(), "decode")
+    assert torch.equal(y17, y40[:17])
+
+
 @pytest.mark.parametrize("spec,T,experts", [
     (synth.LayerSpec(256, 256, 4, 0, 2, False, False, mxfp4=True), 5, (0, 3)),
     (synth.LayerSpec(2048, 1024, 4, 1, 2, True, True, mxfp4=True), 100, (1, 4)),
+    # reduction lengths that are not multiples of 256 (the per-step kernel)
+    (synth.LayerSpec(192, 320, 3, 1, 2, True, True, mxfp4=True), 37, (0, 3)),
 ])
 def test_mxfp4_block_dots_bit_exact(spec, T, experts):
     q4, sc = synth.make_weights(spec, seed=6, device="cuda")
@@ -131,6 +157,9 @@ def test_mxfp4_prefill_glm_every_tile():
 @pytest.mark.parametrize("spec,T", [
     (synth.LayerSpec(256, 256, 6, 1, 2, sigmoid=True, renorm=True, mxfp4=True), 70),
     (synth.LayerSpec(1024, 768, 32, 0, 4, sigmoid=False, renorm=True, mxfp4=True), 129),
+    # H, I not multiples of 256: the per-step kernel
+    (synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, mxfp4=True), 70),
+    (synth.LayerSpec(2112, 1088, 8, 1, 3, sigmoid=False, renorm=True, mxfp4=True), 150),
 ])
 def test_mxfp4_prefill_edge_shapes(spec, T):
     _prefill(spec, T, seed=3, zipf=0.6)
