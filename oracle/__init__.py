@@ -47,11 +47,15 @@ def _bind(path):
     lib.oracle_quantize_int4_gs64.argtypes = [p, i64, i64, p, p]
     lib.oracle_quantize_int8_gs64.argtypes = [p, i64, i64, p, p]
     lib.oracle_quantize_mxfp4.argtypes = [p, i64, i64, p, p]
+    lib.oracle_quantize_mxfp8.argtypes = [p, i64, p, p]
+    lib.oracle_mx_dots.argtypes = [i64, i64, i64, i64, p, p, i64, ctypes.c_int, p, p, i64, p]
+    lib.oracle_forward_prefill_mx.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p, p]
     lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_f16.restype = ctypes.c_uint16
     for f in ("oracle_route", "oracle_forward_decode", "oracle_forward_prefill",
               "oracle_quantize_q8_0", "oracle_block_dots", "oracle_router_logits",
-              "oracle_quantize_int4_gs64", "oracle_quantize_int8_gs64", "oracle_quantize_mxfp4"):
+              "oracle_quantize_int4_gs64", "oracle_quantize_int8_gs64", "oracle_quantize_mxfp4",
+              "oracle_quantize_mxfp8", "oracle_mx_dots", "oracle_forward_prefill_mx"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -252,6 +256,53 @@ def block_dots(H, I, E, S, q4, scales, expert, matrix, q_act, weights="int4"):
     if rc != 0:
         raise ValueError("oracle_block_dots: invalid arguments")
     return dots
+
+
+def quantize_mxfp8(v):
+    """MXFP8 (E4M3 elements, one E8M0 scale per 32) of fp32 values (length %
+    32 == 0) -> (uint8 codes, uint8 E8M0 per 32)."""
+    lib = _load()
+    v = _c(v, np.float32).reshape(-1)
+    q = np.zeros(v.size, np.uint8)
+    e = np.zeros(v.size // 32, np.uint8)
+    if lib.oracle_quantize_mxfp8(_ptr(v), v.size, _ptr(q), _ptr(e)) != 0:
+        raise ValueError("oracle_quantize_mxfp8: length must be a multiple of 32")
+    return q, e
+
+
+def mx_dots(H, I, E, S, q4, scales, expert, matrix, qa, ea):
+    """fp64 [T, rows]: matrix `matrix` of expert `expert` of an MXFP4 container
+    against MXFP8 activation rows (qa uint8 [T, K] codes, ea uint8 [T, K/32])."""
+    lib = _load()
+    q4, scales = _c(q4, np.uint8), _c(scales, np.uint8)
+    K = I if matrix == 2 else H
+    rows = H if matrix == 2 else I
+    qa = _c(qa, np.uint8).reshape(-1, K)
+    ea = _c(ea, np.uint8).reshape(-1, K // 32)
+    T = qa.shape[0]
+    out = np.zeros((T, rows), np.float64)
+    rc = lib.oracle_mx_dots(H, I, E, S, _ptr(q4), _ptr(scales), expert, matrix, _ptr(qa),
+                            _ptr(ea), T, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_mx_dots: invalid arguments")
+    return out
+
+
+def forward_prefill_mx(H, I, E, S, k, q4, scales, topk_idx, topk_w, x_bf16, want_h=False):
+    """MX-path layer output of an MXFP4 container (MXFP8 activations), fp64
+    [T, H] (and fp32 h [T, k+S, I])."""
+    lib = _load()
+    q4, scales = _c(q4, np.uint8), _c(scales, np.uint8)
+    topk_idx, topk_w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
+    x = _c(x_bf16, np.uint16)
+    T = x.shape[0]
+    y = np.zeros((T, H), np.float64)
+    h = np.zeros((T, k + S, I), np.float32) if want_h else None
+    rc = lib.oracle_forward_prefill_mx(H, I, E, S, k, _ptr(q4), _ptr(scales), _ptr(topk_idx),
+                                       _ptr(topk_w), _ptr(x), T, _ptr(y), _ptr(h))
+    if rc != 0:
+        raise ValueError("oracle_forward_prefill_mx failed")
+    return (y, h) if want_h else y
 
 
 def f32_to_f16_bits(v: float) -> int:

@@ -28,6 +28,10 @@
  *    per batch: same post, section "几个关键工程动作".
  *  - Q8_0-style int8 activations on the integer path: alphamatch.ai blog
  *    "Colibri：革命性 AI 引擎...", section "優化整數核心".
+ *  - fp4 experts with fp8 activations (the MX path): the DeepSeek V4 row of
+ *    the ai-tools-nav model family table pairs fp4 experts with fp8-e4m3;
+ *    read as OCP MXFP8 (E4M3 elements, one E8M0 scale per 32 values) for
+ *    the activations of an MXFP4 layer's expert GEMMs.
  *  - router choice decides the experts: aixq.cc article, section
  *    "为什么值得关注".
  * Readings where the pages are silent (routing function, tie order, nibble
@@ -607,6 +611,173 @@ int oracle_forward_prefill(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k
     free(hf);
     free(qh);
     free(dh);
+    free(o);
+  }
+  return bad ? OR_EINVAL : OR_OK;
+}
+
+/* ====================================================== MX activation path
+ *
+ * fp4 experts with fp8 activations.  The pages pair fp4 experts with
+ * fp8-e4m3 elsewhere in the same model (ai-tools-nav review, model family
+ * table, the DeepSeek V4 row) and give no activation format for the expert
+ * GEMMs; read here as OCP MXFP8: FP8 E4M3 elements with one E8M0 scale per
+ * 32 consecutive values, the block format of the MXFP4 weights. */
+
+/* FP8 E4M3 value of a code (OCP 8-bit floating point, the E4M3 variant): bit
+ * 7 sign, bits 6-3 exponent e with bias 7, bits 2-0 mantissa m; e = 0 is
+ * subnormal: m/8 * 2^-6; otherwise 2^(e-7) * (1 + m/8).  Magnitude code
+ * 0x7f is NaN; the largest finite magnitude is 0x7e = 448. */
+static double or_e4m3(int code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  const double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return (code & 0x80) ? -v : v;
+}
+
+/* MXFP8 (E4M3) of n fp32 values (n % 32 == 0), per block of 32, following
+ * the OCP microscaling conversion: shared exponent X = floor(log2(max|v|))
+ * - 8 (8 = the largest E4M3 exponent), stored as E8M0 byte E = X + 127
+ * clamped to [0, 254] (E = 0 for an all-zero block); each value becomes the
+ * E4M3 code nearest to v / 2^(E-127), ties to the even code, saturating at
+ * +-448 (sign kept, also for zero). */
+int oracle_quantize_mxfp8(const float *v, int64_t n, uint8_t *q, uint8_t *e8) {
+  if (n < 0 || n % 32) return OR_EINVAL;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float *vb = v + 32 * b;
+    double a = 0.0;
+    for (int i = 0; i < 32; ++i)
+      if (fabs((double)vb[i]) > a) a = fabs((double)vb[i]);
+    int E = 0;
+    if (a > 0.0) {
+      int ex;
+      frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+      E = (ex - 1) - 8 + 127;
+      if (E < 0) E = 0;
+      if (E > 254) E = 254;
+    }
+    e8[b] = (uint8_t)E;
+    for (int i = 0; i < 32; ++i) {
+      const double m = fabs(ldexp((double)vb[i], 127 - E));
+      int c = 0x7e; /* saturate at 448 */
+      for (int j = 0; j < 0x7e; ++j) {
+        const double mid = 0.5 * (or_e4m3(j) + or_e4m3(j + 1));
+        if (m < mid || (m == mid && !(j & 1))) { /* tie: the even code j */
+          c = j;
+          break;
+        }
+      }
+      const int neg = vb[i] < 0.0f || (vb[i] == 0.0f && signbit(vb[i]));
+      q[32 * b + i] = (uint8_t)(c | (neg ? 0x80 : 0));
+    }
+  }
+  return OR_OK;
+}
+
+/* Scaled dot of one 32-block of MXFP4 weight row n (codes + E8M0) with
+ * MXFP8 activations a (codes + E8M0 per block): 2^(Ew-127) * 2^(Ea-127) *
+ * sum over the block of e2m1(w_k) * e4m3(a_k), every product and the sum
+ * exact in fp64. */
+static double or_mx_block(const uint8_t *mat, const uint8_t *sc, int64_t K, int64_t n,
+                          const uint8_t *qa, const uint8_t *ea, int64_t b) {
+  double acc = 0.0;
+  for (int64_t k = 32 * b; k < 32 * (b + 1); ++k) {
+    const uint8_t byte = mat[n * (K / 2) + k / 2];
+    acc += or_e2m1((k & 1) ? (byte >> 4) : (byte & 15)) * or_e4m3(qa[k]);
+  }
+  return ldexp(acc, ((int)sc[n * (K / 32) + b] - 127) + ((int)ea[b] - 127));
+}
+
+/* out[t][n] = sum over blocks b of or_mx_block for matrix m (0 gate, 1 up,
+ * 2 down) of expert e of an MXFP4 container, against T rows of MXFP8
+ * activations (qa [T][K] codes, ea [T][K/32] E8M0), sum in block order. */
+int oracle_mx_dots(int64_t H, int64_t I, int64_t E, int64_t S, const uint8_t *q4,
+                   const uint8_t *scales, int64_t e, int m, const uint8_t *qa,
+                   const uint8_t *ea, int64_t T, double *out) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || m < 0 || m > 2 || e < 0 || e >= E + S || T < 0)
+    return OR_EINVAL;
+  or_layer L = {H, I, E, S, q4, scales, OR_FP4};
+  const int64_t K = (m == 2) ? I : H, rows = (m == 2) ? H : I;
+  const uint8_t *mat = or_mat(&L, e, m), *sc = or_sc(&L, e, m);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t n = 0; n < rows; ++n) {
+      double acc = 0.0;
+      for (int64_t b = 0; b < K / 32; ++b)
+        acc += or_mx_block(mat, sc, K, n, qa + t * K, ea + t * (K / 32), b);
+      out[t * rows + n] = acc;
+    }
+  return OR_OK;
+}
+
+/* MX-path expert FFN for one MXFP8 activation row (qx[H], ex[H/32]):
+ *   g[n] = sum_b mx_block(w_g[n], x, b)   (likewise u)
+ *   h = fp32(silu(g) * u);  (q_h, e_h) = MXFP8(h)
+ *   o[m] = sum_b mx_block(w_d[m], h, b) */
+static int or_ffn_mx(const or_layer *L, int64_t e, const uint8_t *qx, const uint8_t *ex,
+                     float *hf, uint8_t *qh, uint8_t *eh, double *o) {
+  const int64_t H = L->H, I = L->I;
+  const uint8_t *qg = or_mat(L, e, 0), *qu = or_mat(L, e, 1), *qd = or_mat(L, e, 2);
+  const uint8_t *sg = or_sc(L, e, 0), *su = or_sc(L, e, 1), *sd = or_sc(L, e, 2);
+  OR_ROWS_PARALLEL
+  for (int64_t n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int64_t b = 0; b < H / 32; ++b) {
+      g += or_mx_block(qg, sg, H, n, qx, ex, b);
+      u += or_mx_block(qu, su, H, n, qx, ex, b);
+    }
+    hf[n] = (float)(or_silu(g) * u);
+  }
+  if (oracle_quantize_mxfp8(hf, I, qh, eh) != OR_OK) return OR_EINVAL;
+  OR_ROWS_PARALLEL
+  for (int64_t m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int64_t b = 0; b < I / 32; ++b) acc += or_mx_block(qd, sd, I, m, qh, eh, b);
+    o[m] = acc;
+  }
+  return OR_OK;
+}
+
+/* MX-path prefill layer output of an MXFP4 container for T tokens (x bf16,
+ * y fp64 [T][H]): x[t] -> fp32 -> MXFP8, or_ffn_mx per routed expert and the
+ * shared expert, y[t] = sum_j w[t][j] * o_j + o_shared.  h_out as in
+ * oracle_forward_prefill. */
+int oracle_forward_prefill_mx(int64_t H, int64_t I, int64_t E, int64_t S, int64_t k,
+                              const uint8_t *q4, const uint8_t *scales,
+                              const int32_t *topk_idx, const float *topk_w,
+                              const uint16_t *x_bf16, int64_t T, double *y, float *h_out) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64 || E < 1 || S < 0 || S > 1 || k < 1) return OR_EINVAL;
+  or_layer L = {H, I, E, S, q4, scales, OR_FP4};
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad) if(or_tokens_parallel(T))
+  for (int64_t t = 0; t < T; ++t) {
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    uint8_t *qx = (uint8_t *)malloc((size_t)H);
+    uint8_t *ex = (uint8_t *)malloc((size_t)(H / 32));
+    float *hf = (float *)malloc(sizeof(float) * (size_t)I);
+    uint8_t *qh = (uint8_t *)malloc((size_t)I);
+    uint8_t *eh = (uint8_t *)malloc((size_t)(I / 32));
+    double *o = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!xf || !qx || !ex || !hf || !qh || !eh || !o) {
+      bad = 1;
+    } else {
+      for (int64_t i = 0; i < H; ++i) xf[i] = (float)or_bf16(x_bf16[t * H + i]);
+      if (oracle_quantize_mxfp8(xf, H, qx, ex) != OR_OK) bad = 1;
+      double *yt = y + t * H;
+      for (int64_t i = 0; i < H; ++i) yt[i] = 0.0;
+      for (int64_t j = 0; j < k + S && !bad; ++j) {
+        int64_t e = (j < k) ? topk_idx[t * k + j] : E;
+        double w = (j < k) ? (double)topk_w[t * k + j] : 1.0;
+        if (or_ffn_mx(&L, e, qx, ex, hf, qh, eh, o) != OR_OK) bad = 1;
+        if (h_out) memcpy(h_out + (t * (k + S) + j) * I, hf, sizeof(float) * (size_t)I);
+        for (int64_t i = 0; i < H; ++i) yt[i] += w * o[i];
+      }
+    }
+    free(xf);
+    free(qx);
+    free(ex);
+    free(hf);
+    free(qh);
+    free(eh);
     free(o);
   }
   return bad ? OR_EINVAL : OR_OK;

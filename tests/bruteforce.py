@@ -175,3 +175,67 @@ def block_dots(H, I, q4, expert, matrix, q_act, weights="int4"):
     T = a.shape[0]
     prod = w[None, :, :] * a[:, None, :]
     return prod.reshape(T, rows, K // 32, 32).sum(axis=3).astype(np.int32)
+
+
+# ------------------------------------------------------------ MX activations
+
+def e4m3_table() -> np.ndarray:
+    """Magnitudes of FP8 E4M3 codes 0..126 (OCP 8-bit floating point) from
+    their integer significands: code (e, m) is (8 + m) * 2^(e - 10) for e > 0
+    and m * 2^-9 for e = 0.  Code 127 (NaN) is left out."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e > 0, (8 + m) * np.exp2(e - 10.0), m * 2.0 ** -9)
+
+
+def mxfp8(v):
+    """MXFP8 E4M3 per 32 values -> (uint8 codes, uint8 E8M0).  Shared exponent
+    from the fp32 bit pattern of the block maximum (floor(log2) - 8, biased
+    by 127, clamped to [0, 254], 0 for an all-zero block); each element the
+    nearest table magnitude of v / 2^(E-127), ties to the even code, and
+    nothing above 448 (the table's last entry); sign from the sign bit."""
+    v = np.asarray(v, np.float32).reshape(-1, 32)
+    a = np.max(np.abs(v), axis=1)
+    expf = ((a.view(np.uint32) >> 23) & 0xFF).astype(np.int64)
+    floor_log2 = np.where(expf > 0, expf - 127, -150)  # fp32 subnormal maxima clamp to E = 0
+    E = np.where(a > 0, np.clip(floor_log2 - 8 + 127, 0, 254), 0).astype(np.int64)
+    m = np.abs(v.astype(np.float64) * np.exp2(127.0 - E)[:, None])
+    tab = e4m3_table()
+    dist = np.abs(m[..., None] - tab)
+    cand = dist == dist.min(axis=-1, keepdims=True)
+    even = cand & (np.arange(127) % 2 == 0)
+    idx = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    code = idx | np.where(np.signbit(v), 0x80, 0)
+    return code.astype(np.uint8).reshape(-1), E.astype(np.uint8)
+
+
+def mxfp8_values(codes, e8) -> np.ndarray:
+    """fp64 values of MXFP8 codes [..., K] with E8M0 [..., K/32]."""
+    codes = np.asarray(codes, np.uint8)
+    mag = e4m3_table()[np.minimum(codes & 0x7F, 126)]
+    val = np.where(codes & 0x80, -mag, mag)
+    sc = np.repeat(np.exp2(np.asarray(e8, np.float64) - 127.0), 32, axis=-1)
+    return val * sc
+
+
+def prefill_layer_mx(H, I, E, S, q4, scales, topk_idx, topk_w, x_bits):
+    """MX-path layer of an MXFP4 container: MXFP8(x), dense experts, fp32 h,
+    MXFP8(h), down, routing-weighted combine."""
+    x32 = bf16_to_f64(x_bits).astype(np.float32)
+    T = x32.shape[0]
+    qx, ex = mxfp8(x32)
+    xh = mxfp8_values(qx.reshape(T, H), ex.reshape(T, H // 32))
+    experts = dense_experts(H, I, E + S, q4, scales, "mxfp4")
+    wmat = np.zeros((T, E + S))
+    for t in range(T):
+        for j in range(topk_idx.shape[1]):
+            wmat[t, topk_idx[t, j]] += float(np.float32(topk_w[t, j]))
+    if S:
+        wmat[:, E] = 1.0
+    y = np.zeros((T, H))
+    for e, (wg, wu, wd) in enumerate(experts):
+        h = (silu(xh @ wg.T) * (xh @ wu.T)).astype(np.float32)
+        qh, eh = mxfp8(h)
+        hh = mxfp8_values(qh.reshape(T, I), eh.reshape(T, I // 32))
+        y += wmat[:, e:e + 1] * (hh @ wd.T)
+    return y

@@ -22,7 +22,8 @@ CHECKS = [
     pins.check_int4_quant_closed_form, pins.check_int4_quant_properties,
     pins.check_int8_decode_prefill_vs_bruteforce, pins.check_int8_block_dots,
     pins.check_mxfp4_decode_prefill_vs_bruteforce, pins.check_mxfp4_block_dots,
-    pins.check_int8_quant, pins.check_mxfp4_quant,
+    pins.check_int8_quant, pins.check_mxfp4_quant, pins.check_mxfp8_quant, pins.check_mx_dots,
+    pins.check_prefill_mx_vs_bruteforce,
 ]
 
 # (name, text in the oracle, replacement)
@@ -102,6 +103,31 @@ MUTANTS = [
      "acc += or_bf16(x[t * H + k]) * or_bf16(w[k * E + e]);"),
     ("router drops the last column", "for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])",
      "for (int64_t k = 0; k < H - 1; ++k) acc += or_bf16(x[t * H + k])"),
+    ("mxfp8 shared exponent off by one", "E = (ex - 1) - 8 + 127;", "E = (ex - 1) - 7 + 127;"),
+    ("mxfp8 ties away from zero", "if (m < mid || (m == mid && !(j & 1))) {", "if (m < mid) {"),
+    ("mxfp8 overflows to NaN", "int c = 0x7e; /* saturate at 448 */", "int c = 0x7f;"),
+    ("mxfp8 drops the sign of zero",
+     "const int neg = vb[i] < 0.0f || (vb[i] == 0.0f && signbit(vb[i]));",
+     "const int neg = vb[i] < 0.0f;"),
+    ("e4m3 exponent bias 8", "const double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);",
+     "const double v = e ? ldexp(1.0 + m / 8.0, e - 8) : ldexp(m / 8.0, -6);"),
+    ("e4m3 subnormals read as normal",
+     "const double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);",
+     "const double v = ldexp(1.0 + m / 8.0, e - 7);"),
+    ("mx block drops the activation scale",
+     "return ldexp(acc, ((int)sc[n * (K / 32) + b] - 127) + ((int)ea[b] - 127));",
+     "return ldexp(acc, ((int)sc[n * (K / 32) + b] - 127));"),
+    ("mx weight scale per 64",
+     "return ldexp(acc, ((int)sc[n * (K / 32) + b] - 127) + ((int)ea[b] - 127));",
+     "return ldexp(acc, ((int)sc[n * (K / 32) + b / 2] - 127) + ((int)ea[b] - 127));"),
+    ("mx fp4 nibbles high first", "or_e2m1((k & 1) ? (byte >> 4) : (byte & 15))",
+     "or_e2m1((k & 1) ? (byte & 15) : (byte >> 4))"),
+    ("mx activations paired wrongly", "* or_e4m3(qa[k]);", "* or_e4m3(qa[k ^ 1]);"),
+    ("mx up uses gate weights", "u += or_mx_block(qu, su, H, n, qx, ex, b);",
+     "u += or_mx_block(qg, su, H, n, qx, ex, b);"),
+    ("mx down repeats block 0",
+     "for (int64_t b = 0; b < I / 32; ++b) acc += or_mx_block(qd, sd, I, m, qh, eh, b);",
+     "for (int64_t b = 0; b < I / 32; ++b) acc += or_mx_block(qd, sd, I, m, qh, eh + b - b, 0);"),
     ("router accumulates in fp32",
      "double acc = 0.0;\n      for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])",
      "float acc = 0.0f;\n      for (int64_t k = 0; k < H; ++k) acc += or_bf16(x[t * H + k])"),

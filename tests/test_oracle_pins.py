@@ -703,6 +703,98 @@ def check_mxfp4_quant():
     assert np.array_equal(dec, vals)
 
 
+# ---------------------------------------------------- MX activation path
+
+def check_mxfp8_quant():
+    rng = np.random.default_rng(41)
+    v = (rng.standard_normal((8, 64)) * 10.0 ** rng.uniform(-6, 6, (8, 1))).astype(np.float32)
+    v[0, :32] = 0.0
+    v[0, 32:] = -0.0
+    v[1, :32] = rng.uniform(-1e-39, 1e-39, 32)                     # fp32 subnormal maximum
+    tab = bf.e4m3_table()
+    mids = 0.5 * (tab[:-1] + tab[1:])
+    v[2, :31] = mids[rng.choice(len(mids), 31)] * 2.0 ** -20        # exact ties
+    v[2, 31] = 448.0 * 2.0 ** -20                                   # fixes the block exponent
+    v[2, 32:64] = np.array([500.0, 464.0, -470.0, 449.0] * 8) * 2.0 ** 3   # saturation at 448
+    v[3] = rng.uniform(-3e38, 3e38, 64)                             # near the fp32 maximum
+    v[4, :32] = 2.0 ** -126                                         # exact power-of-two maxima
+    v[5, :32] = np.concatenate([[256.0], rng.uniform(-2.0 ** -6, 2.0 ** -6, 31)])  # E4M3 subnormals
+    q, e = oracle.quantize_mxfp8(v)
+    bq, be = bf.mxfp8(v)
+    assert np.array_equal(e, be) and np.array_equal(q, bq)
+    # scale bytes are [row * 2 + block]: the tie block has max 448 * 2^-20
+    # (E 127 - 20), the saturation block 500 * 2^3 (floor log2 = 11, E 130),
+    # 2^-126 maxima clamp E to 0, and a block whose maximum is 256 has E 127
+    assert e[4] == 107 and e[5] == 130 and e[8] == 0 and e[10] == 127
+    assert np.all(q[128 + 32:128 + 64] & 0x7F == 0x7E)             # saturated magnitudes
+    assert np.all(q[256:256 + 32] == 0x40)                          # 2^-126 / 2^-127 = 2.0
+    assert q[0] == 0x00 and q[32] == 0x80                           # +0 and -0
+    # closed form: table values times 2^X round-trip
+    vals = rng.choice(np.concatenate([tab, -tab[1:]]), size=(3, 64))
+    vals[:, 0] = vals[:, 32] = 448.0
+    q2, e2 = oracle.quantize_mxfp8((vals * 2.0 ** -11).astype(np.float32))
+    assert np.all(e2 == 127 - 11)
+    assert np.array_equal(bf.mxfp8_values(q2.reshape(3, 64), e2.reshape(3, 2)),
+                          vals * 2.0 ** -11)
+
+
+def check_mx_dots():
+    # E2M1 codes 0..15 at k = 0..15 of row 0, activation row j one-hot at k = j
+    H, I = 64, 64
+    q = np.zeros(3 * H * I // 2, np.uint8)
+    nib = np.arange(16, dtype=np.uint8)
+    q[:8] = nib[0::2] | (nib[1::2] << 4)
+    z = np.full(3 * H * I // 32, 127, np.uint8)
+    z[0] = 130                                                      # 2^3 on row 0, block 0
+    qa = np.zeros((16, H), np.uint8)
+    qa[np.arange(16), np.arange(16)] = 0x3A                         # E4M3 1.25
+    ea = np.full((16, H // 32), 125, np.uint8)                      # 2^-2
+    out = oracle.mx_dots(H, I, 1, 0, q, z, 0, 0, qa, ea)
+    e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, 0, -.5, -1, -1.5, -2, -3, -4, -6])
+    assert np.array_equal(out[:, 0], e2m1 * 1.25 * 2.0 ** 3 * 2.0 ** -2)
+    assert not out[:, 1:].any()
+    # random codes and scales against the dense brute force
+    spec = SIGMOID_SMALL_F4
+    q4, sc = _host_layer(spec, 16)
+    rng = np.random.default_rng(16)
+    for m in (0, 1, 2):
+        K = spec.inter if m == 2 else spec.hidden
+        qa = rng.integers(0, 256, (3, K)).astype(np.uint8)
+        qa[(qa & 0x7F) == 0x7F] = 0x7E
+        ea = rng.integers(117, 138, (3, K // 32)).astype(np.uint8)
+        got = oracle.mx_dots(spec.hidden, spec.inter, spec.n_experts, spec.n_shared, q4, sc,
+                             spec.n_total - 1, m, qa, ea)
+        wmat = bf.dense_experts(spec.hidden, spec.inter, spec.n_total, q4, sc, "mxfp4")[-1][m]
+        want = bf.mxfp8_values(qa, ea) @ wmat.T
+        assert _rel(got, want) < 1e-12
+
+
+def check_prefill_mx_vs_bruteforce():
+    for spec, T in ((SOFTMAX_SMALL_F4, 4), (SIGMOID_SMALL_F4, 5)):
+        q4, sc, r, x = _decode_case(spec, T, seed=17, zipf=0.3)
+        s = spec
+        sc = sc.copy()
+        sc[:7] = (100, 110, 127, 128, 130, 135, 60)
+        args = (s.hidden, s.inter, s.n_experts, s.n_shared, s.top_k, q4, sc, r["topk_idx"],
+                r["topk_w"], x)
+        y = oracle.forward_prefill_mx(*args)
+        yb = bf.prefill_layer_mx(s.hidden, s.inter, s.n_experts, s.n_shared, q4, sc,
+                                 r["topk_idx"], r["topk_w"], x)
+        assert _rel(y, yb) < 1e-10
+
+
+def test_mxfp8_quant():
+    check_mxfp8_quant()
+
+
+def test_mx_dots():
+    check_mx_dots()
+
+
+def test_prefill_mx_vs_bruteforce():
+    check_prefill_mx_vs_bruteforce()
+
+
 def test_int8_quant():
     check_int8_quant()
 
