@@ -432,6 +432,7 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
     gemm_us = sum(kern.get(k, {"avg_us": 0})["avg_us"] for k in ("gemm_gateup", "gemm_down"))
     out = {"workload": name, "path": "prefill",
            "weights": spec.weights, "tokens": T, "ms_per_step": round(ms, 4),
+           "activations": "mxfp8 (MX matrix cores)" if spec.mx_act else "q8_0 (int8 matrix cores)",
            "tokens_per_s": round(T / (ms * 1e-3), 1),
            "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
            "int8_frac": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -560,6 +561,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="main workload only")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the 2048-token GLM prefill workload (for profiling it)")
+    ap.add_argument("--prefill-mx-only", action="store_true",
+                    help="the 2048-token GLM-shaped prefill with MXFP4 experts on the MX path")
     ap.add_argument("--prefill-dense-only", action="store_true",
                     help="the GLM-shaped GEMMs with every one of 2048 tokens on each expert")
     ap.add_argument("--decode-t4-only", action="store_true",
@@ -598,6 +601,12 @@ def main():
         pw = synth.WORKLOADS["glm_prefill"]
         print(json.dumps(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
                                            args.steps, args.warmup, copies=1)), flush=True)
+        return
+    if args.prefill_mx_only:
+        pw = synth.WORKLOADS["glm_prefill"]
+        spec = dataclasses.replace(pw.spec, mxfp4=True, mx_act=True)
+        print(json.dumps(secondary_prefill("glm_mxfp4_mx_prefill_T2048", spec, 2048,
+                                           pw.zipf_alpha, args.steps, args.warmup)), flush=True)
         return
     if args.prefill_dense_only:
         print(json.dumps(prefill_dense(args.steps, args.warmup)), flush=True)
@@ -708,6 +717,14 @@ def main():
         secondary.append(secondary_prefill("olmoe_mxfp4_prefill_T512",
                                            dataclasses.replace(ow.spec, mxfp4=True), 512, 0.0,
                                            20, 3, copies=4))
+        # the MX path: MXFP8 activations on the MX matrix cores (block scales in hardware)
+        secondary.append(secondary_prefill("olmoe_mxfp4_mx_prefill_T512",
+                                           dataclasses.replace(ow.spec, mxfp4=True, mx_act=True),
+                                           512, 0.0, 20, 3, copies=4))
+        pw = synth.WORKLOADS["glm_prefill"]
+        secondary.append(secondary_prefill("glm_mxfp4_mx_prefill_T2048",
+                                           dataclasses.replace(pw.spec, mxfp4=True, mx_act=True),
+                                           2048, pw.zipf_alpha, 10, 2))
         aw = synth.WORKLOADS["a3b"]
         for t in aw.tokens:
             secondary.append(secondary_decode("a3b_decode_T%d" % t, aw.spec, t, aw.zipf_alpha, 4,

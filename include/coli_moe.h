@@ -69,6 +69,18 @@ enum {
   COLI_ROUTE_RENORM = 1u << 8
 };
 
+/* ---- activation format of the prefill path (coli_moe_layer_t.flags) ------
+ * COLI_ACT_MXFP8: for MXFP4 layers only (COLI_E_INVALID otherwise).  The
+ * pages pair fp4 experts with fp8-e4m3 elsewhere in the same model
+ * (ai-tools-nav review, model family table, the DeepSeek V4 row); with this
+ * flag coli_moe_forward_prefill quantises the activations (x, and h between
+ * the GEMMs) to MXFP8 -- OCP FP8 E4M3 codes with one E8M0 scale per 32
+ * values, see coli_moe_quantize_mxfp8 -- instead of Q8_0, and runs both
+ * GEMMs on gfx950's MX matrix cores, which apply the weight and activation
+ * block scales themselves.  Needs H and I multiples of 128
+ * (COLI_E_UNSUPPORTED otherwise).  Decode ignores the flag. */
+enum { COLI_ACT_MXFP8 = 1u << 16 };
+
 /* output element type of the forward calls */
 enum { COLI_OUT_BF16 = 0, COLI_OUT_F32 = 1 };
 
@@ -134,7 +146,7 @@ typedef struct coli_moe_layer {
   int32_t n_experts;     /* E, routed experts */
   int32_t n_shared;      /* S, 0 or 1 always-on shared experts (index E) */
   int32_t top_k;         /* k */
-  uint32_t flags;        /* COLI_ROUTE_* */
+  uint32_t flags;        /* COLI_ROUTE_* | COLI_ACT_MXFP8 */
   float routed_scale;    /* multiplies every routing weight (1.0f usually) */
   const uint8_t *q4;     /* device, see above */
   const uint16_t *scales;/* device, fp16 bit patterns, see above */
@@ -362,6 +374,32 @@ int coli_moe_mfma_probe(int32_t kind, int32_t iters, int32_t workgroups, uint32_
 int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert,
                         int32_t matrix, const int8_t *q_act, int32_t T,
                         int32_t *dots, void *stream);
+
+/* MXFP8 quantisation of n values (n a multiple of 32), the activation format
+ * of the MX path (COLI_ACT_MXFP8), following the OCP microscaling
+ * conversion.  Per block of 32 values v: X = floor(log2 max|v|) - 8 (8 = the
+ * largest FP8 E4M3 exponent), stored as E8M0 byte E = X + 127 clamped to
+ * [0, 254] (E = 0 for an all-zero block); each value becomes the E4M3 code
+ * (bit 7 sign, exponent bias 7, 3 mantissa bits, subnormals, magnitude 0x7f
+ * unused) nearest to v / 2^(E-127), ties to the even code, saturating at
+ * +-448, the sign kept also for zero.
+ *  src [n] bf16 or fp32 (src_dtype);  q [n] E4M3 codes;  e8m0 [n/32].
+ * The same device code as the MX prefill path's quantiser. */
+int coli_moe_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t n,
+                            uint8_t *q, uint8_t *e8m0, void *stream);
+
+/* One weight matrix of one expert of an MXFP4 layer against T rows of MXFP8
+ * activations, on the MX matrix cores -- the GEMM of the MX prefill path:
+ *   out[t][n] = sum over 32-blocks b of 2^(Ew[n][b]-127) * 2^(Ea[t][b]-127)
+ *               * sum_{k in block b} e2m1(w[n][k]) * e4m3(a[t][k])
+ * accumulated in fp32 by the hardware (its order is not specified).
+ *  matrix 0 = gate, 1 = up (K = H, rows = I), 2 = down (K = I, rows = H);
+ *  K must be a multiple of 128 (COLI_E_UNSUPPORTED otherwise).
+ *  q_act [T*K] E4M3 codes, e_act [T*K/32] E8M0, T in [1, 4096];
+ *  out [T*rows] fp32.  COLI_E_INVALID for layers that are not MXFP4. */
+int coli_moe_mx_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t matrix,
+                     const uint8_t *q_act, const uint8_t *e_act, int32_t T, float *out,
+                     void *stream);
 
 /* ---- optional kernel timing ----------------------------------------------
  * For benchmarks and profilers.  After coli_moe_set_trace(t) with t != NULL,

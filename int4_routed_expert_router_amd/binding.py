@@ -16,6 +16,7 @@ COLI_OUT_BF16, COLI_OUT_F32 = 0, 1
 COLI_SRC_BF16, COLI_SRC_F32 = 0, 1
 COLI_ENTRY_ROUTE, COLI_ENTRY_DECODE, COLI_ENTRY_PREFILL = 0, 1, 2
 COLI_WEIGHTS_INT4, COLI_WEIGHTS_INT8, COLI_WEIGHTS_MXFP4 = 0, 1, 2
+COLI_ACT_MXFP8 = 1 << 16
 
 
 class ColiError(RuntimeError):
@@ -84,6 +85,8 @@ def _load():
         lib.coli_moe_read_probe.argtypes = [vp, i64, vp, vp]
         lib.coli_moe_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
         lib.coli_moe_block_dots.argtypes = [P(_LayerC), i32, i32, vp, i32, vp, vp]
+        lib.coli_moe_quantize_mxfp8.argtypes = [vp, i32, i64, vp, vp, vp]
+        lib.coli_moe_mx_dots.argtypes = [P(_LayerC), i32, i32, vp, vp, i32, vp, vp]
         lib.coli_moe_strerror.argtypes = [ctypes.c_int]
         lib.coli_moe_strerror.restype = ctypes.c_char_p
         lib.coli_moe_set_trace.argtypes = [ctypes.POINTER(_TraceC)]
@@ -94,7 +97,7 @@ def _load():
                   "coli_moe_forward_decode_noalloc", "coli_moe_forward_prefill", "coli_moe_quantize_q8_0", "coli_moe_block_dots",
                   "coli_moe_quantize_int4_gs64", "coli_moe_quantize_int8_gs64",
                   "coli_moe_quantize_mxfp4", "coli_moe_read_probe",
-                  "coli_moe_mfma_probe"):
+                  "coli_moe_mfma_probe", "coli_moe_quantize_mxfp8", "coli_moe_mx_dots"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -263,6 +266,18 @@ def coli_moe_block_dots(layer: Layer, expert: int, matrix: int, q_act, T: int, d
                         stream=None):
     _check("coli_moe_block_dots", _load().coli_moe_block_dots(
         ctypes.byref(layer.c), expert, matrix, _ptr(q_act), T, _ptr(dots), _stream(stream)))
+
+
+def coli_moe_quantize_mxfp8(src, src_dtype: int, n: int, q, e8m0, stream=None):
+    _check("coli_moe_quantize_mxfp8", _load().coli_moe_quantize_mxfp8(
+        _ptr(src), src_dtype, n, _ptr(q), _ptr(e8m0), _stream(stream)))
+
+
+def coli_moe_mx_dots(layer: Layer, expert: int, matrix: int, q_act, e_act, T: int, out,
+                     stream=None):
+    _check("coli_moe_mx_dots", _load().coli_moe_mx_dots(
+        ctypes.byref(layer.c), expert, matrix, _ptr(q_act), _ptr(e_act), T, _ptr(out),
+        _stream(stream)))
 
 
 def _hip_runtime():

@@ -29,11 +29,14 @@ int check_layer(const coli_moe_layer_t *l, Layer *out) {
   if (l->n_experts < 1 || l->n_experts > kMaxExperts) return COLI_E_INVALID;
   if (l->n_shared < 0 || l->n_shared > 1) return COLI_E_INVALID;
   if (l->top_k < 1 || l->top_k > l->n_experts || l->top_k > kMaxTopK) return COLI_E_INVALID;
-  if (l->flags & ~(uint32_t)(COLI_ROUTE_SIGMOID | COLI_ROUTE_RENORM)) return COLI_E_INVALID;
+  if (l->flags & ~(uint32_t)(COLI_ROUTE_SIGMOID | COLI_ROUTE_RENORM | COLI_ACT_MXFP8))
+    return COLI_E_INVALID;
   if (!isfinite(l->routed_scale)) return COLI_E_INVALID;
   if (l->weight_format != COLI_WEIGHTS_INT4 && l->weight_format != COLI_WEIGHTS_INT8 &&
       l->weight_format != COLI_WEIGHTS_MXFP4)
     return COLI_E_INVALID;
+  // MXFP8 activations pair with MXFP4 weights only
+  if ((l->flags & COLI_ACT_MXFP8) && l->weight_format != COLI_WEIGHTS_MXFP4) return COLI_E_INVALID;
   if (out) {
     out->H = H;
     out->I = I;
@@ -87,6 +90,9 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
   if ((rc = check_route(route))) return rc;
   if ((rc = check_tokens(*L, T, entry == COLI_ENTRY_DECODE ? kMaxDecodeT : kMaxT))) return rc;
   if (entry == COLI_ENTRY_DECODE && L->I > kMaxDecodeInter) return COLI_E_UNSUPPORTED;
+  // the MX prefill steps through k 128 at a time
+  if (entry != COLI_ENTRY_DECODE && (L->flags & COLI_ACT_MXFP8) && (L->H % 128 || L->I % 128))
+    return COLI_E_UNSUPPORTED;
   if (!x || !y) return COLI_E_INVALID;
   if (y_dtype != COLI_OUT_BF16 && y_dtype != COLI_OUT_F32) return COLI_E_INVALID;
   if (!aligned(x, 16) || !aligned(y, 16)) return COLI_E_ALIGN;
@@ -292,6 +298,31 @@ int coli_moe_block_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t m
   if (T < 1 || T > 4096 || !q_act || !dots) return COLI_E_INVALID;
   if (!aligned(q_act, 16) || !aligned(dots, 16)) return COLI_E_ALIGN;
   return launch_block_dots(L, expert, matrix, q_act, T, dots, reinterpret_cast<hipStream_t>(stream));
+}
+
+int coli_moe_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t n, uint8_t *q,
+                            uint8_t *e8m0, void *stream) {
+  if (!src || !q || !e8m0) return COLI_E_INVALID;
+  if (src_dtype != COLI_SRC_BF16 && src_dtype != COLI_SRC_F32) return COLI_E_INVALID;
+  if (n < 32 || n % 32 || n > (int64_t(1) << 34)) return COLI_E_INVALID;
+  if (!aligned(src, 16) || !aligned(q, 16)) return COLI_E_ALIGN;
+  return launch_quantize_mxfp8(src, src_dtype, n, q, e8m0, reinterpret_cast<hipStream_t>(stream));
+}
+
+int coli_moe_mx_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t matrix,
+                     const uint8_t *q_act, const uint8_t *e_act, int32_t T, float *out,
+                     void *stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(L))) return rc;
+  if (!L.f4) return COLI_E_INVALID;
+  if (expert < 0 || expert >= L.E + L.S || matrix < 0 || matrix > 2) return COLI_E_INVALID;
+  if (T < 1 || T > 4096 || !q_act || !e_act || !out) return COLI_E_INVALID;
+  if ((matrix == 2 ? L.I : L.H) % 128) return COLI_E_UNSUPPORTED;
+  if (!aligned(q_act, 16) || !aligned(e_act, 4) || !aligned(out, 16)) return COLI_E_ALIGN;
+  return launch_mx_dots(L, expert, matrix, q_act, e_act, T, out,
+                        reinterpret_cast<hipStream_t>(stream));
 }
 
 int coli_moe_set_trace(coli_moe_trace_t *trace) {

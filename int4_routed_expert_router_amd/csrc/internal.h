@@ -65,6 +65,11 @@ int launch_quantize_mxfp4(const void *src, int src_dtype, int64_t n, uint8_t *q4
                           hipStream_t s);
 int launch_block_dots(const Layer &L, int expert, int matrix, const int8_t *q_act, int T,
                       int32_t *dots, hipStream_t s);
+// MX path (prefill.hip): MXFP8 quantiser and one matrix's MX GEMM in fp32.
+int launch_quantize_mxfp8(const void *src, int src_dtype, int64_t n, uint8_t *q, uint8_t *e8,
+                          hipStream_t s);
+int launch_mx_dots(const Layer &L, int expert, int matrix, const uint8_t *qa, const uint8_t *ea,
+                   int T, float *out, hipStream_t s);
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_E_HIP; }
 

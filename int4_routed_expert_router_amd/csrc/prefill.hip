@@ -1348,6 +1348,263 @@ dgemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
   }
 }
 
+// ------------------------------------------ MX path: MXFP4 x MXFP8 on the MX matrix cores
+//
+// Layers flagged COLI_ACT_MXFP8 (MXFP4 weights) quantise the activations to
+// MXFP8 -- FP8 E4M3 codes with one E8M0 scale per 32 values, the OCP
+// microscaling format of the weights -- and run both GEMMs on
+// v_mfma_scale_f32_16x16x128_f8f6f4, which applies the two E8M0 scales of
+// every 32-block itself: there is no per-block epilogue on the vector ALUs.
+//
+// Operand layout of the instruction (measured on the GPU with an in-bounds
+// probe): lane l = r + 16 g holds row (or column) r.  An FP4 operand holds
+// k in [32g, 32g + 32) as 16 bytes, low nibble first; an FP8 operand holds
+// k in [16g, 16g + 16) in bytes 0..15 and k in [64 + 16g, 64 + 16g + 16) in
+// bytes 16..31.  Lane l's scale byte belongs to row r and the 32-block g.
+// The result tile is laid out as in the other 16x16 instructions.
+constexpr int kMxK = 128;  // k per instruction
+typedef int coli_i32x8 __attribute__((ext_vector_type(8)));
+typedef float coli_f32x4v __attribute__((ext_vector_type(4)));
+
+// E8M0 shared exponent of a 32-block with maximum magnitude amax:
+// floor(log2 amax) - 8 (the largest E4M3 exponent) + 127, clamped to
+// [0, 254]; 0 for an all-zero block.  floor(log2) comes from the fp32
+// exponent field; a subnormal amax clamps to 0 anyway.
+COLI_DEV uint32_t mx8_exponent(float amax) {
+  const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);  // biased; 0 for 0 / subnormal
+  const int E = ex - 127 - 8 + 127;
+  return amax > 0.0f ? (uint32_t)max(0, min(254, E)) : 0u;
+}
+
+// E4M3 code of v / 2^(E-127) (v fp32), nearest with ties to the even code,
+// saturating at 448, sign kept (also for zero).  The scaled magnitude m is
+// exact (a power-of-two scaling; only values far below the smallest code
+// can lose bits, and they code 0 either way).
+COLI_DEV uint32_t mx8_code(float v, uint32_t E) {
+  // 2^(127 - E) is a normal fp32 number for E <= 253; fp32 inputs give E <= 246
+  const float m = E <= 253 ? fabsf(v) * __uint_as_float((254u - E) << 23)
+                           : fabsf(v) * 0x1p-126f * 0.5f;
+  uint32_t c;
+  if (m >= 448.0f) {
+    c = 0x7e;
+  } else if (m < 0x1p-6f) {            // subnormal codes: m / 2^-9, nearest even
+    c = (uint32_t)rintf(m * 512.0f);   // 8 = 2^-6, the smallest normal code
+  } else {
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;  // 2^e <= m
+    uint32_t r = (uint32_t)rintf(m * __uint_as_float((uint32_t)(127 + 3 - e) << 23));  // 8..16
+    int ee = e;
+    if (r == 16) {
+      r = 8;
+      ++ee;
+    }
+    c = ((uint32_t)(ee + 7) << 3) | (r - 8);
+  }
+  return c | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+// MXFP8 of n values (n % 32 == 0), one thread per 32-block: codes [n], E8M0 [n / 32].
+__global__ void __launch_bounds__(kThreads) quantize_mx_kernel(const void *__restrict__ src,
+                                                               int src_dtype, int64_t nb,
+                                                               uint8_t *__restrict__ q,
+                                                               uint8_t *__restrict__ e8) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nb) return;
+  float v[32];
+  if (src_dtype == COLI_SRC_BF16) {
+    const uint4 *s = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(src) + 32 * b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 w = s[j];
+      const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * j + 2 * i] = __uint_as_float(d[i] << 16);
+        v[8 * j + 2 * i + 1] = __uint_as_float(d[i] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4 *s = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(src) + 32 * b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 w = s[j];
+      v[4 * j] = w.x;
+      v[4 * j + 1] = w.y;
+      v[4 * j + 2] = w.z;
+      v[4 * j + 3] = w.w;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t E = mx8_exponent(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    w[j] = mx8_code(v[4 * j], E) | (mx8_code(v[4 * j + 1], E) << 8) |
+           (mx8_code(v[4 * j + 2], E) << 16) | (mx8_code(v[4 * j + 3], E) << 24);
+  uint4 *dst = reinterpret_cast<uint4 *>(q + 32 * b);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  e8[b] = (uint8_t)E;
+}
+
+// One K step of a wave's operands: 4 weight row tiles (16 bytes of E2M1
+// codes and a scale byte per lane) and 2 token tiles (32 bytes of E4M3
+// codes and a scale byte per lane).
+struct MxOps {
+  uint4 a[4];
+  uint32_t sa[4];
+  uint4 b[2][2];
+  uint32_t sb[2];
+};
+
+// Work items, tiles and wave roles as gemm_kernel: wave (wn, wm) computes
+// weight row tiles wave_row_tile(wn, 0..3) against token tiles 2wm, 2wm+1.
+//  gate/up: epilogue h = silu(g) * u, then MXFP8 of h per 32 channels (one
+//           wave holds the 32 channels of one block for its 32 tokens).
+//  down   : fp32 o rows.   dots: fp32 [T][rows] of one matrix (debug).
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) mxgemm_kernel(
+    GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
+    const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
+    int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
+    uint8_t *__restrict__ qh_out, uint8_t *__restrict__ eh_out, float *__restrict__ o_out) {
+  __shared__ int rowid[BM];
+  __shared__ int outrow[BM];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wid >> 1, wm = wid & 1;
+  const int r16 = lane & 15, gq = lane >> 4;
+  const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
+  const int items = band_items(ntiles, n_ntiles);
+  const int K = g.K;
+  const int G = gridDim.x;
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const uint8_t *act = reinterpret_cast<const uint8_t *>(g.act);
+  const uint8_t *act_e = reinterpret_cast<const uint8_t *>(g.act_d);
+
+  for (int item = vid; item < items; item += G) {
+    int tile, ntile;
+    item_coords(item, n_ntiles, tile, ntile);
+    if (tile >= ntiles) continue;
+    const Item it = setup_item<MODE>(tile, ntile, tiles, fixed_ntok, fixed_expert, r, T, k,
+                                     rowid, outrow);
+    const uint8_t *wq = g.wq + (int64_t)it.expert * expert_stride_q;
+    const uint8_t *ws = reinterpret_cast<const uint8_t *>(g.ws + (int64_t)it.expert * expert_stride_s);
+    // this lane's sources: weight rows (clamped to row 0 past the matrix)
+    const uint8_t *pa[4];
+    const uint32_t *psa[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int t = wave_row_tile<MODE>(wn, a);
+      int n;
+      int64_t oq = 0, os = 0;
+      if (MODE == kGateUp) {
+        n = it.n0 + 16 * (t & 3) + r16;
+        if (t >= 4) {
+          oq = g.up_offset_q;
+          os = 2 * g.up_offset_s;  // 16-bit units -> bytes
+        }
+      } else {
+        n = it.n0 + 16 * t + r16;
+      }
+      if (n >= g.rows) n = 0;
+      pa[a] = wq + oq + (int64_t)n * (K / 2) + 16 * gq;
+      psa[a] = reinterpret_cast<const uint32_t *>(ws + os + (int64_t)n * (K / 32));
+    }
+    const uint8_t *pb[2];
+    const uint32_t *psb[2];
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const int row = rowid[32 * wm + 16 * ms + r16];
+      pb[ms] = act + (int64_t)row * K + 16 * gq;
+      psb[ms] = reinterpret_cast<const uint32_t *>(act_e + (int64_t)row * (K / 32));
+    }
+    auto load = [&](int k0, MxOps &o) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        o.a[a] = *reinterpret_cast<const uint4 *>(pa[a] + k0 / 2);
+        o.sa[a] = (psa[a][k0 / 128] >> (8 * gq)) & 0xffu;
+      }
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        o.b[ms][0] = *reinterpret_cast<const uint4 *>(pb[ms] + k0);
+        o.b[ms][1] = *reinterpret_cast<const uint4 *>(pb[ms] + k0 + 64);
+        o.sb[ms] = (psb[ms][k0 / 128] >> (8 * gq)) & 0xffu;
+      }
+    };
+    coli_f32x4v acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = coli_f32x4v{0.f, 0.f, 0.f, 0.f};
+    MxOps cur, nxt;
+    load(0, cur);
+    for (int k0 = 0; k0 < K; k0 += kMxK) {
+      load(min(k0 + kMxK, K - kMxK), nxt);  // the last step reloads itself (in bounds)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const coli_i32x8 av = {(int)cur.a[a].x, (int)cur.a[a].y, (int)cur.a[a].z,
+                               (int)cur.a[a].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+          const coli_i32x8 bv = {(int)cur.b[ms][0].x, (int)cur.b[ms][0].y, (int)cur.b[ms][0].z,
+                                 (int)cur.b[ms][0].w, (int)cur.b[ms][1].x, (int)cur.b[ms][1].y,
+                                 (int)cur.b[ms][1].z, (int)cur.b[ms][1].w};
+          // formats: A E2M1 (4), B E4M3 (0); scale byte 0 of each register
+          acc[a * 2 + ms] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              av, bv, acc[a * 2 + ms], 4, 0, 0, (int)cur.sa[a], 0, (int)cur.sb[ms]);
+        }
+      }
+      cur = nxt;
+    }
+
+    if (MODE == kGateUp) {
+      const int I = g.rows;
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const int m = 32 * wm + 16 * ms + r16;
+        float hv[2][4];
+        float amax = 0.0f;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[ns][i] = silu_mul(acc[ns * 2 + ms][i], acc[(2 + ns) * 2 + ms][i]);
+            amax = fmaxf(amax, fabsf(hv[ns][i]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const uint32_t E = mx8_exponent(amax);
+        uint32_t qw[2];
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+          qw[ns] = mx8_code(hv[ns][0], E) | (mx8_code(hv[ns][1], E) << 8) |
+                   (mx8_code(hv[ns][2], E) << 16) | (mx8_code(hv[ns][3], E) << 24);
+        const int ch = it.n0 + 32 * wn;  // first channel of this wave's block
+        if (m < it.ntok && ch < I) {
+          uint8_t *qrow = qh_out + (int64_t)outrow[m] * I + ch;
+          *reinterpret_cast<uint32_t *>(qrow + 4 * gq) = qw[0];
+          *reinterpret_cast<uint32_t *>(qrow + 16 + 4 * gq) = qw[1];
+          if (gq == 0) eh_out[(int64_t)outrow[m] * (I / 32) + ch / 32] = (uint8_t)E;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const int m = 32 * wm + 16 * ms + r16;
+        if (m >= it.ntok) continue;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int n = it.n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * gq;
+          if (n < g.rows)
+            *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
+                make_float4(acc[a * 2 + ms][0], acc[a * 2 + ms][1], acc[a * 2 + ms][2],
+                            acc[a * 2 + ms][3]);
+        }
+      }
+    }
+  }
+}
+
 struct PrefillWs {
   int8_t *qx;
   uint16_t *dx;
@@ -1416,6 +1673,33 @@ int launch_quantize_q8_0(const void *src, int src_dtype, int64_t n, int8_t *q, u
   return hip_status(hipGetLastError());
 }
 
+int launch_quantize_mxfp8(const void *src, int src_dtype, int64_t n, uint8_t *q, uint8_t *e8,
+                          hipStream_t s) {
+  const int64_t nb = n / 32;
+  launch_k(COLI_K_QUANTIZE, quantize_mx_kernel, dim3((unsigned)((nb + kThreads - 1) / kThreads)),
+           dim3(kThreads), 0, s, src, src_dtype, nb, q, e8);
+  return hip_status(hipGetLastError());
+}
+
+int launch_mx_dots(const Layer &L, int expert, int matrix, const uint8_t *qa, const uint8_t *ea,
+                   int T, float *out, hipStream_t s) {
+  GemmArgs g{};
+  g.rs = 1;
+  g.wq = L.q4 + (int64_t)matrix * L.I * L.H / 2;
+  g.ws = L.scales + (int64_t)matrix * L.I * L.H / 64;
+  g.rows = matrix == 2 ? L.H : L.I;
+  g.K = matrix == 2 ? L.I : L.H;
+  g.act = reinterpret_cast<const int8_t *>(qa);
+  g.act_d = reinterpret_cast<const uint16_t *>(ea);
+  const int nn = (g.rows + BR - 1) / BR;
+  const int ntile = (T + BM - 1) / BM;
+  coli_moe_route_t none{};
+  launch_k(COLI_K_BLOCK_DOTS, mxgemm_kernel<kDots>, dim3(grid_for(band_items_host(ntile, nn))),
+           dim3(kThreads), 0, s, g, none, (const int4 *)nullptr, (const int *)nullptr, T, expert,
+           T, 1, nn, L.expert_bytes, L.expert_scales, (uint8_t *)nullptr, (uint8_t *)nullptr, out);
+  return hip_status(hipGetLastError());
+}
+
 namespace {
 
 // The int4 forward on the DMA GEMM (dgemm_layer).
@@ -1469,9 +1753,63 @@ int launch_prefill_dgemm(const Layer &L, const coli_moe_route_t &r, const uint16
 
 }  // namespace
 
+namespace {
+
+// The MX forward (MXFP4 weights, COLI_ACT_MXFP8): MXFP8 of x, plan, the two
+// MX GEMMs (h in MXFP8 between them), combine.
+int launch_prefill_mx(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T,
+                      void *y, int y_dtype, const PrefillWs &w, hipStream_t s) {
+  uint8_t *qx = reinterpret_cast<uint8_t *>(w.qx), *ex = reinterpret_cast<uint8_t *>(w.dx);
+  uint8_t *qh = reinterpret_cast<uint8_t *>(w.qh), *eh = reinterpret_cast<uint8_t *>(w.dh);
+  int rc = launch_quantize_mxfp8(x, COLI_SRC_BF16, (int64_t)T * L.H, qx, ex, s);
+  if (rc) return rc;
+  launch_k(COLI_K_PLAN, plan_kernel, dim3(1), dim3(1024), 0, s, r, T, L.k, L.E, L.S, w.tiles,
+           w.ntiles);
+  if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  const int mt = max_tiles(L, T);
+  {  // gate / up + SwiGLU + MXFP8(h)
+    GemmArgs g{};
+    g.rs = 1;
+    g.wq = L.q4;
+    g.ws = L.scales;
+    g.rows = L.I;
+    g.K = L.H;
+    g.act = reinterpret_cast<const int8_t *>(qx);
+    g.act_d = reinterpret_cast<const uint16_t *>(ex);
+    g.up_offset_q = (int64_t)L.I * L.H / 2;
+    g.up_offset_s = (int64_t)L.I * L.H / 64;
+    const int nn = (L.I + 63) / 64;
+    launch_k(COLI_K_GEMM_GATEUP, mxgemm_kernel<kGateUp>, dim3(grid_for(band_items_host(mt, nn))),
+             dim3(kThreads), 0, s, g, r, (const int4 *)w.tiles, (const int *)w.ntiles, 0, 0, T,
+             L.k, nn, L.expert_bytes, L.expert_scales, qh, eh, (float *)nullptr);
+    if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  }
+  {  // down
+    GemmArgs g{};
+    g.rs = 1;
+    g.wq = L.q4 + (int64_t)L.I * L.H;
+    g.ws = L.scales + (int64_t)2 * L.I * L.H / 64;
+    g.rows = L.H;
+    g.K = L.I;
+    g.act = reinterpret_cast<const int8_t *>(qh);
+    g.act_d = reinterpret_cast<const uint16_t *>(eh);
+    const int nn = (L.H + BR - 1) / BR;
+    launch_k(COLI_K_GEMM_DOWN, mxgemm_kernel<kDown>, dim3(grid_for(band_items_host(mt, nn))),
+             dim3(kThreads), 0, s, g, r, (const int4 *)w.tiles, (const int *)w.ntiles, 0, 0, T,
+             L.k, nn, L.expert_bytes, L.expert_scales, (uint8_t *)nullptr, (uint8_t *)nullptr,
+             w.o);
+    if (hipGetLastError() != hipSuccess) return COLI_E_HIP;
+  }
+  launch_combine(w.o, r, T, L.H, L.k, L.S, y, y_dtype, s);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
 int launch_prefill(const Layer &L, const coli_moe_route_t &r, const uint16_t *x, int T, void *y,
                    int y_dtype, void *ws, hipStream_t s) {
   const PrefillWs w = carve(L, T, ws);
+  if (L.f4 && (L.flags & COLI_ACT_MXFP8)) return launch_prefill_mx(L, r, x, T, y, y_dtype, w, s);
   if (dgemm_layer(L)) return launch_prefill_dgemm(L, r, x, T, y, y_dtype, w, s);
   int rc = launch_quantize_q8_0(x, COLI_SRC_BF16, (int64_t)T * L.H, w.qx, w.dx, s);
   if (rc) return rc;

@@ -51,10 +51,12 @@ class LayerSpec:
     routed_scale: float = 1.0
     int8: bool = False   # one int8 byte per weight instead of a nibble
     mxfp4: bool = False  # E2M1 nibbles with one E8M0 scale byte per 32 weights
+    mx_act: bool = False  # prefill activations in MXFP8 (MXFP4 layers; flag bit 1 << 16)
 
     @property
     def flags(self) -> int:
-        return (1 if self.sigmoid else 0) | (256 if self.renorm else 0)
+        return (1 if self.sigmoid else 0) | (256 if self.renorm else 0) | (
+            1 << 16 if self.mx_act else 0)
 
     @property
     def weights(self) -> str:

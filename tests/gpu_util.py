@@ -217,3 +217,87 @@ def check_prefill_output(spec, L, g, x, y, tokens, tol=REL_TOL):
           flush=True)
     assert np.all(err <= tol * denom + budget), float(np.max(over))
     return rel_err(yv, ref), int(np.count_nonzero(err > tol * denom))
+
+
+def mx_flip_budget(spec: synth.LayerSpec, L: coli.Layer, topk_idx: np.ndarray,
+                   topk_w: np.ndarray, x: torch.Tensor, tokens, band=2.0 ** -12):
+    """Oracle MX-path output of `tokens` and, per output element, the most
+    that MXFP8 decisions of h sitting on a boundary can move it.
+
+    Both sides quantise h (fp32) to MXFP8; the GPU's h differs from the
+    oracle's by the MX instruction's own rounding (up to ~2^-14 of a
+    block's largest terms when its E4M3 values span a wide range, measured)
+    and the SwiGLU's exp, so an E4M3 code whose scaled value lies within `band`
+    (relative) of a rounding midpoint may round the other way (one code step
+    of that binade), and a block whose maximum lies within `band` of a power
+    of two may take the neighbouring shared exponent (every element then
+    moves by at most two code steps of its own magnitude).  A change of dh in
+    h[n] moves down output m by at most |dh| * |W_down[m, n]|.  Returns
+    (ref [len(tokens), H], budget [same])."""
+    from bruteforce import E2M1, e4m3_table
+    tokens = list(tokens)
+    H, I, k, S = spec.hidden, spec.inter, spec.top_k, spec.n_shared
+    idx = topk_idx.reshape(-1, k)[tokens]
+    w = topk_w.reshape(-1, k)[tokens]
+    used = sorted(set(int(e) for e in idx.ravel()))
+    experts = used + ([spec.n_experts] if S else [])
+    q4h, sch = synth.expert_slice(spec, L.q4, L.scales, experts)
+    remap = np.zeros(spec.n_experts, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    xb = synth.bf16_bits(x)[tokens]
+    ref, h = oracle.forward_prefill_mx(H, I, len(used), S, k, q4h, sch, remap[idx], w, xb,
+                                       want_h=True)
+    tab = e4m3_table()
+    mids = 0.5 * (tab[:-1] + tab[1:])
+    mb, ms = I * H // 2, I * H // 32
+    eb, es = 3 * mb, 3 * ms
+    budget = np.zeros((len(tokens), H))
+    for ti in range(len(tokens)):
+        for j in range(k + S):
+            le = int(remap[idx[ti, j]]) if j < k else len(used)
+            wj = float(np.float32(w[ti, j])) if j < k else 1.0
+            hv = h[ti, j].astype(np.float64).reshape(I // 32, 32)
+            amax = np.abs(hv).max(axis=1)
+            with np.errstate(divide="ignore"):
+                fl = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))), 0.0)
+            X = np.clip(fl - 8 + 127, 0, 254) - 127
+            m = np.abs(hv) * np.exp2(-X)[:, None]
+            near = np.min(np.abs(m[..., None] - mids), axis=-1)
+            with np.errstate(divide="ignore"):
+                e = np.floor(np.log2(np.where(m > 0, m, 1.0)))
+            step = np.where(m < 2.0 ** -6, 2.0 ** -9, np.exp2(e - 3)) * np.exp2(X)[:, None]
+            # the instruction's error follows the magnitude of a dot's terms, not its
+            # result: a floor of 2^-4 of the band at the block's largest value
+            code_risk = (near < band * np.maximum(m, 2.0 ** -4 * m.max(axis=1, keepdims=True))) & (
+                m < 448.0)
+            pow2 = np.exp2(fl)
+            exp_risk = (amax > 0) & ((np.abs(amax - pow2) < band * amax)
+                                     | (np.abs(amax - 2 * pow2) < band * amax))
+            col = (code_risk * step + exp_risk[:, None] * 2.0 * step).reshape(I)
+            cols = np.flatnonzero(col)
+            if cols.size == 0:
+                continue
+            base = le * eb + 2 * mb
+            b = np.asarray(q4h[base:base + mb], np.uint8).reshape(H, I // 2)[:, cols // 2]
+            nib = np.where(cols % 2 == 1, b >> 4, b & 15).astype(np.int64)
+            sc = np.asarray(sch[le * es + 2 * ms:le * es + 3 * ms], np.uint8).reshape(H, I // 32)
+            wabs = E2M1[nib & 7] * np.exp2(sc[:, cols // 32].astype(np.float64) - 127.0)
+            budget[ti] += wj * (wabs @ col[cols])
+    return ref, budget
+
+
+def check_prefill_output_mx(spec, L, g, x, y, tokens, tol=REL_TOL):
+    """check_prefill_output for the MX path (mx_flip_budget)."""
+    tokens = list(tokens)
+    ref, budget = mx_flip_budget(spec, L, g["topk_idx"], g["topk_w"], x, tokens)
+    yv = y.float().cpu().numpy()[tokens].astype(np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    denom = np.maximum(np.abs(ref), rms)
+    err = np.abs(yv - ref)
+    over = (err - budget) / denom
+    worst = np.unravel_index(int(np.argmax(over)), over.shape)
+    print("  worst element: token %d, column %d: |err| / scale %.3g, budget / scale %.3g"
+          % (tokens[worst[0]], worst[1], err[worst] / denom[worst], budget[worst] / denom[worst]),
+          flush=True)
+    assert np.all(err <= tol * denom + budget), float(np.max(over))
+    return rel_err(yv, ref), int(np.count_nonzero(err > tol * denom))

@@ -39,12 +39,12 @@ def test_library_exports_every_declared_symbol():
     assert coli.coli_moe_strerror(-3) == "workspace too small"
 
 
-def _layer(**kw):
+def _layer(mxfp4=False, **kw):
     args = dict(hidden=2048, inter=512, n_experts=256, n_shared=1, top_k=8,
                 flags=coli.COLI_ROUTE_SIGMOID | coli.COLI_ROUTE_RENORM, q4=FAKE, scales=FAKE)
     args.update(kw)
     return coli.Layer(args["hidden"], args["inter"], args["n_experts"], args["n_shared"],
-                      args["top_k"], args["flags"], args["q4"], args["scales"])
+                      args["top_k"], args["flags"], args["q4"], args["scales"], mxfp4=mxfp4)
 
 
 class _FakeRoute:
@@ -163,6 +163,39 @@ def test_route_quantize_dots_reject_bad_calls():
     assert bd(ctypes.byref(L.c), 257, 0, FAKE, 4, FAKE, None) == -1   # expert out of range
     assert bd(ctypes.byref(L.c), 0, 3, FAKE, 4, FAKE, None) == -1     # matrix out of range
     assert bd(ctypes.byref(L.c), 0, 0, FAKE, 0, FAKE, None) == -1     # T = 0
+
+
+def test_mx_path_rejects_bad_calls():
+    """MXFP8 activations pair with MXFP4 weights only; the MX prefill needs H
+    and I multiples of 128; the MX debug calls check their arguments."""
+    lib = binding.raw_library()
+    r = ctypes.byref(_FakeRoute().c)
+    big = 1 << 40
+    mx = coli.COLI_ROUTE_SIGMOID | coli.COLI_ACT_MXFP8
+    pre = lib.coli_moe_forward_prefill
+    assert pre(ctypes.byref(_layer(flags=mx).c), r, FAKE, 4, FAKE, 0, FAKE, big, None) == -1
+    odd = _layer(mxfp4=True, flags=mx, hidden=192, inter=320)
+    assert pre(ctypes.byref(odd.c), r, FAKE, 4, FAKE, 0, FAKE, big, None) == -2
+    # decode ignores the flag: an int4-style argument error still comes first
+    assert lib.coli_moe_forward_decode(ctypes.byref(odd.c), r, FAKE + 2, 1, FAKE, 0, FAKE, big,
+                                       None) == -4
+    q = lib.coli_moe_quantize_mxfp8
+    assert q(FAKE, 0, 33, FAKE, FAKE, None) == -1            # n % 32
+    assert q(FAKE, 2, 64, FAKE, FAKE, None) == -1            # dtype
+    assert q(None, 0, 64, FAKE, FAKE, None) == -1            # src NULL
+    assert q(FAKE + 2, 0, 64, FAKE, FAKE, None) == -4        # src align
+    assert q(FAKE, 0, (1 << 34) + 32, FAKE, FAKE, None) == -1
+    d = lib.coli_moe_mx_dots
+    f4 = _layer(mxfp4=True)
+    assert d(ctypes.byref(_layer().c), 0, 0, FAKE, FAKE, 4, FAKE, None) == -1   # not MXFP4
+    assert d(ctypes.byref(f4.c), 257, 0, FAKE, FAKE, 4, FAKE, None) == -1       # expert
+    assert d(ctypes.byref(f4.c), 0, 3, FAKE, FAKE, 4, FAKE, None) == -1         # matrix
+    assert d(ctypes.byref(f4.c), 0, 0, FAKE, FAKE, 0, FAKE, None) == -1         # T
+    assert d(ctypes.byref(f4.c), 0, 0, FAKE, FAKE, 4097, FAKE, None) == -1
+    assert d(ctypes.byref(f4.c), 0, 0, FAKE + 8, FAKE, 4, FAKE, None) == -4     # q align
+    assert d(ctypes.byref(f4.c), 0, 0, FAKE, FAKE + 2, 4, FAKE, None) == -4     # e align
+    assert d(ctypes.byref(_layer(mxfp4=True, hidden=192).c), 0, 0, FAKE, FAKE, 4, FAKE,
+             None) == -2                                                        # K % 128
 
 
 def test_route_hidden_rejects_bad_calls():
