@@ -77,7 +77,7 @@ enum {
  * the GEMMs) to MXFP8 -- OCP FP8 E4M3 codes with one E8M0 scale per 32
  * values, see coli_moe_quantize_mxfp8 -- instead of Q8_0, and runs both
  * GEMMs on gfx950's MX matrix cores, which apply the weight and activation
- * block scales themselves.  Needs H and I multiples of 128
+ * block scales themselves.  Needs H and I multiples of 256
  * (COLI_E_UNSUPPORTED otherwise).  Decode ignores the flag. */
 enum { COLI_ACT_MXFP8 = 1u << 16 };
 
@@ -394,7 +394,7 @@ int coli_moe_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t n,
  *               * sum_{k in block b} e2m1(w[n][k]) * e4m3(a[t][k])
  * accumulated in fp32 by the hardware (its order is not specified).
  *  matrix 0 = gate, 1 = up (K = H, rows = I), 2 = down (K = I, rows = H);
- *  K must be a multiple of 128 (COLI_E_UNSUPPORTED otherwise).
+ *  K must be a multiple of 256 (COLI_E_UNSUPPORTED otherwise).
  *  q_act [T*K] E4M3 codes, e_act [T*K/32] E8M0, T in [1, 4096];
  *  out [T*rows] fp32.  COLI_E_INVALID for layers that are not MXFP4. */
 int coli_moe_mx_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t matrix,

@@ -90,8 +90,8 @@ int check_forward(const coli_moe_layer_t *layer, const coli_moe_route_t *route,
   if ((rc = check_route(route))) return rc;
   if ((rc = check_tokens(*L, T, entry == COLI_ENTRY_DECODE ? kMaxDecodeT : kMaxT))) return rc;
   if (entry == COLI_ENTRY_DECODE && L->I > kMaxDecodeInter) return COLI_E_UNSUPPORTED;
-  // the MX prefill steps through k 128 at a time
-  if (entry != COLI_ENTRY_DECODE && (L->flags & COLI_ACT_MXFP8) && (L->H % 128 || L->I % 128))
+  // the MX prefill stages k 256 at a time
+  if (entry != COLI_ENTRY_DECODE && (L->flags & COLI_ACT_MXFP8) && (L->H % 256 || L->I % 256))
     return COLI_E_UNSUPPORTED;
   if (!x || !y) return COLI_E_INVALID;
   if (y_dtype != COLI_OUT_BF16 && y_dtype != COLI_OUT_F32) return COLI_E_INVALID;
@@ -319,7 +319,7 @@ int coli_moe_mx_dots(const coli_moe_layer_t *layer, int32_t expert, int32_t matr
   if (!L.f4) return COLI_E_INVALID;
   if (expert < 0 || expert >= L.E + L.S || matrix < 0 || matrix > 2) return COLI_E_INVALID;
   if (T < 1 || T > 4096 || !q_act || !e_act || !out) return COLI_E_INVALID;
-  if ((matrix == 2 ? L.I : L.H) % 128) return COLI_E_UNSUPPORTED;
+  if ((matrix == 2 ? L.I : L.H) % 256) return COLI_E_UNSUPPORTED;
   if (!aligned(q_act, 16) || !aligned(e_act, 4) || !aligned(out, 16)) return COLI_E_ALIGN;
   return launch_mx_dots(L, expert, matrix, q_act, e_act, T, out,
                         reinterpret_cast<hipStream_t>(stream));

@@ -1448,159 +1448,214 @@ __global__ void __launch_bounds__(kThreads) quantize_mx_kernel(const void *__res
   e8[b] = (uint8_t)E;
 }
 
-// One K step of a wave's operands: 4 weight row tiles (16 bytes of E2M1
-// codes and a scale byte per lane) and 2 token tiles (32 bytes of E4M3
-// codes and a scale byte per lane).
-struct MxOps {
-  uint4 a[4];
-  uint32_t sa[4];
-  uint4 b[2][2];
-  uint32_t sb[2];
+// Stages filled by DMA (global_load_lds), as in dgemm_kernel: one stage
+// holds 256 k of the item's 128 weight rows (E2M1, 16 KB) and of its 64
+// token rows (E4M3, 16 KB), with both sides' E8M0 scale bytes.  Layouts are
+// XOR-swizzled at 16-byte granularity so that every DMA instruction moves
+// whole 128-byte lines and every 16-byte operand read of a half-wavefront
+// hits distinct banks: weight row r keeps 16-byte chunk c at c ^ ((r>>1)&7),
+// token t keeps chunk j at j ^ (t & 15).
+struct MStage {
+  uint4 w[BR * 8];   // [row][chunk]: 32 E2M1 codes = one 32-block of one row
+  uint4 a[BM * 16];  // [token][chunk]: 16 E4M3 codes
+  uint2 sw[BR];      // [row]: E8M0 of the stage's 8 blocks
+  uint2 sa[BM];      // [token]: E8M0 of the stage's 8 blocks
 };
 
-// Work items, tiles and wave roles as gemm_kernel: wave (wn, wm) computes
-// weight row tiles wave_row_tile(wn, 0..3) against token tiles 2wm, 2wm+1.
-//  gate/up: epilogue h = silu(g) * u, then MXFP8 of h per 32 channels (one
-//           wave holds the 32 channels of one block for its 32 tokens).
-//  down   : fp32 o rows.   dots: fp32 [T][rows] of one matrix (debug).
-template <int MODE>
-__global__ void __launch_bounds__(kThreads) mxgemm_kernel(
-    GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
-    const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
-    int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
-    uint8_t *__restrict__ qh_out, uint8_t *__restrict__ eh_out, float *__restrict__ o_out) {
-  __shared__ int rowid[BM];
-  __shared__ int outrow[BM];
+// One item from DMA-filled stages.  Wave wv computes weight rows
+// [16wv, 16wv+16) and [64+16wv, 64+16wv+16) (gate/up: gate and up of the
+// same 16 channels) against each 16-token subtile that holds a token (NTS).
+template <int MODE, int NTS>
+COLI_DEV void mxd_item(const GemmArgs &g, const Item &it, const int *rowid, const int *outrow,
+                       MStage &B0, MStage &B1, float (*xch)[4][16], uint8_t *qh_out,
+                       uint8_t *eh_out, float *o_out) {
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wid >> 1, wm = wid & 1;
-  const int r16 = lane & 15, gq = lane >> 4;
-  const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
-  const int items = band_items(ntiles, n_ntiles);
-  const int K = g.K;
-  const int G = gridDim.x;
-  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kq = lane >> 4, lr = lane & 15;
+  const int nst = g.K / kSK;
   const uint8_t *act = reinterpret_cast<const uint8_t *>(g.act);
   const uint8_t *act_e = reinterpret_cast<const uint8_t *>(g.act_d);
+  // ---- DMA sources of this lane
+  const uint8_t *sw_src, *sa_src, *w_src[4], *a_src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * wv + 8 * j + (lane >> 3);  // instruction 4wv + j: rows 8(4wv+j)..+7
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    const uint8_t *q;
+    const uint16_t *unused;
+    weight_row<MODE == kDots ? kDown : MODE>(g, it.n0, row, q, unused);
+    w_src[j] = q + 16 * chunk;
+    const int t = 16 * wv + 4 * j + (lane >> 4);   // tokens 4(4wv+j)..+3
+    a_src[j] = act + (int64_t)rowid[t] * g.K + 16 * ((lane & 15) ^ (t & 15));
+  }
+  {
+    const int row = 32 * wv + (lane >> 1);
+    const uint8_t *unused;
+    const uint16_t *sc;
+    weight_row<MODE == kDots ? kDown : MODE>(g, it.n0, row, unused, sc);
+    sw_src = reinterpret_cast<const uint8_t *>(sc) + 4 * (lane & 1);
+    const int t = 32 * (wv & 1) + (lane >> 1);
+    sa_src = act_e + (int64_t)rowid[t] * (g.K / 32) + 4 * (lane & 1);
+  }
+  const bool tok_live = wv < NTS;              // tokens 16wv..16wv+15 hold one
+  const bool sa_live = wv < 2 && 2 * wv < NTS;  // waves 0, 1 move 32 tokens' scales each
+  // DMA instruction p (0..9) of stage st
+  auto issue_part = [&](MStage &B, int st, int p) {
+    if (p < 4) {
+      dma16(w_src[p] + st * (kSK / 2), &B.w[(4 * wv + p) * 64]);
+    } else if (p < 8) {
+      if (tok_live) dma16(a_src[p - 4] + st * kSK, &B.a[(4 * wv + p - 4) * 64]);
+    } else if (p == 8) {
+      dma4(sw_src + st * 8, reinterpret_cast<uint8_t *>(B.sw) + 256 * wv);
+    } else if (sa_live) {
+      dma4(sa_src + st * 8, reinterpret_cast<uint8_t *>(B.sa) + 256 * wv);
+    }
+  };
 
+  coli_f32x4v acc[2][NTS];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) acc[rs][ts] = coli_f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  const int rA = 16 * wv + lr;  // row of tile rs = 0 (tile 1: + 64, same swizzle)
+  const uint32_t offA = rA * 128, fA = (rA >> 1) & 7;
+  // one stage: two 128-k steps; stage `nxt`'s DMA goes out along the way
+  auto compute = [&](const MStage &B, MStage &N, int nxt) {
+    uint2 swv[2], sav[NTS];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) swv[rs] = B.sw[rA + 64 * rs];
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) sav[ts] = B.sa[16 * ts + lr];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (nxt >= 0) {
+#pragma unroll
+        for (int p = 5 * s; p < 5 * s + 5; ++p) issue_part(N, nxt, p);
+      }
+      coli_i32x8 av[2], bv[NTS];
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const char *>(B.w) + offA + rs * 64 * 128 + 16 * ((4 * s + kq) ^ fA));
+        av[rs] = coli_i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int ts = 0; ts < NTS; ++ts) {
+        const int t = 16 * ts + lr;
+        const char *row = reinterpret_cast<const char *>(B.a) + t * 256;
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(row + 16 * ((8 * s + kq) ^ (t & 15)));
+        const uint4 v1 = *reinterpret_cast<const uint4 *>(row + 16 * ((8 * s + 4 + kq) ^ (t & 15)));
+        bv[ts] = coli_i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                            (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      }
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const uint32_t sa = ((s ? swv[rs].y : swv[rs].x) >> (8 * kq)) & 0xffu;
+#pragma unroll
+        for (int ts = 0; ts < NTS; ++ts) {
+          const uint32_t sb = ((s ? sav[ts].y : sav[ts].x) >> (8 * kq)) & 0xffu;
+          // formats: A E2M1 (4), B E4M3 (0); scale byte 0 of each register
+          acc[rs][ts] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              av[rs], bv[ts], acc[rs][ts], 4, 0, 0, (int)sa, 0, (int)sb);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < 10; ++p) issue_part(B0, 0, p);
+  wait_dma();
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    compute(B0, B1, st + 1 < nst ? st + 1 : -1);
+    wait_dma();
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    compute(B1, B0, st + 2 < nst ? st + 2 : -1);
+    wait_dma();
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  if (MODE == kGateUp) {
+    // h = silu(g) * u for channels n0 + 16wv + 4kq + i; MXFP8 of h per 32
+    // channels: waves 2p and 2p+1 hold the two halves of block p
+    float hv[NTS][4], am[NTS];
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hv[ts][i] = silu_mul(acc[0][ts][i], acc[1][ts][i]);
+        a = fmaxf(a, fabsf(hv[ts][i]));
+      }
+      a = fmaxf(a, __shfl_xor(a, 16, 64));
+      a = fmaxf(a, __shfl_xor(a, 32, 64));
+      am[ts] = a;
+      if (kq == 0) xch[wv][ts][lr] = a;
+    }
+    __syncthreads();
+    const int I = g.rows;
+    const int ch0 = it.n0 + 16 * wv;
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      const uint32_t E = mx8_exponent(fmaxf(am[ts], xch[wv ^ 1][ts][lr]));
+      const uint32_t packed = mx8_code(hv[ts][0], E) | (mx8_code(hv[ts][1], E) << 8) |
+                              (mx8_code(hv[ts][2], E) << 16) | (mx8_code(hv[ts][3], E) << 24);
+      const int m = 16 * ts + lr;
+      if (m < it.ntok && ch0 < I) {
+        const int64_t orow = outrow[m];
+        *reinterpret_cast<uint32_t *>(qh_out + orow * I + ch0 + 4 * kq) = packed;
+        if ((wv & 1) == 0 && kq == 0) eh_out[orow * (I / 32) + ch0 / 32] = (uint8_t)E;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) {
+      const int m = 16 * ts + lr;
+      if (m >= it.ntok) continue;
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const int n = it.n0 + 16 * wv + 64 * rs + 4 * kq;
+        if (n < g.rows)
+          *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
+              make_float4(acc[rs][ts][0], acc[rs][ts][1], acc[rs][ts][2], acc[rs][ts][3]);
+      }
+    }
+  }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mxgemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
+              const int *__restrict__ ntiles_p, int fixed_ntok, int fixed_expert, int T, int k,
+              int n_ntiles, int64_t expert_stride_q, int64_t expert_stride_s,
+              uint8_t *__restrict__ qh_out, uint8_t *__restrict__ eh_out,
+              float *__restrict__ o_out) {
+  __shared__ MStage B0;
+  __shared__ MStage B1;
+  __shared__ int rowid[BM];
+  __shared__ int outrow[BM];
+  __shared__ float xch[4][4][16];
+  const int ntiles = tiles ? ntiles_p[0] : (fixed_ntok + BM - 1) / BM;
+  const int items = band_items(ntiles, n_ntiles);
+  const int G = gridDim.x;
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
   for (int item = vid; item < items; item += G) {
     int tile, ntile;
     item_coords(item, n_ntiles, tile, ntile);
     if (tile >= ntiles) continue;
     const Item it = setup_item<MODE>(tile, ntile, tiles, fixed_ntok, fixed_expert, r, T, k,
                                      rowid, outrow);
-    const uint8_t *wq = g.wq + (int64_t)it.expert * expert_stride_q;
-    const uint8_t *ws = reinterpret_cast<const uint8_t *>(g.ws + (int64_t)it.expert * expert_stride_s);
-    // this lane's sources: weight rows (clamped to row 0 past the matrix)
-    const uint8_t *pa[4];
-    const uint32_t *psa[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t = wave_row_tile<MODE>(wn, a);
-      int n;
-      int64_t oq = 0, os = 0;
-      if (MODE == kGateUp) {
-        n = it.n0 + 16 * (t & 3) + r16;
-        if (t >= 4) {
-          oq = g.up_offset_q;
-          os = 2 * g.up_offset_s;  // 16-bit units -> bytes
-        }
-      } else {
-        n = it.n0 + 16 * t + r16;
-      }
-      if (n >= g.rows) n = 0;
-      pa[a] = wq + oq + (int64_t)n * (K / 2) + 16 * gq;
-      psa[a] = reinterpret_cast<const uint32_t *>(ws + os + (int64_t)n * (K / 32));
-    }
-    const uint8_t *pb[2];
-    const uint32_t *psb[2];
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const int row = rowid[32 * wm + 16 * ms + r16];
-      pb[ms] = act + (int64_t)row * K + 16 * gq;
-      psb[ms] = reinterpret_cast<const uint32_t *>(act_e + (int64_t)row * (K / 32));
-    }
-    auto load = [&](int k0, MxOps &o) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        o.a[a] = *reinterpret_cast<const uint4 *>(pa[a] + k0 / 2);
-        o.sa[a] = (psa[a][k0 / 128] >> (8 * gq)) & 0xffu;
-      }
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
-        o.b[ms][0] = *reinterpret_cast<const uint4 *>(pb[ms] + k0);
-        o.b[ms][1] = *reinterpret_cast<const uint4 *>(pb[ms] + k0 + 64);
-        o.sb[ms] = (psb[ms][k0 / 128] >> (8 * gq)) & 0xffu;
-      }
-    };
-    coli_f32x4v acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = coli_f32x4v{0.f, 0.f, 0.f, 0.f};
-    MxOps cur, nxt;
-    load(0, cur);
-    for (int k0 = 0; k0 < K; k0 += kMxK) {
-      load(min(k0 + kMxK, K - kMxK), nxt);  // the last step reloads itself (in bounds)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const coli_i32x8 av = {(int)cur.a[a].x, (int)cur.a[a].y, (int)cur.a[a].z,
-                               (int)cur.a[a].w, 0, 0, 0, 0};
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-          const coli_i32x8 bv = {(int)cur.b[ms][0].x, (int)cur.b[ms][0].y, (int)cur.b[ms][0].z,
-                                 (int)cur.b[ms][0].w, (int)cur.b[ms][1].x, (int)cur.b[ms][1].y,
-                                 (int)cur.b[ms][1].z, (int)cur.b[ms][1].w};
-          // formats: A E2M1 (4), B E4M3 (0); scale byte 0 of each register
-          acc[a * 2 + ms] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av, bv, acc[a * 2 + ms], 4, 0, 0, (int)cur.sa[a], 0, (int)cur.sb[ms]);
-        }
-      }
-      cur = nxt;
-    }
-
-    if (MODE == kGateUp) {
-      const int I = g.rows;
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
-        const int m = 32 * wm + 16 * ms + r16;
-        float hv[2][4];
-        float amax = 0.0f;
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hv[ns][i] = silu_mul(acc[ns * 2 + ms][i], acc[(2 + ns) * 2 + ms][i]);
-            amax = fmaxf(amax, fabsf(hv[ns][i]));
-          }
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const uint32_t E = mx8_exponent(amax);
-        uint32_t qw[2];
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-          qw[ns] = mx8_code(hv[ns][0], E) | (mx8_code(hv[ns][1], E) << 8) |
-                   (mx8_code(hv[ns][2], E) << 16) | (mx8_code(hv[ns][3], E) << 24);
-        const int ch = it.n0 + 32 * wn;  // first channel of this wave's block
-        if (m < it.ntok && ch < I) {
-          uint8_t *qrow = qh_out + (int64_t)outrow[m] * I + ch;
-          *reinterpret_cast<uint32_t *>(qrow + 4 * gq) = qw[0];
-          *reinterpret_cast<uint32_t *>(qrow + 16 + 4 * gq) = qw[1];
-          if (gq == 0) eh_out[(int64_t)outrow[m] * (I / 32) + ch / 32] = (uint8_t)E;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
-        const int m = 32 * wm + 16 * ms + r16;
-        if (m >= it.ntok) continue;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int n = it.n0 + 16 * wave_row_tile<MODE>(wn, a) + 4 * gq;
-          if (n < g.rows)
-            *reinterpret_cast<float4 *>(o_out + (int64_t)outrow[m] * g.rows + n) =
-                make_float4(acc[a * 2 + ms][0], acc[a * 2 + ms][1], acc[a * 2 + ms][2],
-                            acc[a * 2 + ms][3]);
-        }
-      }
+    GemmArgs ge = g;
+    ge.wq = g.wq + (int64_t)it.expert * expert_stride_q;
+    ge.ws = g.ws + (int64_t)it.expert * expert_stride_s;
+    switch ((it.ntok + 15) >> 4) {
+      case 1: mxd_item<MODE, 1>(ge, it, rowid, outrow, B0, B1, xch, qh_out, eh_out, o_out); break;
+      case 2: mxd_item<MODE, 2>(ge, it, rowid, outrow, B0, B1, xch, qh_out, eh_out, o_out); break;
+      case 3: mxd_item<MODE, 3>(ge, it, rowid, outrow, B0, B1, xch, qh_out, eh_out, o_out); break;
+      default: mxd_item<MODE, 4>(ge, it, rowid, outrow, B0, B1, xch, qh_out, eh_out, o_out); break;
     }
   }
 }

@@ -167,7 +167,7 @@ def test_route_quantize_dots_reject_bad_calls():
 
 def test_mx_path_rejects_bad_calls():
     """MXFP8 activations pair with MXFP4 weights only; the MX prefill needs H
-    and I multiples of 128; the MX debug calls check their arguments."""
+    and I multiples of 256; the MX debug calls check their arguments."""
     lib = binding.raw_library()
     r = ctypes.byref(_FakeRoute().c)
     big = 1 << 40
@@ -195,7 +195,7 @@ def test_mx_path_rejects_bad_calls():
     assert d(ctypes.byref(f4.c), 0, 0, FAKE + 8, FAKE, 4, FAKE, None) == -4     # q align
     assert d(ctypes.byref(f4.c), 0, 0, FAKE, FAKE + 2, 4, FAKE, None) == -4     # e align
     assert d(ctypes.byref(_layer(mxfp4=True, hidden=192).c), 0, 0, FAKE, FAKE, 4, FAKE,
-             None) == -2                                                        # K % 128
+             None) == -2                                                        # K % 256
 
 
 def test_route_hidden_rejects_bad_calls():

@@ -67,8 +67,8 @@ def _mx_acts(T, K, g):
 
 
 @pytest.mark.parametrize("spec,T,experts", [
-    (synth.LayerSpec(256, 128, 4, 1, 2, True, True, mxfp4=True), 5, (0, 4)),
-    (synth.LayerSpec(384, 640, 3, 1, 2, True, True, mxfp4=True), 70, (1, 3)),
+    (synth.LayerSpec(256, 256, 4, 1, 2, True, True, mxfp4=True), 5, (0, 4)),
+    (synth.LayerSpec(512, 768, 3, 1, 2, True, True, mxfp4=True), 70, (1, 3)),
     (synth.LayerSpec(2048, 1024, 4, 1, 2, True, True, mxfp4=True), 129, (2,)),
     (synth.WORKLOADS["glm"].spec, 64, (17,)),
 ])
@@ -126,9 +126,10 @@ def _case(spec, T, seed=0, zipf=0.0, tokens=None, cover=None):
 
 
 @pytest.mark.parametrize("spec,T", [
-    (synth.LayerSpec(256, 128, 8, 1, 2, sigmoid=True, renorm=True), 70),
-    (synth.LayerSpec(384, 640, 6, 0, 3, sigmoid=False, renorm=True), 129),
-    (synth.LayerSpec(128, 128, 1, 1, 1, sigmoid=False, renorm=False), 1),
+    (synth.LayerSpec(256, 256, 8, 1, 2, sigmoid=True, renorm=True), 70),
+    (synth.LayerSpec(768, 512, 8, 1, 2, sigmoid=True, renorm=True), 70),   # odd stage count
+    (synth.LayerSpec(512, 768, 6, 0, 3, sigmoid=False, renorm=True), 129),
+    (synth.LayerSpec(256, 256, 1, 1, 1, sigmoid=False, renorm=False), 1),
 ])
 def test_mx_prefill_edge_shapes(spec, T):
     _case(_mx(spec), T, seed=3, zipf=0.6)
@@ -160,6 +161,6 @@ def test_mx_prefill_unsupported_shape():
     spec = synth.LayerSpec(192, 320, 6, 1, 2, sigmoid=True, renorm=True, mxfp4=True, mx_act=True)
     L = gpu_layer(spec)
     r = run_route(L, synth.make_logits(spec, 4).cuda())
-    with pytest.raises(coli.ColiError) as e:   # H, I not multiples of 128
+    with pytest.raises(coli.ColiError) as e:   # H, I not multiples of 256
         forward(L, r, synth.make_x(spec, 4).cuda(), "prefill")
     assert e.value.status == coli.binding.COLI_E_UNSUPPORTED
