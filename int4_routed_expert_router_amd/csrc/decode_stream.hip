@@ -59,17 +59,12 @@ COLI_DEV int value_index(int lane) {
   return idx;
 }
 
-// Which slots a launch computes: every slot of a one-token batch (kAll1);
-// in a larger batch, the slots holding exactly one token, with the same
-// single-token code (kSingles), or the others (kMulti), or every slot with
-// the general code (kAllN).  A slot's tokens get the same arithmetic
-// whichever launch computes them.
-enum { kAll1 = 0, kSingles = 1, kMulti = 2, kAllN = 3 };
-
-// Whether a batch of several tokens splits its single-token slots off into a
-// launch of their own: it pays where a slot's weights are large (measured on
-// H 6144, I 2048); on small layers (I 512) the extra launch costs more.
-inline bool split_singles(const Layer &L) { return L.I >= 2048; }
+// Which slots a kernel's code computes: every slot of a one-token batch
+// (kAll1); in a larger batch, the slots holding exactly one token, with the
+// same single-token code (kSingles), or the others with the general code
+// (kMulti).  A slot's tokens get the same arithmetic whichever launch
+// computes them.
+enum { kAll1 = 0, kSingles = 1, kMulti = 2 };
 
 // Union slot `slot`: slots 0 .. S-1 are the shared expert (all T tokens, rows
 // T*k + t), then one slot per routed expert of the union (counts[e] tokens,
@@ -169,9 +164,8 @@ COLI_DEV void store_h_pair(float *row, int n, float h) {
 // LDS holds tg tokens: tg x 4 x NCH quads of paired bf16, then tg x NCH
 // chunk biases.
 template <int CPL, int RPW, int MODE, class C>
-__global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
-    Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
-    float *__restrict__ h_out) {
+COLI_DEV void gateup_body(Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T,
+                          int tg, float *__restrict__ h_out) {
   constexpr bool ONE = MODE == kAll1 || MODE == kSingles;  // one token in the slot
   constexpr int NCH = 64 * CPL;
   extern __shared__ uint4 smem[];
@@ -289,6 +283,28 @@ __global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
         store_h_pair<C>(h_out + (int64_t)(sl.pos0 + g0 + ti) * I, n0 + vi / 2, silu_mul(tot, up));
     }
   }
+}
+
+template <int CPL, int RPW, int MODE, class C>
+__global__ void __launch_bounds__(kThreads) gateup_stream_kernel(
+    Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
+    float *__restrict__ h_out) {
+  gateup_body<CPL, RPW, MODE, C>(L, r, x, T, tg, h_out);
+}
+
+// Every slot of a batch of several tokens in one launch: a workgroup whose
+// slot holds one token runs the one-token code, the others the general code
+// (each slot's arithmetic is that of the launch mode of its own code).
+template <int CPL, int RPW, class C>
+__global__ void __launch_bounds__(kThreads) gateup_mixed_kernel(
+    Layer L, coli_moe_route_t r, const uint16_t *__restrict__ x, int T, int tg,
+    float *__restrict__ h_out) {
+  const int slot = blockIdx.x * kWaves / (L.I / RPW);  // the workgroup's slot
+  if (slot >= L.S + r.n_union[0]) return;
+  if (slot >= L.S && r.counts[r.union_ids[slot - L.S]] == 1)
+    gateup_body<CPL, RPW, kSingles, C>(L, r, x, T, tg, h_out);
+  else
+    gateup_body<CPL, RPW, kMulti, C>(L, r, x, T, tg, h_out);
 }
 
 // ------------------------------------------------------------------ down
@@ -452,9 +468,8 @@ template <class C, int KW>
 constexpr int mfma_tpw() { return (KW == 512 ? 2 : 4) / C::Q; }
 
 template <int NA, int MODE, class C, int KW>
-__global__ void __launch_bounds__(kThreads) down_mfma_kernel(
-    Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
-    float *__restrict__ o_out) {
+COLI_DEV void down_mfma_body(Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
+                             float *__restrict__ o_out) {
   static_assert(mfma_kw_ok<KW>(), "k per wavefront");
   constexpr bool ONE = MODE == kAll1 || MODE == kSingles;  // one token in the slot
   constexpr int TPW = mfma_tpw<C, KW>();
@@ -644,6 +659,26 @@ __global__ void __launch_bounds__(kThreads) down_mfma_kernel(
   }
 }
 
+template <int NA, int MODE, class C, int KW>
+__global__ void __launch_bounds__(kThreads) down_mfma_kernel(
+    Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
+    float *__restrict__ o_out) {
+  down_mfma_body<NA, MODE, C, KW>(L, r, T, h_in, o_out);
+}
+
+// Every slot of a batch of several tokens in one launch, as for gate/up
+template <int NA, class C, int KW>
+__global__ void __launch_bounds__(kThreads) down_mfma_mixed_kernel(
+    Layer L, coli_moe_route_t r, int T, const float *__restrict__ h_in,
+    float *__restrict__ o_out) {
+  const int slot = blockIdx.x / (L.H / (16 * mfma_tpw<C, KW>()));  // the workgroup's slot
+  if (slot >= L.S + r.n_union[0]) return;
+  if (slot >= L.S && r.counts[r.union_ids[slot - L.S]] == 1)
+    down_mfma_body<1, kSingles, C, KW>(L, r, T, h_in, o_out);
+  else
+    down_mfma_body<NA, kMulti, C, KW>(L, r, T, h_in, o_out);
+}
+
 constexpr int kMaxStage = 4;  // tokens of one slot staged in LDS at once
 
 // gate/up rows per wavefront: two with int4 codes, one with int8 codes
@@ -662,18 +697,12 @@ hipError_t gateup_cpl(const Layer &L, const coli_moe_route_t &r, const uint16_t 
   while (tg > 1 && tg * per_token > 65536) --tg;
   const size_t lds = tg * per_token;
   const dim3 grid((waves + kWaves - 1) / kWaves);
-  if (T == 1) {
+  if (T == 1)
     launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kAll1, C>, grid,
              dim3(kThreads), lds, s, L, r, x, T, tg, h);
-  } else if (split_singles(L)) {  // single-token slots with the one-token code
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kSingles, C>, grid,
-             dim3(kThreads), lds, s, L, r, x, T, tg, h);
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kMulti, C>, grid,
-             dim3(kThreads), lds, s, L, r, x, T, tg, h);
-  } else {
-    launch_k(COLI_K_DECODE_GATEUP, gateup_stream_kernel<CPL, RPW, kAllN, C>, grid,
-             dim3(kThreads), lds, s, L, r, x, T, tg, h);
-  }
+  else  // one launch, each workgroup with its slot's code
+    launch_k(COLI_K_DECODE_GATEUP, gateup_mixed_kernel<CPL, RPW, C>, grid, dim3(kThreads), lds, s,
+             L, r, x, T, tg, h);
   return hipGetLastError();
 }
 
@@ -712,27 +741,13 @@ hipError_t down_mfma(const Layer &L, const coli_moe_route_t &r, int T, const flo
              L, r, T, h, o);
     return hipGetLastError();
   }
-  // small layers, up to 8 tokens: one launch over every slot; at 9..16
-  // tokens the one-token slots take the one-token code here too (measured:
-  // 35B-A3B-class layer at 16 tokens, down 22.7 -> 19.9 us per layer)
-  if (!split_singles(L) && T <= 8) {
-    if (T <= 8)
-      launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kAllN, C, KW>, grid, dim3(kThreads), 0, s,
-               L, r, T, h, o);
-    else
-      launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, kAllN, C, KW>, grid, dim3(kThreads), 0, s,
-               L, r, T, h, o);
-    return hipGetLastError();
-  }
-  // most slots of a small batch hold one token: those run the one-token code
-  launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kSingles, C, KW>, grid, dim3(kThreads), 0, s,
-           L, r, T, h, o);
+  // one launch, each workgroup with its slot's code
   if (T <= 8)
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<1, kMulti, C, KW>, grid, dim3(kThreads), 0, s,
-             L, r, T, h, o);
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_mixed_kernel<1, C, KW>, grid, dim3(kThreads), 0, s, L,
+             r, T, h, o);
   else
-    launch_k(COLI_K_DECODE_DOWN, down_mfma_kernel<2, kMulti, C, KW>, grid, dim3(kThreads), 0, s,
-             L, r, T, h, o);
+    launch_k(COLI_K_DECODE_DOWN, down_mfma_mixed_kernel<2, C, KW>, grid, dim3(kThreads), 0, s, L,
+             r, T, h, o);
   return hipGetLastError();
 }
 
