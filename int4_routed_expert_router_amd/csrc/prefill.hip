@@ -1361,8 +1361,8 @@ dgemm_kernel(GemmArgs g, coli_moe_route_t r, const int4 *__restrict__ tiles,
 // k in [32g, 32g + 32) as 16 bytes, low nibble first; an FP8 operand holds
 // k in [16g, 16g + 16) in bytes 0..15 and k in [64 + 16g, 64 + 16g + 16) in
 // bytes 16..31.  Lane l's scale byte belongs to row r and the 32-block g.
-// The result tile is laid out as in the other 16x16 instructions.
-constexpr int kMxK = 128;  // k per instruction
+// The result tile is laid out as in the other 16x16 instructions; one
+// instruction covers 128 k.
 typedef int coli_i32x8 __attribute__((ext_vector_type(8)));
 typedef float coli_f32x4v __attribute__((ext_vector_type(4)));
 
