@@ -57,3 +57,26 @@ def test_small_layer_batch_invariant(fmt, which, T):
     for t in range(T):
         yt = forward(L, run_route(L, lg[t:t + 1].contiguous()), x[t:t + 1].contiguous(), "decode")
         assert torch.equal(yt[0], y[t]), "%s token %d of %d depends on its batch" % (fmt, t, T)
+
+
+# every batch size of the one-launch multi-token decode: each workgroup runs
+# its slot's one-token or general code, and a token's result matches the
+# same token decoded alone
+A3B = synth.WORKLOADS["a3b"].spec
+LARGE_I = synth.LayerSpec(2048, 2048, 6, 1, 3, sigmoid=True, renorm=True)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8", "mxfp4"])
+@pytest.mark.parametrize("which", ["a3b", "large_i"])
+def test_batch_invariant_every_T(fmt, which):
+    spec = _spec(A3B if which == "a3b" else LARGE_I, fmt)
+    print("batch invariance at T = 2..16: %s %s" % (fmt, which), flush=True)
+    L = gpu_layer(spec, seed=31)
+    lg = synth.make_logits(spec, 16, seed=31, zipf_alpha=synth.ZIPF_ALPHA).cuda()
+    x = synth.make_x(spec, 16, seed=31).cuda()
+    alone = [forward(L, run_route(L, lg[t:t + 1].contiguous()), x[t:t + 1].contiguous(),
+                     "decode")[0] for t in range(16)]
+    for T in range(2, 17):
+        y = forward(L, run_route(L, lg[:T].contiguous()), x[:T].contiguous(), "decode")
+        for t in range(T):
+            assert torch.equal(y[t], alone[t]), "%s %s: token %d of %d" % (fmt, which, t, T)
