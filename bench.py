@@ -44,6 +44,7 @@ if _ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak (POP/s -> TOPS)
+FP8_PEAK_TOPS = 5000.0     # MI355X dense fp8 matrix peak; E2M1 x E4M3 runs at this rate
 # fp32 vector peak; a bf16 dot2 (two products and two adds per lane) issues
 # at the same rate as a packed fp32 FMA, so it is the dot2 router's ALU peak
 FP32_VECTOR_PEAK_TFLOPS = 157.3
@@ -430,13 +431,16 @@ def secondary_prefill(name, spec, T, zipf, steps, warmup, layer=None, copies=1,
     nbytes = union_bytes(spec, [lg], spec.top_k)
     ops = 2.0 * 3 * spec.hidden * spec.inter * T * (spec.top_k + spec.n_shared)
     gemm_us = sum(kern.get(k, {"avg_us": 0})["avg_us"] for k in ("gemm_gateup", "gemm_down"))
+    # the matrix-core format the GEMMs run in: int8 (Q8_0 activations) or the
+    # scaled MX instruction (E2M1 weights x E4M3 activations, the fp8 rate)
+    fmt, peak = ("mx", FP8_PEAK_TOPS) if spec.mx_act else ("int8", INT8_PEAK_TOPS)
     out = {"workload": name, "path": "prefill",
            "weights": spec.weights, "tokens": T, "ms_per_step": round(ms, 4),
            "activations": "mxfp8 (MX matrix cores)" if spec.mx_act else "q8_0 (int8 matrix cores)",
            "tokens_per_s": round(T / (ms * 1e-3), 1),
-           "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
-           "int8_frac": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-           "gemm_int8_TOPS": round(ops / (gemm_us * 1e-6) / 1e12, 2) if gemm_us else None,
+           fmt + "_TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
+           fmt + "_frac": round(ops / (ms * 1e-3) / 1e12 / peak, 4),
+           "gemm_" + fmt + "_TOPS": round(ops / (gemm_us * 1e-6) / 1e12, 2) if gemm_us else None,
            "weight_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
@@ -458,6 +462,19 @@ def prefill_dense(steps, warmup):
 
     spec = synth.LayerSpec(6144, 2048, 1, 1, 1, sigmoid=True, renorm=True)
     out = secondary_prefill("glm_shape_dense_2experts_T2048", spec, 2048, 0.0, steps, warmup)
+    out["note"] = "routed expert 0 and the shared expert each take all 2048 tokens"
+    return out
+
+
+def prefill_dense_mx(steps, warmup):
+    """The same two dense GEMMs with MXFP4 experts on the MX path (MXFP8
+    activations, block scales applied by the scaled matrix-core instruction)."""
+    import synth
+
+    spec = synth.LayerSpec(6144, 2048, 1, 1, 1, sigmoid=True, renorm=True, mxfp4=True,
+                           mx_act=True)
+    out = secondary_prefill("glm_shape_dense_2experts_mxfp4_mx_T2048", spec, 2048, 0.0, steps,
+                            warmup)
     out["note"] = "routed expert 0 and the shared expert each take all 2048 tokens"
     return out
 
@@ -610,6 +627,7 @@ def main():
         return
     if args.prefill_dense_only:
         print(json.dumps(prefill_dense(args.steps, args.warmup)), flush=True)
+        print(json.dumps(prefill_dense_mx(args.steps, args.warmup)), flush=True)
         return
     if args.decode_t4_only:
         w = synth.WORKLOADS["glm"]
@@ -687,6 +705,8 @@ def main():
         del stack
         torch.cuda.empty_cache()
         secondary.append(prefill_dense(10, 2))
+        torch.cuda.empty_cache()
+        secondary.append(prefill_dense_mx(10, 2))
         torch.cuda.empty_cache()
         secondary.append(secondary_router("glm_router_T1", w.spec, 1, 200, 10))
         secondary.append(secondary_router("glm_router_T2048", w.spec, 2048, 20, 3))
