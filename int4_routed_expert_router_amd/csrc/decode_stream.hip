@@ -14,12 +14,14 @@
 // a shift) and meet the activations in v_dot2_f32_bf16; each 32-chunk's bias
 // 136 * sum(x) is removed before its fp16 group scale.  int8 codes (same
 // container, one byte per weight) become exact bf16 values q through an
-// fp32 conversion of each sign-extended byte (see the codecs below).  Lane partials of
-// several rows are combined with a reduce-scatter (each shuffle step halves
-// the values a lane carries).  A token's arithmetic does not depend on the
-// other tokens of the batch.  With I = 2048, down runs on the bf16 matrix
-// cores instead (down_mfma_kernel): the weights dequantised the same way are
-// the B operand and the tokens' h halves the A operand.
+// fp32 conversion of each sign-extended byte (the codecs are in codec.h).
+// Lane partials of several rows are combined with a reduce-scatter (each
+// shuffle step halves the values a lane carries).  A token's arithmetic
+// does not depend on the other tokens of the batch.  With I = 512, 1024 or
+// 2048, down runs on the bf16 matrix cores instead (down_mfma_kernel): the
+// weights dequantised the same way are the B operand and the tokens' h
+// halves the A operand.  A batch of several tokens makes one launch per
+// GEMV, in which each workgroup runs its slot's one-token or general code.
 #include "device_common.h"
 #include "codec.h"
 #include "internal.h"
