@@ -131,12 +131,9 @@ COLI_DEV void quantize_chunk8(const float v[8], uint32_t &lo, uint32_t &hi,
 // MXFP4 (OCP MX conversion): a block of 32 is 4 consecutive lanes.  The
 // shared exponent floor(log2 max|w|) - 2 is read from the maximum's fp32
 // exponent field e: E8M0 byte E = max(e - 2, 0) (a subnormal or zero maximum
-// gives 0).  Each value is scaled by 2^(127 - E) (exact: the result is below
-// 8, and a result that small to be rounded is code 0 anyway) and its E2M1
-// magnitude code counts the grid midpoints it reaches -- strictly for the
-// midpoints above an even code, inclusively for those above an odd code, so
-// ties go to the even code -- saturating at 7 (6.0).  The sign bit is the
-// value's own, zero included.
+// gives 0).  Each value is scaled by 2^(127 - E) and becomes the nearest
+// E2M1 code, ties to the even code, saturating at code 7 (6.0); the sign bit
+// is the value's own, zero included.
 COLI_DEV void quantize_chunk_fp4(const float v[8], uint32_t &packed, uint8_t &e_out) {
   uint32_t ab = 0;
 #pragma unroll
@@ -146,16 +143,16 @@ COLI_DEV void quantize_chunk_fp4(const float v[8], uint32_t &packed, uint8_t &e_
   const int e = (int)(ab >> 23);
   const uint32_t E = (uint32_t)max(e - 2, 0);
   const float f = __uint_as_float((254u - E) << 23);  // 2^(127 - E)
-  packed = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float m = fabsf(v[i] * f);
-    const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-                       (uint32_t)(m > 5.0f);
-    const uint32_t nib = c | ((__float_as_uint(v[i]) >> 28) & 8u);
-    packed |= nib << (4 * i);
-  }
+  // f is a power of two, so v * f is exact except far below the least nonzero
+  // code, where only the sign survives either way.  The hardware conversion
+  // (scale 1) applies exactly the rounding above to two values at a time,
+  // element 2j going to the low nibble of byte j.
+  uint32_t p = 0;
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0] * f, v[1] * f, 1.0f, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2] * f, v[3] * f, 1.0f, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4] * f, v[5] * f, 1.0f, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6] * f, v[7] * f, 1.0f, 3);
+  packed = p;
   e_out = (uint8_t)E;
 }
 
