@@ -1100,18 +1100,31 @@ COLI_DEV void dgemm_item(const GemmArgs &g, const Item &it, const int *rowid, co
   struct Ops {
     long a[2], b[NTS];
   };
-  auto read_ops = [&](const DStage &B, int b, Ops &o) {
+  // LDS reads of block b's operands (raw nibble words and activation
+  // pairs), then their unpacking into MFMA operands: split so that the
+  // previous block's scale FMAs can run while the reads are in flight
+  struct Raw {
+    uint32_t w[2];
+    uint2 v[NTS];
+  };
+  auto load_ops = [&](const DStage &B, int b, Raw &rw) {
     const char *wb = reinterpret_cast<const char *>(B.w) + (offA ^ (16 * b));
 #pragma unroll
+    for (int rs = 0; rs < 2; ++rs) rw.w[rs] = *reinterpret_cast<const uint32_t *>(wb + rs * 64 * 128);
+    const char *ab = reinterpret_cast<const char *>(B.a) + (offB ^ (32 * b));
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) rw.v[ts] = *reinterpret_cast<const uint2 *>(ab + ts * 16 * 256);
+  };
+  auto unpack_ops = [&](const Raw &rw, Ops &o) {
+#pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
-      const uint32_t x = *reinterpret_cast<const uint32_t *>(wb + rs * 64 * 128);
+      const uint32_t x = rw.w[rs];
       const uint32_t ev = (x << 4) & 0xf0f0f0f0u, od = x & 0xf0f0f0f0u;
       o.a[rs] = (long)(((uint64_t)od << 32) | ev);
     }
-    const char *ab = reinterpret_cast<const char *>(B.a) + (offB ^ (32 * b));
 #pragma unroll
     for (int ts = 0; ts < NTS; ++ts) {
-      uint2 v = *reinterpret_cast<const uint2 *>(ab + ts * 16 * 256);
+      uint2 v = rw.v[ts];
       if (MODE == kDots) v = even_odd8(v.x, v.y);  // caller's codes are in natural order
       o.b[ts] = (long)(((uint64_t)v.y << 32) | v.x);
     }
@@ -1146,6 +1159,9 @@ COLI_DEV void dgemm_item(const GemmArgs &g, const Item &it, const int *rowid, co
         const uint4 q = swh[rs][i >> 1];
         const uint32_t hw = (i & 1) ? ((gq & 2) ? q.w : q.z) : ((gq & 2) ? q.y : q.x);
         c.w[rs][i] = f16_to_f32((uint16_t)((gq & 1) ? hw >> 16 : hw));
+        // kept as fp32 values: folded into the FMAs as v_fma_mix_f32 (mixed
+        // fp16 operand) the compiler would issue at a lower rate
+        asm volatile("" : "+v"(c.w[rs][i]));
       }
     const uint4 *sa = &B.sa[lr * 4 + (gq ^ fsa)];
 #pragma unroll
@@ -1195,9 +1211,11 @@ COLI_DEV void dgemm_item(const GemmArgs &g, const Item &it, const int *rowid, co
   // next stage's DMA (into `N`, if `nxt` >= 0) is issued along the way
   auto compute = [&](const DStage &B, int st, DStage &N, int nxt) {
     Ops o;
+    Raw rw;
     Scl c0, c1;
     coli_i32x4 d0[2][NTS], d1[2][NTS];
-    read_ops(B, 0, o);
+    load_ops(B, 0, rw);
+    unpack_ops(rw, o);
     if (MODE != kDots) {
       read_sw(B);
       read_scl(B, 0, c0);
@@ -1209,12 +1227,21 @@ COLI_DEV void dgemm_item(const GemmArgs &g, const Item &it, const int *rowid, co
         issue_part(N, nxt, b);
         if (b < 2) issue_part(N, nxt, 8 + b);
       }
+      // order within a block: next block's LDS reads, this block's scale
+      // FMAs (which cover the read latency), then the next block's unpack
+      // and MFMAs; the scheduling barriers keep the compiler from hoisting
+      // the unpack (and with it the LDS wait) above the FMAs
       if (b + 1 < kSB) {
-        read_ops(B, b + 1, o);
+        load_ops(B, b + 1, rw);
         if (MODE != kDots && ((b + 1) & 1) == 0) read_scl(B, (b + 1) >> 1, ((b >> 1) & 1) ? c0 : c1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      finish(st, b, ((b >> 1) & 1) ? c1 : c0, (b & 1) ? d1 : d0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (b + 1 < kSB) {
+        unpack_ops(rw, o);
         mfmas(o, (b & 1) ? d0 : d1);
       }
-      finish(st, b, ((b >> 1) & 1) ? c1 : c0, (b & 1) ? d1 : d0);
     }
   };
 
