@@ -578,6 +578,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="main workload only")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the 2048-token GLM prefill workload (for profiling it)")
+    ap.add_argument("--prefill-tokens", type=int, default=2048,
+                    help="tokens of the --prefill-only / --prefill-mx-only run (default 2048)")
     ap.add_argument("--prefill-mx-only", action="store_true",
                     help="the 2048-token GLM-shaped prefill with MXFP4 experts on the MX path")
     ap.add_argument("--prefill-dense-only", action="store_true",
@@ -616,13 +618,15 @@ def main():
         return
     if args.prefill_only:
         pw = synth.WORKLOADS["glm_prefill"]
-        print(json.dumps(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
+        T = args.prefill_tokens
+        print(json.dumps(secondary_prefill("glm_prefill_T%d" % T, pw.spec, T, pw.zipf_alpha,
                                            args.steps, args.warmup, copies=1)), flush=True)
         return
     if args.prefill_mx_only:
         pw = synth.WORKLOADS["glm_prefill"]
         spec = dataclasses.replace(pw.spec, mxfp4=True, mx_act=True)
-        print(json.dumps(secondary_prefill("glm_mxfp4_mx_prefill_T2048", spec, 2048,
+        T = args.prefill_tokens
+        print(json.dumps(secondary_prefill("glm_mxfp4_mx_prefill_T%d" % T, spec, T,
                                            pw.zipf_alpha, args.steps, args.warmup)), flush=True)
         return
     if args.prefill_dense_only:
@@ -702,6 +706,13 @@ def main():
         secondary.append(secondary_prefill("glm_prefill_T2048", pw.spec, 2048, pw.zipf_alpha,
                                            10, 2, layer=stack.layers[0], k32_ceiling=k32,
                                            cpu=not args.no_cpu))
+        # an extra, clearly labelled run of the same layer at 16,384 tokens:
+        # most experts then sit above the int8 ridge (625 ops per weight byte)
+        ext = secondary_prefill("glm_prefill_T16384_extra", pw.spec, 16384, pw.zipf_alpha, 5, 2,
+                                layer=stack.layers[0], k32_ceiling=k32)
+        ext["note"] = ("extra run: the 2048-token GLM prefill layer at 8x the tokens, "
+                       "so the expert GEMMs are compute-heavy")
+        secondary.append(ext)
         del stack
         torch.cuda.empty_cache()
         secondary.append(prefill_dense(10, 2))
@@ -742,9 +753,19 @@ def main():
                                            dataclasses.replace(ow.spec, mxfp4=True, mx_act=True),
                                            512, 0.0, 20, 3, copies=4))
         pw = synth.WORKLOADS["glm_prefill"]
-        secondary.append(secondary_prefill("glm_mxfp4_mx_prefill_T2048",
-                                           dataclasses.replace(pw.spec, mxfp4=True, mx_act=True),
-                                           2048, pw.zipf_alpha, 10, 2))
+        import int4_routed_expert_router_amd as coli
+        mxspec = dataclasses.replace(pw.spec, mxfp4=True, mx_act=True)
+        mxl = coli.Layer.from_spec(mxspec, *synth.make_weights(mxspec, seed=0, layer=0,
+                                                               device="cuda"))
+        secondary.append(secondary_prefill("glm_mxfp4_mx_prefill_T2048", mxspec, 2048,
+                                           pw.zipf_alpha, 10, 2, layer=mxl))
+        ext = secondary_prefill("glm_mxfp4_mx_prefill_T16384_extra", mxspec, 16384,
+                                pw.zipf_alpha, 5, 2, layer=mxl)
+        ext["note"] = ("extra run: the 2048-token GLM prefill layer (MXFP4 experts, MX path) "
+                       "at 8x the tokens, so the expert GEMMs are compute-heavy")
+        secondary.append(ext)
+        del mxl
+        torch.cuda.empty_cache()
         aw = synth.WORKLOADS["a3b"]
         for t in aw.tokens:
             secondary.append(secondary_decode("a3b_decode_T%d" % t, aw.spec, t, aw.zipf_alpha, 4,
