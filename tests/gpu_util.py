@@ -75,6 +75,29 @@ def cover_tokens(g, T: int, k: int, tile: int = 64, hottest: int = 0, shared: bo
     return sorted(toks)
 
 
+def sample_tokens(g, T: int, k: int, tile: int = 64, hottest: int = 2, every: int = 16):
+    """A bounded sample for batches too large to compare every tile: for each
+    expert, the first row of its first tile and the last row of its last
+    tile; for the `hottest` most-loaded experts, the first and last row of
+    every tile; the shared expert's first and last token and the first row
+    of every `every`-th tile."""
+    counts, offsets, pairs = g["counts"], g["offsets"], np.asarray(g["pairs"]).ravel()
+    toks = set()
+    for e in range(len(counts)):
+        n = int(counts[e])
+        if n:
+            toks.add(int(pairs[offsets[e]]) // k)
+            toks.add(int(pairs[offsets[e] + n - 1]) // k)
+    for e in np.argsort(-np.asarray(counts), kind="stable")[:hottest]:
+        n = int(counts[e])
+        for pos in range(n):
+            if pos % tile in (0, tile - 1) or pos == n - 1:
+                toks.add(int(pairs[offsets[e] + pos]) // k)
+    toks.update(range(0, T, tile * every))
+    toks.add(T - 1)
+    return sorted(toks)
+
+
 def forward(L: coli.Layer, r: coli.Route, x: torch.Tensor, entry: str, y_dtype=coli.COLI_OUT_F32):
     T = x.shape[0]
     ent = coli.COLI_ENTRY_DECODE if entry == "decode" else coli.COLI_ENTRY_PREFILL

@@ -13,7 +13,7 @@ import int4_routed_expert_router_amd as coli
 import oracle
 import synth
 from gpu_util import (check_prefill_output_mx, checked_route, cover_tokens, forward, gpu_layer,
-                      run_route)
+                      run_route, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,27 @@ def test_mx_prefill_glm_every_tile():
     of the hottest expert."""
     w = synth.WORKLOADS["glm_prefill"]
     _case(_mx(w.spec), 600, zipf=w.zipf_alpha, tokens=[300], cover=dict(tile=64, hottest=1))
+
+
+@pytest.mark.timeout(900)
+def test_mx_prefill_glm_16384_sampled():
+    """The GLM-shaped MX layer at 16,384 tokens (the bench's extra run):
+    each expert's first and last token, every tile boundary of the two
+    hottest experts and sampled shared-expert tiles."""
+    w = synth.WORKLOADS["glm_prefill"]
+    spec = _mx(w.spec)
+    print("mx prefill case: GLM layer, T=16384 (sampled)", flush=True)
+    L = gpu_layer(spec, seed=0)
+    T = 16384
+    lg = synth.make_logits(spec, T, seed=0, zipf_alpha=w.zipf_alpha).cuda()
+    x = synth.make_x(spec, T, seed=0).cuda()
+    r = run_route(L, lg)
+    y = forward(L, r, x, "prefill")
+    g = checked_route(spec, r, lg)
+    toks = sample_tokens(g, T, spec.top_k)
+    print("  comparing %d tokens" % len(toks), flush=True)
+    err, n_budget = check_prefill_output_mx(spec, L, g, x, y, toks)
+    print("  rel err %.3g, %d elements within the boundary budget" % (err, n_budget), flush=True)
 
 
 def test_mx_prefill_deterministic_and_bf16():

@@ -7,7 +7,7 @@ import int4_routed_expert_router_amd as coli
 import oracle
 import synth
 from gpu_util import (check_prefill_output, checked_route, cover_tokens, forward, gpu_layer,
-                      run_route)
+                      run_route, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,26 @@ def test_prefill_glm_2048_every_tile():
     w = synth.WORKLOADS["glm_prefill"]
     _prefill_case(w.spec, 2048, zipf=w.zipf_alpha, tokens=[777],
                   cover=dict(tile=64, hottest=3))
+
+
+@pytest.mark.timeout(900)
+def test_prefill_glm_16384_sampled():
+    """The GLM-shaped layer at 16,384 tokens, the bench's extra compute-heavy
+    run: each expert's first and last token, every tile boundary of the two
+    hottest experts (about 570 tokens each) and sampled shared-expert tiles."""
+    w = synth.WORKLOADS["glm_prefill"]
+    print("prefill case: GLM layer, T=16384 (sampled)", flush=True)
+    L = gpu_layer(w.spec, seed=0)
+    T = 16384
+    lg = synth.make_logits(w.spec, T, seed=0, zipf_alpha=w.zipf_alpha).cuda()
+    x = synth.make_x(w.spec, T, seed=0).cuda()
+    r = run_route(L, lg)
+    y = forward(L, r, x, "prefill")
+    g = checked_route(w.spec, r, lg)
+    toks = sample_tokens(g, T, w.spec.top_k)
+    print("  comparing %d tokens" % len(toks), flush=True)
+    err, n_budget = check_prefill_output(w.spec, L, g, x, y, toks)
+    print("  rel err %.3g, %d elements within the boundary budget" % (err, n_budget), flush=True)
 
 
 @pytest.mark.parametrize("spec,T", [
